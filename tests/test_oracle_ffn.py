@@ -1,0 +1,231 @@
+"""Pins of the oracle's expert FFN and combine (bf16/f32 and FP8 variants):
+a library dense-FFN special case, pure-Python brute force on tiny shapes,
+closed forms and invariants."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import make_inputs
+
+
+def getters(w1, w2):
+    return (lambda e: w1[e]), (lambda e: w2[e])
+
+
+def test_single_expert_is_dense_swiglu_ffn_torch():
+    # E = 1, k = 1: the MoE layer is exactly a dense SwiGLU FFN (weight 1)
+    rng = np.random.default_rng(0)
+    T, H, I = 5, 24, 40
+    x = rng.standard_normal((T, H))
+    w1 = rng.standard_normal((1, 2 * I, H)) / 5
+    w2 = rng.standard_normal((1, H, I)) / 6
+    ids, w = oracle.route(rng.standard_normal((T, 1)).astype(np.float32), 1)
+    got = oracle.ffn(x, *getters(w1, w2), ids, w)
+    X, W1, W2 = (torch.from_numpy(a) for a in (x, w1[0], w2[0]))
+    ref = (torch.nn.functional.silu(X @ W1[:I].T) * (X @ W1[I:].T)) @ W2.T
+    assert np.allclose(got, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def brute_moe(x, w1, w2, ids, w):
+    """Pure-Python loops, no numpy arithmetic."""
+    T, H = len(x), len(x[0])
+    k = len(ids[0])
+    I = len(w2[0][0])
+    out = [[0.0] * H for _ in range(T)]
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t][j])
+            h = []
+            for n in range(I):
+                g = sum(float(w1[e][n][c]) * float(x[t][c]) for c in range(H))
+                u = sum(float(w1[e][I + n][c]) * float(x[t][c]) for c in range(H))
+                h.append(g / (1.0 + math.exp(-g)) * u)
+            for r in range(H):
+                y = sum(float(w2[e][r][n]) * h[n] for n in range(I))
+                out[t][r] += float(w[t][j]) * y
+    return np.array(out)
+
+
+@pytest.mark.parametrize("T,E,H,I,k", [(1, 1, 3, 2, 1), (3, 4, 5, 7, 2), (4, 3, 8, 6, 3), (2, 4, 6, 16, 4)])
+def test_ffn_matches_pure_python_brute_force(T, E, H, I, k):
+    rng = np.random.default_rng(T * 7 + E)
+    x = rng.standard_normal((T, H))
+    w1 = rng.standard_normal((E, 2 * I, H))
+    w2 = rng.standard_normal((E, H, I))
+    ids, w = oracle.route(rng.standard_normal((T, E)).astype(np.float32), k)
+    got = oracle.ffn(x, *getters(w1, w2), ids, w)
+    ref = brute_moe(x.tolist(), w1.tolist(), w2.tolist(), ids.tolist(), w.tolist())
+    assert np.allclose(got, ref, rtol=1e-11, atol=1e-11)
+    # a subset of tokens gives the same rows
+    sub = [T - 1, 0]
+    assert np.allclose(oracle.ffn(x, *getters(w1, w2), ids, w, tokens=sub), ref[sub], rtol=1e-11, atol=1e-11)
+
+
+def test_ffn_closed_form_scalar():
+    # H = I = 1: out = w2 * SiLU(a) * b with gate a = ln 3 -> sigmoid = 3/4
+    a, b, c = math.log(3.0), 2.0, 0.5
+    x = np.array([[1.0]])
+    w1 = np.array([[[a], [b]]])
+    w2 = np.array([[[c]]])
+    ids = np.array([[0]], dtype=np.int32)
+    out = oracle.ffn(x, *getters(w1, w2), ids, np.array([[0.25]]))
+    assert out[0, 0] == pytest.approx(0.25 * c * (a * 0.75) * b, rel=1e-15)
+
+
+def test_ffn_invariants():
+    rng = np.random.default_rng(5)
+    T, E, H, I, k = 6, 5, 8, 12, 3
+    x = rng.standard_normal((T, H))
+    w1 = rng.standard_normal((E, 2 * I, H))
+    w2 = rng.standard_normal((E, H, I))
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    ids, w = oracle.route(L, k)
+    base = oracle.ffn(x, *getters(w1, w2), ids, w)
+    # x = 0 -> out = 0
+    assert np.all(oracle.ffn(np.zeros_like(x), *getters(w1, w2), ids, w) == 0)
+    # scaling FC2 by 2 doubles the output exactly
+    assert np.array_equal(oracle.ffn(x, *getters(w1, 2 * w2), ids, w), 2 * base)
+    # token permutation (rows of x and logits together) permutes everything
+    perm = rng.permutation(T)
+    ids_p, w_p = oracle.route(L[perm], k)
+    assert np.array_equal(ids_p, ids[perm])
+    assert np.allclose(oracle.ffn(x[perm], *getters(w1, w2), ids_p, w_p), base[perm], rtol=1e-13, atol=1e-13)
+    # identical experts: out_t = (sum_j w_tj) * FFN(x_t)
+    same1 = np.repeat(w1[:1], E, 0)
+    same2 = np.repeat(w2[:1], E, 0)
+    one = oracle.ffn(x, *getters(same1, same2), np.zeros((T, 1), np.int32), np.ones((T, 1)))
+    got = oracle.ffn(x, *getters(same1, same2), ids, w)
+    assert np.allclose(got, w.sum(1, keepdims=True) * one, rtol=1e-12, atol=1e-12)
+    # one-hot weights pick a single expert's FFN
+    oh = np.zeros_like(w)
+    oh[:, 1] = 1.0
+    got = oracle.ffn(x, *getters(w1, w2), ids, oh)
+    for t in range(T):
+        e = ids[t, 1]
+        ref = oracle.ffn(x[t:t + 1], *getters(w1, w2), np.array([[e]], np.int32), np.ones((1, 1)))
+        assert np.allclose(got[t], ref[0], rtol=1e-13, atol=1e-13)
+
+
+def test_gate_and_up_are_not_interchangeable():
+    # SiLU is applied to the first half only: swapping halves must change the result
+    rng = np.random.default_rng(6)
+    H, I = 4, 3
+    x = rng.standard_normal((1, H))
+    w1 = rng.standard_normal((1, 2 * I, H))
+    w2 = rng.standard_normal((1, H, I))
+    ids, w = np.zeros((1, 1), np.int32), np.ones((1, 1))
+    a = oracle.ffn(x, *getters(w1, w2), ids, w)
+    sw = np.concatenate([w1[:, I:], w1[:, :I]], 1)
+    b = oracle.ffn(x, *getters(sw, w2), ids, w)
+    assert not np.allclose(a, b)
+
+
+# ------------------------------------------------------------------ FP8 ---
+
+def test_quant_rows_closed_forms():
+    v = np.array([[1.0, -2.0, 0.5, 4.0], [0.0, 0.0, 0.0, 0.0], [-448.0, 1.0, 2.0, 3.0]], np.float32)
+    q, s = oracle.quant_rows_e4m3(v)
+    assert s[0] == np.float32(4.0) / np.float32(448.0)
+    assert q[0, 3] == 0x7E                            # the absmax element maps to 448
+    assert s[1] == 1.0 and np.all(q[1] == 0)          # zero row: scale 1, codes 0
+    assert s[2] == 1.0 and q[2, 0] == 0xFE and q[2, 1] == 0x38
+    # dequantised values are within half an e4m3 step (relative 2^-4) of the input
+    d = oracle.e4m3fn_decode(q) * s[:, None]
+    assert np.all(np.abs(d - v) <= np.abs(v) * 2.0 ** -4 + 2.0 ** -9 * s[:, None])
+
+
+def test_ffn_fp8_lossless_special_case_equals_plain_ffn():
+    # x rows on the e4m3 grid with absmax 448*2^-4 (exact power-of-two scale) and
+    # I = 1 (h is one value per slot, so its quantisation is exact up to one f32
+    # rounding): the FP8 path equals the plain FFN on the dequantised operands.
+    rng = np.random.default_rng(7)
+    T, E, H, I, k = 4, 3, 16, 1, 2
+    codes = rng.integers(0, 0x7E, size=(T, H)).astype(np.uint8)
+    codes[:, 0] = 0x7E
+    codes |= (rng.integers(0, 2, size=(T, H)) * 0x80).astype(np.uint8)
+    xv = (oracle.e4m3fn_decode(codes) * 2.0 ** -4).astype(np.float32)
+    x_bits = (xv.view(np.uint32) >> 16).astype(np.uint16)       # exact: few mantissa bits
+    assert np.array_equal(oracle.bf16_bits_to_f64(x_bits), xv.astype(np.float64))
+    w1q = rng.integers(0, 256, size=(E, 2 * I, H)).astype(np.uint8)
+    w1q[(w1q & 0x7F) == 0x7F] = 0x30
+    w2q = rng.integers(0, 256, size=(E, H, I)).astype(np.uint8)
+    w2q[(w2q & 0x7F) == 0x7F] = 0x31
+    s1 = rng.uniform(0.5, 2, size=(E, 2 * I)).astype(np.float32)
+    s2 = rng.uniform(0.5, 2, size=(E, H)).astype(np.float32)
+    ids, w = oracle.route(rng.standard_normal((T, E)).astype(np.float32), k)
+    got = oracle.ffn_fp8(x_bits, lambda e: w1q[e], s1, lambda e: w2q[e], s2, ids, w)
+    W1 = oracle.e4m3fn_decode(w1q) * s1[..., None].astype(np.float64)
+    W2 = oracle.e4m3fn_decode(w2q) * s2[..., None].astype(np.float64)
+    ref = oracle.ffn(xv.astype(np.float64), *getters(W1, W2), ids, w)
+    assert oracle.normwise_rel_err(got, ref) < 1e-6
+
+
+def test_ffn_fp8_close_to_unquantised_on_random_inputs():
+    # informational bound: W8A8 e4m3 on N(0,1) data stays within a few percent
+    inp = make_inputs(6, 4, 256, 128, 2, dtype="fp8", routing="normal", seed=1)
+    master = make_inputs(6, 4, 256, 128, 2, dtype="f32", routing="normal", seed=1)
+    ids, w = oracle.route(inp.host_logits(), 2)
+    got = oracle.ffn_fp8(inp.host_x(), inp.host_w1, inp.host_w1_scale(), inp.host_w2,
+                         inp.host_w2_scale(), ids, w)
+    x64 = oracle.bf16_bits_to_f64(inp.host_x())
+    ref = oracle.ffn(x64, lambda e: master.host_w1(e).astype(np.float64),
+                     lambda e: master.host_w2(e).astype(np.float64), ids, w)
+    assert oracle.normwise_rel_err(got, ref) < 0.1
+
+
+def _fp8_case(rng, T=3, E=2, H=32, I=32, k=1):
+    w1q = rng.integers(0, 256, size=(E, 2 * I, H)).astype(np.uint8)
+    w1q[(w1q & 0x7F) == 0x7F] = 0x30
+    s1 = rng.uniform(0.01, 0.02, size=(E, 2 * I)).astype(np.float32)
+    return w1q, s1
+
+
+def test_ffn_fp8_quantises_x_per_token():
+    # rows with absmax exactly 448*2^-3 get the power-of-two scale 2^-3, so the
+    # dequantised row x^ is exact in bf16; feeding x^ again must give the same
+    # output bit for bit (quantisation is idempotent) and differ from feeding x
+    # unquantised through the plain FFN.
+    rng = np.random.default_rng(11)
+    T, E, H, I, k = 3, 2, 32, 8, 2
+    xv = rng.standard_normal((T, H)).astype(np.float32)
+    xv[:, 5] = 56.0                               # 448 * 2^-3
+    x_bits = (torch.from_numpy(xv).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    xb = oracle.bf16_bits_to_f64(x_bits).astype(np.float32)
+    q, s = oracle.quant_rows_e4m3(xb)
+    assert np.all(s == np.float32(0.125))
+    xhat = (oracle.e4m3fn_decode(q) * 0.125).astype(np.float32)
+    xhat_bits = (xhat.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(oracle.bf16_bits_to_f64(xhat_bits), xhat.astype(np.float64))
+    w1q, s1 = _fp8_case(rng, T, E, H, I)
+    w2q = rng.integers(0, 0x7E, size=(E, H, I)).astype(np.uint8)
+    s2 = np.full((E, H), 0.5, np.float32)
+    ids, w = oracle.route(rng.standard_normal((T, E)).astype(np.float32), k)
+    a = oracle.ffn_fp8(x_bits, lambda e: w1q[e], s1, lambda e: w2q[e], s2, ids, w)
+    b = oracle.ffn_fp8(xhat_bits, lambda e: w1q[e], s1, lambda e: w2q[e], s2, ids, w)
+    assert np.array_equal(a, b)
+    assert not np.array_equal(xb, xhat)
+
+
+def test_ffn_fp8_quantises_h_per_slot_on_grid():
+    # FC2 = identity (code 1.0 on the diagonal, scale 1) so y = h^: every output
+    # element must be (row scale) * (an e4m3 value), row scale = absmax/448.
+    rng = np.random.default_rng(12)
+    T, E, H, k = 4, 2, 16, 1
+    I = H
+    x_bits = (torch.randn(T, H, generator=torch.Generator().manual_seed(0))
+              .to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    w1q, s1 = _fp8_case(rng, T, E, H, I)
+    w2q = np.zeros((E, H, I), np.uint8)
+    for e in range(E):
+        np.fill_diagonal(w2q[e], 0x38)
+    s2 = np.ones((E, H), np.float32)
+    ids = np.array([[t % E] for t in range(T)], np.int32)
+    out = oracle.ffn_fp8(x_bits, lambda e: w1q[e], s1, lambda e: w2q[e], s2, ids, np.ones((T, 1)))
+    grid = oracle.E4M3FN_VALUES[:127]
+    for row in out:
+        b = np.float32(np.max(np.abs(row)).astype(np.float32) / np.float32(448.0))
+        r = np.abs(row) / np.float64(b)
+        assert np.all(np.min(np.abs(r[:, None] - grid[None, :]), axis=1) <= 1e-5 * np.maximum(r, 1))
