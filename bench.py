@@ -1,0 +1,230 @@
+"""Benchmark of the fused MoE expert FFN hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: router softmax + top-k,
+token-to-expert alignment, FC1 (gate|up) + SiLU*up, FC2, top-k weighted
+combine, all in libmoe.so's HIP kernels on torch's current stream. Inputs and
+weights are resident in HBM before the timed region; outputs and workspace are
+allocated once, outside it.
+
+Default workload: decode, bf16, T=16 tokens, E=64 experts, H=4096, I=1536,
+top-8, balanced routing (every expert gets 2 slots), seed 0.
+
+Prints one JSON line: tokens/s of the whole step, the HBM roofline of the
+dominant kernel (FC1, timed live with HIP events on the same stream), and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE FC1+FC2 layer tokens/s; expert-weight HBM GB/s (% of peak) at decode"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2516.6
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload number 1..5 (default 2)")
+    ap.add_argument("--block-m", type=int, default=64)
+    ap.add_argument("--flags", type=int, default=0, help="extra moe_ffn flags (e.g. 256 = no XCD remap)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "moe_expert_ffn_router_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
+    taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f).get(f"{kernel}@{workload}")
+    if not rec or rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, target_s: float):
+    """The CPU oracle as it stands, on the first n tokens of the same workload;
+    n grows until about target_s seconds of oracle work have been timed."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                            if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas_threads = 1
+    logits = inp.host_logits()
+    x_bits = inp.host_x()
+    # host copies of the weights of the experts the sample can touch (not timed)
+    ids_all, _ = oracle.route(logits, inp.k)
+    w1h, w2h = {}, {}
+    t_spent, n, per_tok = 0.0, 0, []
+    sample_out = None
+    while n < inp.T and t_spent < target_s:
+        n_next = min(inp.T, max(n + 1, 2 * n))
+        for e in np.unique(ids_all[:n_next]):
+            e = int(e)
+            if e not in w1h:
+                w1h[e], w2h[e] = inp.host_w1(e), inp.host_w2(e)
+        toks = list(range(n_next))
+        t0 = time.perf_counter()
+        ids, w = oracle.route(logits[:n_next], inp.k)
+        if inp.dtype == "fp8":
+            sample_out = oracle.ffn_fp8(x_bits[:n_next], w1h.__getitem__, inp.host_w1_scale(),
+                                        w2h.__getitem__, inp.host_w2_scale(), ids, w, toks)
+        elif inp.dtype == "bf16":
+            sample_out = oracle.ffn(oracle.bf16_bits_to_f64(x_bits[:n_next]),
+                                    lambda e: oracle.bf16_bits_to_f64(w1h[e]),
+                                    lambda e: oracle.bf16_bits_to_f64(w2h[e]), ids, w, toks)
+        else:
+            sample_out = oracle.ffn(x_bits[:n_next].astype(np.float64),
+                                    lambda e: w1h[e].astype(np.float64),
+                                    lambda e: w2h[e].astype(np.float64), ids, w, toks)
+        dt = time.perf_counter() - t0
+        t_spent += dt
+        per_tok.append((n_next, dt))
+        n = n_next
+    n_last, dt_last = per_tok[-1]
+    return {"value": n_last / dt_last, "unit": "tokens/s",
+            "cores": blas_threads, "kind": "oracle",
+            "sample": f"first {n_last} of {inp.T} tokens of the same workload "
+                      f"(oracle route + fp64 FFN incl. bf16/e4m3 decode), {dt_last:.2f} s",
+            "host_cpus": len(os.sched_getaffinity(0))}, sample_out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_expert_ffn_router_amd as moe
+    from synth import CONFIGS, config_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    cfg = CONFIGS[args.config]
+    inp = config_inputs(args.config, device="cuda")
+    T, E, H, I, k, M = inp.T, inp.E, inp.H, inp.I, inp.k, args.block_m
+    S = T * k
+    dev = inp.x.device
+    dt_code = {"f32": moe.MOE_DTYPE_F32, "bf16": moe.MOE_DTYPE_BF16, "fp8": moe.MOE_DTYPE_FP8}[inp.dtype]
+
+    # everything the step writes, allocated once
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+    cap = moe.align_capacity(T, k, E, M)
+    sid = torch.empty(cap, dtype=torch.int32, device=dev)
+    be = torch.empty(cap // M, dtype=torch.int32, device=dev)
+    npad = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = moe.alloc_workspace(T, E, H, I, k, M, dt_code, dev)
+    out = torch.empty((T, H), dtype=torch.float32 if inp.dtype == "f32" else torch.bfloat16,
+                      device=dev)
+
+    def ffn(flags):
+        f = flags | args.flags
+        if inp.dtype == "fp8":
+            moe.ffn_fp8(inp.x, inp.w1, inp.w1_scale, inp.w2, inp.w2_scale, ids, wts, sid, be, npad,
+                        M, f, ws, out)
+        elif inp.dtype == "bf16":
+            moe.ffn_bf16(inp.x, inp.w1, inp.w2, ids, wts, sid, be, npad, M, f, ws, out)
+        else:
+            moe.ffn_f32(inp.x, inp.w1, inp.w2, ids, wts, sid, be, npad, M, f, ws, out)
+
+    stream = torch.cuda.current_stream()
+    n_ev = args.steps
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+
+    def step(i=None):
+        moe.route_topk(inp.logits, k, out=(ids, wts), stream=stream)
+        moe.align_block(ids, E, M, out=(sid, be, npad), stream=stream)
+        if i is not None:
+            ev_a[i].record(stream)
+        ffn(moe.STAGE_FC1)
+        if i is not None:
+            ev_b[i].record(stream)
+        ffn(moe.STAGE_FC2 | moe.STAGE_COMBINE)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    fc1_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]))
+
+    # algorithmic work (active experts from this run's routing)
+    ids_h = ids.cpu().numpy()
+    A = int(np.unique(ids_h).size)
+    bw = {"f32": 4, "bf16": 2, "fp8": 1}[inp.dtype]
+    bx = {"f32": 4, "bf16": 2, "fp8": 2}[inp.dtype]
+    w_bytes = A * 3 * I * H * bw + (A * (2 * I + H) * 4 if inp.dtype == "fp8" else 0)
+    layer_bytes = w_bytes + T * H * bx + T * H * (4 if inp.dtype == "f32" else 2) + T * E * 4 + S * 8
+    flops = S * 6 * H * I
+    fc1_bytes = A * 2 * I * H * bw + (A * 2 * I * 4 if inp.dtype == "fp8" else 0) \
+        + T * H * bx + S * I * (2 if inp.dtype == "bf16" else 4)
+    fc1_gbs = fc1_bytes / (fc1_ms * 1e-3) / 1e9
+    step_s = ms_per_step * 1e-3
+    wl = cfg["name"]
+    roofline = {"bound": "hbm", "achieved": round(fc1_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(fc1_gbs / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic("fc1", wl), "kernel": "fc1 (FC1 gate|up + SiLU*up)",
+                "kernel_ms": round(fc1_ms, 4), "alg_bytes_per_launch": fc1_bytes}
+    rec = {
+        "metric": METRIC, "value": round(T / step_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": inp.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl, "T": T, "E": E, "H": H, "I": I, "k": k, "block_m": M,
+                   "routing": cfg["routing"], "active_experts": A, "seed": 0},
+        "expert_weight_gbps": round(w_bytes / step_s / 1e9, 1),
+        "expert_weight_hbm_frac": round(w_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
+        "layer_alg_bytes": layer_bytes,
+        "tflops": round(flops / step_s / 1e12, 2),
+        "mfma_bf16_frac": round(flops / step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": roofline,
+        "source_digest": source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        cb, _ = cpu_baseline(inp, args.cpu_seconds)
+        rec["cpu_baseline"] = cb
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,203 @@
+/*
+ * moe.h -- C ABI of libmoe.so: the fused MoE expert feed-forward of LLM
+ * serving on one AMD Instinct MI355X (gfx950).
+ *
+ * Path: router softmax + top-k  ->  token-to-expert alignment  ->
+ *       FC1 (gate|up) + SiLU-and-mul  ->  FC2 (down)  ->  top-k weighted combine.
+ *
+ * Sources (web pages; cited by title and section):
+ *  - "vLLM support for NVIDIA Vera Rubin NVL72" (Chinese summary), section
+ *    "Locality domain": in small-token MoE decode the forward pass is dominated
+ *    by reading the FC1/FC2 expert weights from HBM.
+ *  - "vLLM SM architecture adaptation" (Chinese), section 4.3 and the selection
+ *    flow figure of section 9: one fused kernel over all experts, FP8 dequant
+ *    inside the GEMM loop; section 3.1: scaled GEMM with scales applied around
+ *    an fp32 accumulator; section 1: FP8 is E4M3.
+ *  - V100 vLLM fork article (Japanese), "wall 2": silu_and_mul between FC1 and
+ *    FC2; "wall 5": MoE routing kernels and an FP8 activation quantiser.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never frees, keeps or reallocates them. Tensors are row-major, contiguous.
+ *  - bf16 is passed as its uint16_t bit pattern; fp8 is OCP e4m3fn bytes
+ *    (bias 7, max 448, no infinities).
+ *  - Each call validates its arguments on the host, enqueues its kernels on
+ *    `stream` (NULL = the null stream) and returns; it never synchronises the
+ *    host, never allocates device memory and keeps no state between calls
+ *    other than a per-device cache of the device's CU count.
+ *  - On a bad argument nothing is launched and the status says why. A launch
+ *    failure returns MOE_ERR_HIP. Faults inside a kernel surface at the
+ *    caller's next synchronisation, as usual in HIP. Device-resident values
+ *    are not validated (e.g. an expert id outside [0, E) is undefined).
+ *  - Inputs are never written. Calls are reentrant when their outputs and
+ *    workspaces do not overlap.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t* moe_stream_t; /* identical to hipStream_t */
+
+#define MOE_ABI_VERSION 1
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  MOE_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
+  MOE_ERR_WORKSPACE = 4,   /* workspace too small */
+  MOE_ERR_UNSUPPORTED = 5, /* a valid request this build does not serve */
+  MOE_ERR_HIP = 6          /* a HIP runtime call or launch failed */
+} moe_status;
+
+/* Element types of the FFN (argument `dtype` of moe_ffn_workspace_bytes). */
+enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1, MOE_DTYPE_FP8 = 2 };
+
+/* `flags` bits of the moe_ffn_* calls.
+ * Stage bits select which stages run; 0 (no stage bit) runs the whole FFN.
+ * Running the stages in separate calls with the same workspace gives the same
+ * result as one call (the workspace carries the intermediates).
+ *   FC1      : [fp8: per-token activation quantisation +] FC1 gate|up + SiLU*up
+ *   FC2      : [fp8: per-slot quantisation of h +] FC2
+ *   COMBINE  : top-k weighted combine into `out`
+ * MOE_FFN_NO_XCD_REMAP turns off the placement of contiguous weight ranges
+ * on one XCD (for A/B measurement); results are identical either way. */
+#define MOE_FFN_STAGE_FC1 (1u << 0)
+#define MOE_FFN_STAGE_FC2 (1u << 1)
+#define MOE_FFN_STAGE_COMBINE (1u << 2)
+#define MOE_FFN_NO_XCD_REMAP (1u << 8)
+
+/* Human-readable name of a status (static storage, never NULL). */
+const char* moe_status_str(moe_status s);
+
+/* MOE_ABI_VERSION of the loaded library. */
+int moe_abi_version(void);
+
+/*
+ * Router softmax + top-k.
+ * Passage: the Vera Rubin page ("hardware growth vs bottlenecks") links FP32
+ * exp throughput to softmax; the V100 article ("wall 5") names the MoE routing
+ * kernels. The ordering rule is this library's reading (the pages give none).
+ *
+ *  logits        [T, E] float32, device.
+ *  topk_ids      [T, k] int32, device, written: for each token the k experts
+ *                first in the order (logit descending, expert index ascending;
+ *                -0.0 equals +0.0; -inf sorts last). Slot j is the j-th.
+ *  topk_weights  [T, k] float32, device, written: p[e] = softmax(logits[t])[e]
+ *                of each chosen expert, computed in fp32; divided by the sum
+ *                of the k chosen p when renormalize != 0.
+ *  Limits: 0 <= T, 1 <= E <= 1024, 1 <= k <= E. T == 0 launches nothing.
+ *  NaN logits, or a row whose logits are all -inf, are outside the contract.
+ */
+moe_status moe_route_topk(const float* logits, int T, int E, int k, int renormalize,
+                          int32_t* topk_ids, float* topk_weights, moe_stream_t stream);
+
+/*
+ * Token-to-expert alignment.
+ * Passage: "vLLM SM architecture adaptation", section 4.3 and the section 9
+ * figure run the MoE layer as one fused kernel over all experts; the index
+ * structure such a kernel needs is this library's reading.
+ *
+ * moe_align_capacity returns the number of int32 elements `sorted_ids` must
+ * hold: round_up(S + min(E, S) * (block_m - 1), block_m), S = T * k. The
+ * number of blocks is capacity / block_m (the length of `block_expert`).
+ *
+ *  topk_ids      [T, k] int32, device: expert of flat slot s = t*k + j.
+ *  sorted_ids    [capacity] int32, device, written: for e = 0..E-1 the slots
+ *                routed to e in ascending s, each expert's run padded to a
+ *                multiple of block_m with the sentinel S. Entries at and past
+ *                *num_padded also hold S.
+ *  block_expert  [capacity / block_m] int32, device, written: the expert of
+ *                each block; -1 for blocks at and past *num_padded / block_m.
+ *  num_padded    [1] int32, device, written: total padded length (a multiple
+ *                of block_m).
+ *  Limits: 0 <= T, 1 <= E <= 1024, 1 <= k <= E, T * k < 2^24, block_m a power
+ *  of two in [1, 256]. The result is deterministic (no order-dependent atomics).
+ */
+size_t moe_align_capacity(int T, int k, int E, int block_m);
+moe_status moe_align_block(const int32_t* topk_ids, int T, int k, int E, int block_m,
+                           int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
+                           moe_stream_t stream);
+
+/*
+ * Bytes of device workspace the FFN needs (dtype = MOE_DTYPE_*). Base must be
+ * 256-byte aligned; its contents need no initialisation. Layout, S = T*k,
+ * each region starting at the next 256-byte boundary after the previous one:
+ *   bf16: h bf16 [S, I] | y f32 [S, H]
+ *   fp8 : h f32 [S, I] | hq e4m3 [S, I] | hs f32 [S] | xq e4m3 [T, H] |
+ *         xs f32 [T] | y f32 [S, H]
+ *   f32 : h f32 [S, I] | y f32 [S, H]
+ * h = SiLU(gate) * up and y = FC2 output, both indexed by flat slot
+ * s = t*k + j; hq/hs and xq/xs are the quantised h and x with their scales.
+ */
+size_t moe_ffn_workspace_bytes(int T, int E, int H, int I, int k, int block_m, int dtype);
+
+/*
+ * FFN, bf16 weights and activations, fp32 accumulation.
+ * Passage: FC1/FC2 of the Vera Rubin page ("Locality domain"); silu_and_mul of
+ * the V100 article ("wall 2"); the combine (sum over a token's k slots of
+ * weight x expert output) is the plain reading of a top-k MoE layer.
+ *
+ *  x             [T, H] bf16.
+ *  w1            [E, 2I, H] bf16: rows [0, I) gate, rows [I, 2I) up.
+ *  w2            [E, H, I] bf16.
+ *  topk_ids, topk_weights   from moe_route_topk (weights are read by COMBINE).
+ *  sorted_ids, block_expert, num_padded   from moe_align_block with the same
+ *                T, k, E and block_m.
+ *  out           [T, H] bf16, written: out[t] = sum_j w[t,j] * y[t*k+j],
+ *                accumulated in fp32 in j order, rounded once (RNE).
+ *  Intermediate h is rounded to bf16 before FC2.
+ *  Limits: 0 <= T, 1 <= E <= 1024, 1 <= k <= E, T * k < 2^24, H and I
+ *  multiples of 128, block_m a power of two in [1, 256]; x, w1, w2, out and
+ *  workspace 16-byte aligned (workspace 256-byte aligned).
+ */
+moe_status moe_ffn_bf16(const uint16_t* x, const uint16_t* w1, const uint16_t* w2,
+                        const int32_t* topk_ids, const float* topk_weights,
+                        const int32_t* sorted_ids, const int32_t* block_expert,
+                        const int32_t* num_padded, int T, int E, int H, int I, int k,
+                        int block_m, unsigned flags, void* workspace, size_t workspace_bytes,
+                        uint16_t* out, moe_stream_t stream);
+
+/*
+ * FFN, W8A8 OCP fp8 e4m3fn with fp32 accumulation (scaled-GEMM semantics of
+ * "vLLM SM architecture adaptation" section 3.1; FP8 activation quantiser of
+ * the V100 article, "wall 5").
+ *
+ *  x             [T, H] bf16; quantised inside per token: a_t = absmax/448
+ *                (fp32; 1 for a zero row), code = e4m3fn_rne_sat(x / a_t).
+ *  w1            [E, 2I, H] e4m3fn codes, w1_scale [E, 2I] fp32 per output row.
+ *  w2            [E, H, I] e4m3fn codes, w2_scale [E, H] fp32 per output row.
+ *  h = SiLU(g) * u is formed in fp32 with g = acc * w1_scale * a_t (likewise u)
+ *  and quantised per (token, expert) slot row the same way before FC2;
+ *  y = acc * w2_scale * b_s. Other arguments and limits as moe_ffn_bf16.
+ */
+moe_status moe_ffn_fp8(const uint16_t* x, const uint8_t* w1, const float* w1_scale,
+                       const uint8_t* w2, const float* w2_scale, const int32_t* topk_ids,
+                       const float* topk_weights, const int32_t* sorted_ids,
+                       const int32_t* block_expert, const int32_t* num_padded, int T, int E,
+                       int H, int I, int k, int block_m, unsigned flags, void* workspace,
+                       size_t workspace_bytes, uint16_t* out, moe_stream_t stream);
+
+/*
+ * FFN, fp32 throughout (small problems; plain wave-per-output kernels, not a
+ * performance path). Same semantics as moe_ffn_bf16 with float32 x, w1, w2,
+ * h and out. Limits: H and I multiples of 4; otherwise as moe_ffn_bf16.
+ */
+moe_status moe_ffn_f32(const float* x, const float* w1, const float* w2,
+                       const int32_t* topk_ids, const float* topk_weights,
+                       const int32_t* sorted_ids, const int32_t* block_expert,
+                       const int32_t* num_padded, int T, int E, int H, int I, int k,
+                       int block_m, unsigned flags, void* workspace, size_t workspace_bytes,
+                       float* out, moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

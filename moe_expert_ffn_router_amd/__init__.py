@@ -1,0 +1,250 @@
+"""Thin Python binding of libmoe.so (fused MoE expert FFN on MI355X / gfx950).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libmoe.so; torch supplies device memory and the current stream. Importing the
+package loads the library and raises if it has not been built; nothing here
+computes a result on the CPU.
+
+The names mirror the C ABI in include/moe.h:
+
+    route_topk(logits, k, renormalize=False)           -> (topk_ids, topk_weights)
+    align_block(topk_ids, E, block_m)                   -> (sorted_ids, block_expert, num_padded)
+    ffn_bf16(x, w1, w2, ids, wts, sorted_ids, block_expert, num_padded, block_m, ...) -> out
+    ffn_fp8(x, w1, w1_scale, w2, w2_scale, ids, wts, ..., block_m, ...)              -> out
+    ffn_f32(x, w1, w2, ids, wts, ..., block_m, ...)                                 -> out
+    forward(x, logits, w1, w2, k, ...)   convenience chaining of the three calls
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch  # loads torch's HIP runtime first; libmoe.so then binds to the same one
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK = 0
+MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_FP8 = 0, 1, 2
+STAGE_FC1, STAGE_FC2, STAGE_COMBINE = 1 << 0, 1 << 1, 1 << 2
+NO_XCD_REMAP = 1 << 8
+ABI_VERSION = 1
+
+EXPORTS = ("moe_status_str", "moe_abi_version", "moe_route_topk", "moe_align_capacity",
+           "moe_align_block", "moe_ffn_workspace_bytes", "moe_ffn_bf16", "moe_ffn_fp8",
+           "moe_ffn_f32")
+
+
+class MoEError(RuntimeError):
+    """A libmoe call returned a non-OK status."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(or python -m moe_expert_ffn_router_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, U, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
+    lib.moe_status_str.restype = ctypes.c_char_p
+    lib.moe_status_str.argtypes = [I]
+    lib.moe_abi_version.restype = I
+    lib.moe_abi_version.argtypes = []
+    lib.moe_route_topk.restype = I
+    lib.moe_route_topk.argtypes = [P, I, I, I, I, P, P, P]
+    lib.moe_align_capacity.restype = Z
+    lib.moe_align_capacity.argtypes = [I, I, I, I]
+    lib.moe_align_block.restype = I
+    lib.moe_align_block.argtypes = [P, I, I, I, I, P, P, P, P]
+    lib.moe_ffn_workspace_bytes.restype = Z
+    lib.moe_ffn_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    ffn_tail = [P, P, P, P, P, I, I, I, I, I, I, U, P, Z, P, P]
+    lib.moe_ffn_bf16.restype = I
+    lib.moe_ffn_bf16.argtypes = [P, P, P] + ffn_tail
+    lib.moe_ffn_f32.restype = I
+    lib.moe_ffn_f32.argtypes = [P, P, P] + ffn_tail
+    lib.moe_ffn_fp8.restype = I
+    lib.moe_ffn_fp8.argtypes = [P, P, P, P, P] + ffn_tail
+    if lib.moe_abi_version() != ABI_VERSION:
+        raise ImportError(f"libmoe ABI {lib.moe_abi_version()} != binding ABI {ABI_VERSION}")
+    return lib
+
+
+lib = _load()
+
+
+def status_str(s: int) -> str:
+    return lib.moe_status_str(s).decode()
+
+
+def _check(s: int) -> None:
+    if s != MOE_OK:
+        raise MoEError(s, status_str(s))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream: Optional[torch.cuda.Stream]) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtypes, device=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device (cuda/hip) tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ------------------------------------------------------------- routing ---
+
+def route_topk(logits: torch.Tensor, k: int, renormalize: bool = False, out=None,
+               stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Router softmax + top-k (moe_route_topk). logits [T, E] float32."""
+    _need(logits, "logits", (torch.float32,))
+    T, E = logits.shape
+    if out is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+        wts = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    else:
+        ids, wts = out
+    _check(lib.moe_route_topk(_ptr(logits), T, E, k, int(bool(renormalize)), _ptr(ids),
+                              _ptr(wts), _stream(stream)))
+    return ids, wts
+
+
+def align_capacity(T: int, k: int, E: int, block_m: int) -> int:
+    return int(lib.moe_align_capacity(T, k, E, block_m))
+
+
+def align_block(topk_ids: torch.Tensor, E: int, block_m: int, out=None, stream=None):
+    """Token-to-expert alignment (moe_align_block). Returns device tensors
+    (sorted_ids [cap], block_expert [cap/block_m], num_padded [1])."""
+    _need(topk_ids, "topk_ids", (torch.int32,))
+    T, k = topk_ids.shape
+    cap = align_capacity(T, k, E, block_m)
+    if out is None:
+        dev = topk_ids.device
+        sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
+        block_expert = torch.empty(cap // max(block_m, 1), dtype=torch.int32, device=dev)
+        num_padded = torch.empty(1, dtype=torch.int32, device=dev)
+    else:
+        sorted_ids, block_expert, num_padded = out
+    _check(lib.moe_align_block(_ptr(topk_ids), T, k, E, block_m, _ptr(sorted_ids),
+                               _ptr(block_expert), _ptr(num_padded), _stream(stream)))
+    return sorted_ids, block_expert, num_padded
+
+
+# ----------------------------------------------------------------- FFN ---
+
+def workspace_bytes(T: int, E: int, H: int, I: int, k: int, block_m: int, dtype: int) -> int:
+    return int(lib.moe_ffn_workspace_bytes(T, E, H, I, k, block_m, dtype))
+
+
+def alloc_workspace(T, E, H, I, k, block_m, dtype, device) -> torch.Tensor:
+    n = workspace_bytes(T, E, H, I, k, block_m, dtype)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _ffn_common(x, ids, wts, sorted_ids, block_expert, num_padded):
+    _need(ids, "topk_ids", (torch.int32,), x.device)
+    _need(wts, "topk_weights", (torch.float32,), x.device)
+    _need(sorted_ids, "sorted_ids", (torch.int32,), x.device)
+    _need(block_expert, "block_expert", (torch.int32,), x.device)
+    _need(num_padded, "num_padded", (torch.int32,), x.device)
+
+
+def ffn_bf16(x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert, num_padded,
+             block_m: int, flags: int = 0, workspace=None, out=None, stream=None):
+    """moe_ffn_bf16: x [T,H], w1 [E,2I,H], w2 [E,H,I] bfloat16 -> out [T,H] bfloat16."""
+    _need(x, "x", (torch.bfloat16,))
+    _need(w1, "w1", (torch.bfloat16,), x.device)
+    _need(w2, "w2", (torch.bfloat16,), x.device)
+    _ffn_common(x, topk_ids, topk_weights, sorted_ids, block_expert, num_padded)
+    T, H = x.shape
+    E, I2, _ = w1.shape
+    k = topk_ids.shape[1]
+    if workspace is None:
+        workspace = alloc_workspace(T, E, H, I2 // 2, k, block_m, MOE_DTYPE_BF16, x.device)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _check(lib.moe_ffn_bf16(_ptr(x), _ptr(w1), _ptr(w2), _ptr(topk_ids), _ptr(topk_weights),
+                            _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded), T, E, H,
+                            I2 // 2, k, block_m, flags, _ptr(workspace), workspace.numel(),
+                            _ptr(out), _stream(stream)))
+    return out
+
+
+def ffn_fp8(x, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids, block_expert,
+            num_padded, block_m: int, flags: int = 0, workspace=None, out=None, stream=None):
+    """moe_ffn_fp8: x [T,H] bfloat16; w1 [E,2I,H], w2 [E,H,I] e4m3fn codes (uint8 or
+    float8_e4m3fn) with float32 per-output-row scales -> out [T,H] bfloat16."""
+    fp8 = (torch.uint8, torch.float8_e4m3fn)
+    _need(x, "x", (torch.bfloat16,))
+    _need(w1, "w1", fp8, x.device)
+    _need(w2, "w2", fp8, x.device)
+    _need(w1_scale, "w1_scale", (torch.float32,), x.device)
+    _need(w2_scale, "w2_scale", (torch.float32,), x.device)
+    _ffn_common(x, topk_ids, topk_weights, sorted_ids, block_expert, num_padded)
+    T, H = x.shape
+    E, I2, _ = w1.shape
+    k = topk_ids.shape[1]
+    if workspace is None:
+        workspace = alloc_workspace(T, E, H, I2 // 2, k, block_m, MOE_DTYPE_FP8, x.device)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _check(lib.moe_ffn_fp8(_ptr(x), _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale),
+                           _ptr(topk_ids), _ptr(topk_weights), _ptr(sorted_ids),
+                           _ptr(block_expert), _ptr(num_padded), T, E, H, I2 // 2, k, block_m,
+                           flags, _ptr(workspace), workspace.numel(), _ptr(out),
+                           _stream(stream)))
+    return out
+
+
+def ffn_f32(x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert, num_padded,
+            block_m: int, flags: int = 0, workspace=None, out=None, stream=None):
+    """moe_ffn_f32: float32 throughout."""
+    _need(x, "x", (torch.float32,))
+    _need(w1, "w1", (torch.float32,), x.device)
+    _need(w2, "w2", (torch.float32,), x.device)
+    _ffn_common(x, topk_ids, topk_weights, sorted_ids, block_expert, num_padded)
+    T, H = x.shape
+    E, I2, _ = w1.shape
+    k = topk_ids.shape[1]
+    if workspace is None:
+        workspace = alloc_workspace(T, E, H, I2 // 2, k, block_m, MOE_DTYPE_F32, x.device)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    _check(lib.moe_ffn_f32(_ptr(x), _ptr(w1), _ptr(w2), _ptr(topk_ids), _ptr(topk_weights),
+                           _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded), T, E, H,
+                           I2 // 2, k, block_m, flags, _ptr(workspace), workspace.numel(),
+                           _ptr(out), _stream(stream)))
+    return out
+
+
+def forward(x, logits, w1, w2, k: int, block_m: int = 64, renormalize: bool = False,
+            w1_scale=None, w2_scale=None, flags: int = 0, stream=None):
+    """route_topk -> align_block -> ffn_{f32,bf16,fp8}, dtype taken from w1."""
+    E = w1.shape[0]
+    ids, wts = route_topk(logits, k, renormalize, stream=stream)
+    sorted_ids, block_expert, num_padded = align_block(ids, E, block_m, stream=stream)
+    if w1.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return ffn_fp8(x, w1, w1_scale, w2, w2_scale, ids, wts, sorted_ids, block_expert,
+                       num_padded, block_m, flags, stream=stream)
+    if w1.dtype == torch.bfloat16:
+        return ffn_bf16(x, w1, w2, ids, wts, sorted_ids, block_expert, num_padded, block_m,
+                        flags, stream=stream)
+    return ffn_f32(x, w1, w2, ids, wts, sorted_ids, block_expert, num_padded, block_m, flags,
+                   stream=stream)

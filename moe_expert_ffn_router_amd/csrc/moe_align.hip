@@ -1,0 +1,144 @@
+// Token-to-expert alignment: a deterministic stable counting sort of the flat
+// slots s = t*k + j by expert, each expert's run padded to a multiple of
+// block_m with the sentinel S.
+//
+// Pages: "vLLM SM architecture adaptation", section 4.3 and the selection-flow
+// figure of section 9, run the MoE layer as one fused kernel over all experts;
+// the block-aligned index lists such a kernel walks are this library's reading.
+//
+// One workgroup of 8 waves. Wave w owns the contiguous slot range
+// [w*per, (w+1)*per). (1) each wave histograms its range into its own LDS row
+// (atomic increments: counts do not depend on order); (2) padded run lengths
+// and their exclusive scan give each expert's offset; (3) a per-(wave, expert)
+// base = offset + counts of lower waves; (4) each wave re-walks its range 64
+// slots at a time: lanes holding the same expert are found with one ballot per
+// expert-id bit, a lane's rank is the number of such lanes below it, and the
+// group's leader advances the wave's running base. Every placement follows from
+// slot order alone, so the output is identical on every run.
+#include "moe_common.h"
+#include "moe_launch.h"
+
+namespace moe {
+
+constexpr int kAlignWaves = 8;
+constexpr int kAlignThreads = kAlignWaves * kWave;
+constexpr int kAlignMaxE = 1024;
+constexpr int kAlignUnroll = 4;
+
+__global__ __launch_bounds__(kAlignThreads) void align_kernel(
+    const int32_t* __restrict__ ids, int S, int E, int log2m, int cap,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
+    int32_t* __restrict__ num_padded) {
+  __shared__ int cnt[kAlignWaves][kAlignMaxE];  // per-wave histograms, then per-wave bases
+  __shared__ int off[kAlignMaxE + 1];           // padded exclusive offsets; off[E] = total
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int M = 1 << log2m;
+
+  for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) cnt[i / E][i % E] = 0;
+  for (int i = tid; i < cap; i += kAlignThreads) sorted_ids[i] = S;
+  for (int i = tid; i < (cap >> log2m); i += kAlignThreads) block_expert[i] = -1;
+  __syncthreads();
+
+  const int per = (S + kAlignWaves - 1) / kAlignWaves;
+  const int s0 = min(S, w * per), s1 = min(S, s0 + per);
+
+  // (1) per-wave histogram
+  for (int sb = s0; sb < s1; sb += kWave * kAlignUnroll) {
+    int e[kAlignUnroll];
+#pragma unroll
+    for (int u = 0; u < kAlignUnroll; ++u) {
+      const int s = sb + u * kWave + lane;
+      e[u] = s < s1 ? ids[s] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kAlignUnroll; ++u)
+      if (e[u] >= 0) atomicAdd(&cnt[w][e[u]], 1);
+  }
+  __syncthreads();
+
+  // (2) padded run length per expert, then exclusive scan by wave 0
+  for (int e = tid; e < E; e += kAlignThreads) {
+    int c = 0;
+#pragma unroll
+    for (int q = 0; q < kAlignWaves; ++q) c += cnt[q][e];
+    off[e] = ((c + M - 1) >> log2m) << log2m;
+  }
+  __syncthreads();
+  if (w == 0) {
+    const int chunk = (E + kWave - 1) / kWave;
+    const int e0 = min(E, lane * chunk), e1 = min(E, e0 + chunk);
+    int local = 0;
+    for (int e = e0; e < e1; ++e) local += off[e];
+    int incl = local;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    int run = incl - local;
+    for (int e = e0; e < e1; ++e) {
+      const int pe = off[e];
+      off[e] = run;
+      run += pe;
+    }
+    if (lane == kWave - 1) off[E] = incl;
+  }
+  __syncthreads();
+
+  // (3) per-(wave, expert) bases and the block -> expert map
+  for (int e = tid; e < E; e += kAlignThreads) {
+    int run = off[e];
+#pragma unroll
+    for (int q = 0; q < kAlignWaves; ++q) {
+      const int c = cnt[q][e];
+      cnt[q][e] = run;
+      run += c;
+    }
+    const int b1 = off[e + 1] >> log2m;
+    for (int b = off[e] >> log2m; b < b1; ++b) block_expert[b] = e;
+  }
+  if (tid == 0) num_padded[0] = off[E];
+  __syncthreads();
+
+  // (4) stable scatter, 64 slots at a time in slot order
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+  for (int sb = s0; sb < s1; sb += kWave * kAlignUnroll) {
+    int ev[kAlignUnroll];
+#pragma unroll
+    for (int u = 0; u < kAlignUnroll; ++u) {
+      const int s = sb + u * kWave + lane;
+      ev[u] = s < s1 ? ids[s] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kAlignUnroll; ++u) {
+      const int s = sb + u * kWave + lane;
+      const bool valid = ev[u] >= 0;
+      const int e = valid ? ev[u] : 0;
+      uint64_t same = __ballot(valid);
+      for (int bit = 0; bit < nbits; ++bit) {
+        const bool one = (e >> bit) & 1;
+        const uint64_t b = __ballot(valid && one);
+        same &= one ? b : ~b;
+      }
+      const int rank = __popcll(same & below);
+      const int tot = __popcll(same);
+      int base = 0;
+      if (valid) base = cnt[w][e];
+      if (valid) sorted_ids[base + rank] = s;
+      if (valid && rank == 0) cnt[w][e] = base + tot;
+    }
+  }
+}
+
+hipError_t launch_align(const int32_t* ids, int S, int E, int block_m, int cap,
+                        int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
+                        hipStream_t stream) {
+  int log2m = 0;
+  while ((1 << log2m) < block_m) ++log2m;
+  align_kernel<<<1, kAlignThreads, 0, stream>>>(ids, S, E, log2m, cap, sorted_ids, block_expert,
+                                                num_padded);
+  return hipGetLastError();
+}
+
+}  // namespace moe

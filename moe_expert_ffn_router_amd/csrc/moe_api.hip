@@ -1,0 +1,181 @@
+// C ABI of libmoe.so: argument validation, then the launchers. Declared in
+// include/moe.h; every export is listed there with its meaning and limits.
+#include <hip/hip_runtime.h>
+
+#include <limits.h>
+
+#include "../../include/moe.h"
+#include "moe_launch.h"
+
+#define MOE_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kMaxE = 1024;
+constexpr long kMaxSlots = 1L << 24;
+
+bool is_pow2_le256(int v) { return v >= 1 && v <= 256 && (v & (v - 1)) == 0; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+moe_status check_common(int T, int E, int k) {
+  if (T < 0 || E < 1 || E > kMaxE || k < 1 || k > E) return MOE_ERR_SHAPE;
+  if ((long)T * k >= kMaxSlots || (long)T * E > INT_MAX) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+size_t capacity(long S, int E, int block_m) {
+  const long active = S < E ? S : E;
+  const long cap = S + active * (block_m - 1);
+  return (size_t)((cap + block_m - 1) / block_m * block_m);
+}
+
+// Validation shared by the three FFN entry points.
+moe_status check_ffn(const void* x, const void* w1, const void* w2, const int32_t* topk_ids,
+                     const float* topk_weights, const int32_t* sorted_ids,
+                     const int32_t* block_expert, const int32_t* num_padded, int T, int E, int H,
+                     int I, int k, int block_m, unsigned flags, const void* workspace,
+                     size_t workspace_bytes, const void* out, int dtype) {
+  moe_status s = check_common(T, E, k);
+  if (s != MOE_OK) return s;
+  const int mult = dtype == MOE_DTYPE_F32 ? 4 : 128;
+  if (H < mult || I < mult || H % mult != 0 || I % mult != 0) return MOE_ERR_SHAPE;
+  if (!is_pow2_le256(block_m)) return MOE_ERR_SHAPE;
+  const unsigned known = MOE_FFN_STAGE_FC1 | MOE_FFN_STAGE_FC2 | MOE_FFN_STAGE_COMBINE |
+                         MOE_FFN_NO_XCD_REMAP;
+  if (flags & ~known) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w1 || !w2 || !topk_ids || !topk_weights || !sorted_ids || !block_expert ||
+      !num_padded || !workspace || !out)
+    return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(out, 16) ||
+      !aligned(workspace, 256) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4) ||
+      !aligned(sorted_ids, 4) || !aligned(block_expert, 4) || !aligned(num_padded, 4))
+    return MOE_ERR_ALIGN;
+  if (workspace_bytes < moe::ffn_workspace_layout(T, H, I, k, dtype).total)
+    return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+moe::FfnProblem problem(const void* x, const void* w1, const float* w1s, const void* w2,
+                        const float* w2s, const int32_t* topk_ids, const float* topk_weights,
+                        const int32_t* sorted_ids, const int32_t* block_expert,
+                        const int32_t* num_padded, int T, int E, int H, int I, int k,
+                        int block_m, unsigned flags, void* workspace, void* out) {
+  return moe::FfnProblem{x, w1, w1s, w2, w2s, topk_ids, topk_weights, sorted_ids, block_expert,
+                         num_padded, T, E, H, I, k, block_m, flags, workspace, out};
+}
+
+}  // namespace
+
+MOE_EXPORT const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: a size is out of range or inconsistent";
+    case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: a pointer is not suitably aligned";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: request not served by this build";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP runtime call or kernel launch failed";
+  }
+  return "MOE_ERR_UNKNOWN: not a moe_status value";
+}
+
+MOE_EXPORT int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+MOE_EXPORT moe_status moe_route_topk(const float* logits, int T, int E, int k, int renormalize,
+                                     int32_t* topk_ids, float* topk_weights,
+                                     moe_stream_t stream) {
+  moe_status s = check_common(T, E, k);
+  if (s != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_weights) return MOE_ERR_NULL;
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4))
+    return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_route_topk(logits, T, E, k, renormalize ? 1 : 0, topk_ids,
+                                           topk_weights, (hipStream_t)stream));
+}
+
+MOE_EXPORT size_t moe_align_capacity(int T, int k, int E, int block_m) {
+  if (check_common(T, E, k) != MOE_OK || !is_pow2_le256(block_m)) return 0;
+  return capacity((long)T * k, E, block_m);
+}
+
+MOE_EXPORT moe_status moe_align_block(const int32_t* topk_ids, int T, int k, int E, int block_m,
+                                      int32_t* sorted_ids, int32_t* block_expert,
+                                      int32_t* num_padded, moe_stream_t stream) {
+  moe_status s = check_common(T, E, k);
+  if (s != MOE_OK) return s;
+  if (!is_pow2_le256(block_m)) return MOE_ERR_SHAPE;
+  const long S = (long)T * k;
+  const size_t cap = capacity(S, E, block_m);
+  if (!num_padded) return MOE_ERR_NULL;
+  if (S > 0 && !topk_ids) return MOE_ERR_NULL;
+  if (cap > 0 && (!sorted_ids || !block_expert)) return MOE_ERR_NULL;
+  if (!aligned(topk_ids, 4) || !aligned(sorted_ids, 4) || !aligned(block_expert, 4) ||
+      !aligned(num_padded, 4))
+    return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_align(topk_ids, (int)S, E, block_m, (int)cap, sorted_ids,
+                                      block_expert, num_padded, (hipStream_t)stream));
+}
+
+MOE_EXPORT size_t moe_ffn_workspace_bytes(int T, int E, int H, int I, int k, int block_m,
+                                          int dtype) {
+  (void)E;
+  (void)block_m;
+  if (dtype != MOE_DTYPE_F32 && dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8) return 0;
+  if (T < 0 || H < 1 || I < 1 || k < 1) return 0;
+  return moe::ffn_workspace_layout(T, H, I, k, dtype).total;
+}
+
+MOE_EXPORT moe_status moe_ffn_bf16(const uint16_t* x, const uint16_t* w1, const uint16_t* w2,
+                                   const int32_t* topk_ids, const float* topk_weights,
+                                   const int32_t* sorted_ids, const int32_t* block_expert,
+                                   const int32_t* num_padded, int T, int E, int H, int I, int k,
+                                   int block_m, unsigned flags, void* workspace,
+                                   size_t workspace_bytes, uint16_t* out, moe_stream_t stream) {
+  moe_status s = check_ffn(x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert,
+                           num_padded, T, E, H, I, k, block_m, flags, workspace, workspace_bytes,
+                           out, MOE_DTYPE_BF16);
+  if (s != MOE_OK || T == 0) return s;
+  return hip_status(moe::launch_ffn_bf16(
+      problem(x, w1, nullptr, w2, nullptr, topk_ids, topk_weights, sorted_ids, block_expert,
+              num_padded, T, E, H, I, k, block_m, flags, workspace, out),
+      (hipStream_t)stream));
+}
+
+MOE_EXPORT moe_status moe_ffn_fp8(const uint16_t* x, const uint8_t* w1, const float* w1_scale,
+                                  const uint8_t* w2, const float* w2_scale,
+                                  const int32_t* topk_ids, const float* topk_weights,
+                                  const int32_t* sorted_ids, const int32_t* block_expert,
+                                  const int32_t* num_padded, int T, int E, int H, int I, int k,
+                                  int block_m, unsigned flags, void* workspace,
+                                  size_t workspace_bytes, uint16_t* out, moe_stream_t stream) {
+  moe_status s = check_ffn(x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert,
+                           num_padded, T, E, H, I, k, block_m, flags, workspace, workspace_bytes,
+                           out, MOE_DTYPE_FP8);
+  if (s != MOE_OK || T == 0) return s;
+  if (!w1_scale || !w2_scale) return MOE_ERR_NULL;
+  if (!aligned(w1_scale, 16) || !aligned(w2_scale, 16)) return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_ffn_fp8(
+      problem(x, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids, block_expert,
+              num_padded, T, E, H, I, k, block_m, flags, workspace, out),
+      (hipStream_t)stream));
+}
+
+MOE_EXPORT moe_status moe_ffn_f32(const float* x, const float* w1, const float* w2,
+                                  const int32_t* topk_ids, const float* topk_weights,
+                                  const int32_t* sorted_ids, const int32_t* block_expert,
+                                  const int32_t* num_padded, int T, int E, int H, int I, int k,
+                                  int block_m, unsigned flags, void* workspace,
+                                  size_t workspace_bytes, float* out, moe_stream_t stream) {
+  moe_status s = check_ffn(x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert,
+                           num_padded, T, E, H, I, k, block_m, flags, workspace, workspace_bytes,
+                           out, MOE_DTYPE_F32);
+  if (s != MOE_OK || T == 0) return s;
+  return hip_status(moe::launch_ffn_f32(
+      problem(x, w1, nullptr, w2, nullptr, topk_ids, topk_weights, sorted_ids, block_expert,
+              num_padded, T, E, H, I, k, block_m, flags, workspace, out),
+      (hipStream_t)stream));
+}

@@ -1,0 +1,51 @@
+// Internal launchers (host side). Arguments are validated by the C ABI layer
+// before any of these is called; each only enqueues kernels on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int renorm, int32_t* ids,
+                             float* wts, hipStream_t stream);
+
+hipError_t launch_align(const int32_t* ids, int S, int E, int block_m, int cap,
+                        int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
+                        hipStream_t stream);
+
+// Workspace carve-up shared by the FFN launchers and moe_ffn_workspace_bytes.
+struct FfnWorkspace {
+  size_t h_off, h_bytes;    // h per slot: bf16 [S, I] (bf16), f32 [S, I] (fp8, f32)
+  size_t hq_off, hq_bytes;  // fp8: e4m3 codes of h [S, I]
+  size_t hs_off, hs_bytes;  // fp8: per-slot scale of h [S]
+  size_t xq_off, xq_bytes;  // fp8: e4m3 codes of x [T, H]
+  size_t xs_off, xs_bytes;  // fp8: per-token scale of x [T]
+  size_t y_off, y_bytes;    // per-slot FC2 output, f32 [S, H]
+  size_t total;
+};
+FfnWorkspace ffn_workspace_layout(int T, int H, int I, int k, int dtype);
+
+struct FfnProblem {
+  const void* x;
+  const void* w1;
+  const float* w1_scale;
+  const void* w2;
+  const float* w2_scale;
+  const int32_t* topk_ids;
+  const float* topk_weights;
+  const int32_t* sorted_ids;
+  const int32_t* block_expert;
+  const int32_t* num_padded;
+  int T, E, H, I, k, block_m;
+  unsigned flags;
+  void* workspace;
+  void* out;
+};
+
+hipError_t launch_ffn_bf16(const FfnProblem& p, hipStream_t stream);
+hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream);
+hipError_t launch_ffn_f32(const FfnProblem& p, hipStream_t stream);
+
+}  // namespace moe

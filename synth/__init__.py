@@ -1,2 +1,3 @@
 """Seeded synthetic workloads for the fused MoE expert FFN (see synth.moe_inputs)."""
-from .moe_inputs import CONFIGS, MoEInputs, make_inputs, config_inputs, fingerprint  # noqa: F401
+from .moe_inputs import (CONFIGS, MoEInputs, config_inputs, draw_topk_ids,  # noqa: F401
+                         fingerprint, make_inputs)

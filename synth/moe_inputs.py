@@ -223,3 +223,29 @@ def fingerprint(inp: MoEInputs) -> str:
     h.update(np.ascontiguousarray(inp.host_x()).tobytes())
     h.update(np.ascontiguousarray(inp.host_logits()).tobytes())
     return h.hexdigest()
+
+
+def draw_topk_ids(T: int, E: int, k: int, seed: int = 0, kind: str = "uniform",
+                  zipf_s: float = 1.2) -> np.ndarray:
+    """Random expert ids [T, k] int32, k distinct experts per token, for tests
+    of the alignment step in isolation. ``kind``: "uniform" (each token a
+    uniformly random k-subset in random order), "zipf" (subset drawn by
+    popularity (rank+1)^-s), "one" (every token's slot 0 is expert 0: one
+    expert holds T slots)."""
+    rng = np.random.default_rng(seed)
+    ids = np.empty((T, k), dtype=np.int32)
+    if kind == "zipf":
+        perm = rng.permutation(E)
+        p = (perm + 1.0) ** (-zipf_s)
+        p /= p.sum()
+    for t in range(T):
+        if kind == "zipf":
+            ids[t] = rng.choice(E, size=k, replace=False, p=p)
+        else:
+            ids[t] = rng.permutation(E)[:k]
+            if kind == "one" and 0 not in ids[t, :1]:
+                pos = np.nonzero(ids[t] == 0)[0]
+                if pos.size:
+                    ids[t, pos[0]] = ids[t, 0]
+                ids[t, 0] = 0
+    return ids

@@ -1,0 +1,136 @@
+"""The C ABI library loads without a GPU, exports exactly what include/moe.h
+declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+m = pytest.importorskip("moe_expert_ffn_router_amd")
+lib = m.lib
+OK, NULL, SHAPE, ALIGN, WORKSPACE, UNSUP = 0, 1, 2, 3, 4, 5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(moe_\w+)\s*\(", text, flags=re.M))
+
+
+def exported_functions():
+    out = subprocess.run(["nm", "-D", "--defined-only", m.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    return {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+
+
+def test_exports_match_header_exactly():
+    decl = declared_functions()
+    assert decl == set(m.EXPORTS)
+    assert exported_functions() == decl
+    for name in decl:
+        assert hasattr(lib, name)
+
+
+def test_abi_version_and_status_strings():
+    assert lib.moe_abi_version() == 1
+    for s in range(7):
+        assert m.status_str(s).startswith("MOE_")
+    assert "UNKNOWN" in m.status_str(99)
+
+
+P = 0x1000  # a 4 KiB-aligned fake device address: never dereferenced on these paths
+
+
+def test_route_validation():
+    f = lib.moe_route_topk
+    assert f(P, 4, 0, 1, 0, P, P, None) == SHAPE          # E < 1
+    assert f(P, 4, 1025, 1, 0, P, P, None) == SHAPE       # E > 1024
+    assert f(P, 4, 8, 0, 0, P, P, None) == SHAPE          # k < 1
+    assert f(P, 4, 8, 9, 0, P, P, None) == SHAPE          # k > E
+    assert f(P, -1, 8, 2, 0, P, P, None) == SHAPE         # T < 0
+    assert f(None, 4, 8, 2, 0, P, P, None) == NULL
+    assert f(P, 4, 8, 2, 0, None, P, None) == NULL
+    assert f(P + 2, 4, 8, 2, 0, P, P, None) == ALIGN
+    assert f(None, 0, 8, 2, 0, None, None, None) == OK    # T = 0: nothing to do
+
+
+def test_align_validation_and_capacity():
+    cap = lib.moe_align_capacity
+    assert cap(16, 8, 64, 64) == 128 + 64 * 63           # S + min(E,S)(M-1), a multiple of M
+    assert cap(4, 2, 8, 16) == 128
+    assert cap(0, 2, 8, 16) == 0
+    assert cap(3, 2, 8, 1) == 6
+    assert cap(16, 8, 64, 3) == 0                          # block_m not a power of two
+    assert cap(16, 8, 64, 512) == 0                        # block_m > 256
+    f = lib.moe_align_block
+    assert f(P, 4, 2, 8, 3, P, P, P, None) == SHAPE
+    assert f(P, 4, 2, 8, 16, P, P, None, None) == NULL
+    assert f(None, 4, 2, 8, 16, P, P, P, None) == NULL
+    assert f(P, 4, 2, 8, 16, None, P, P, None) == NULL
+    assert f(P, 4, 2, 8, 16, P, P, P + 1, None) == ALIGN
+    assert f(P, 1 << 22, 8, 64, 16, P, P, P, None) == SHAPE   # T*k >= 2^24
+
+
+def _ffn_args(**kw):
+    a = dict(x=P, w1=P, w2=P, ids=P, wts=P, sid=P, be=P, npad=P, T=4, E=8, H=256, I=512, k=2,
+             M=16, flags=0, ws=P, wsb=1 << 30, out=P)
+    a.update(kw)
+    return a
+
+
+def call_bf16(**kw):
+    a = _ffn_args(**kw)
+    return lib.moe_ffn_bf16(a["x"], a["w1"], a["w2"], a["ids"], a["wts"], a["sid"], a["be"],
+                            a["npad"], a["T"], a["E"], a["H"], a["I"], a["k"], a["M"], a["flags"],
+                            a["ws"], a["wsb"], a["out"], None)
+
+
+def call_fp8(s1=P, s2=P, **kw):
+    a = _ffn_args(**kw)
+    return lib.moe_ffn_fp8(a["x"], a["w1"], s1, a["w2"], s2, a["ids"], a["wts"], a["sid"],
+                           a["be"], a["npad"], a["T"], a["E"], a["H"], a["I"], a["k"], a["M"],
+                           a["flags"], a["ws"], a["wsb"], a["out"], None)
+
+
+def call_f32(**kw):
+    a = _ffn_args(**kw)
+    return lib.moe_ffn_f32(a["x"], a["w1"], a["w2"], a["ids"], a["wts"], a["sid"], a["be"],
+                           a["npad"], a["T"], a["E"], a["H"], a["I"], a["k"], a["M"], a["flags"],
+                           a["ws"], a["wsb"], a["out"], None)
+
+
+@pytest.mark.parametrize("call", [call_bf16, call_fp8, call_f32])
+def test_ffn_validation(call):
+    assert call(H=200) == SHAPE if call is not call_f32 else call(H=202) == SHAPE
+    assert call(I=0) == SHAPE
+    assert call(k=9) == SHAPE
+    assert call(E=2000) == SHAPE
+    assert call(M=12) == SHAPE
+    assert call(x=None) == NULL
+    assert call(npad=None) == NULL
+    assert call(ws=None) == NULL
+    assert call(out=P + 8) == ALIGN
+    assert call(ws=P + 128) == ALIGN
+    assert call(wsb=16) == WORKSPACE
+    assert call(flags=1 << 20) == UNSUP
+    assert call(T=0, x=None, out=None, ws=None) == OK       # empty batch: nothing launched
+
+
+def test_fp8_scale_pointers_validated():
+    assert call_fp8(s1=None) == NULL
+    assert call_fp8(s2=P + 4) == ALIGN
+
+
+def test_workspace_bytes():
+    ws = lib.moe_ffn_workspace_bytes
+    S, H, I = 16 * 8, 4096, 1536
+    bf = ws(16, 64, H, I, 8, 64, 1)
+    assert bf >= S * I * 2 + S * H * 4 and bf % 256 == 0
+    f8 = ws(16, 64, H, I, 8, 64, 2)
+    assert f8 >= S * I * 4 + S * I + S * 4 + 16 * H + 16 * 4 + S * H * 4
+    assert ws(16, 64, H, I, 8, 64, 7) == 0
+    assert ws(0, 64, H, I, 8, 64, 1) == 0

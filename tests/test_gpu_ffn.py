@@ -1,0 +1,138 @@
+"""GPU parity of the whole path (route -> align -> FFN) against the CPU oracle
+on the five workloads and on small ragged shapes; plus determinism, stage
+splitting, the XCD-remap switch, guard bytes and token permutation."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import make_inputs
+from tests.gpu_util import (BENCH_BLOCK_M, TOL, cfg_inputs, check_align, check_routing, gpu_forward,
+                            moe, oracle_forward, out_f64, say)
+
+pytestmark = pytest.mark.gpu
+
+# tokens the oracle evaluates one by one at the two largest workloads
+SAMPLE = {4: [0, 1, 17, 31, 42, 63], 5: [0, 1, 2, 511, 1000, 2047, 3000, 4095]}
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_config_parity(n):
+    inp = cfg_inputs(n)
+    say(f"ffn config {n} ({inp.dtype}) T={inp.T} E={inp.E} H={inp.H} I={inp.I} k={inp.k} "
+        f"block_m={BENCH_BLOCK_M}")
+    ids, w, al, out = gpu_forward(inp, BENCH_BLOCK_M)
+    tokens = SAMPLE.get(n)
+    ids_o, w_o, ref = oracle_forward(inp, tokens)
+    check_routing(ids, w, ids_o, w_o)
+    check_align(al, ids_o, inp.E, BENCH_BLOCK_M, inp.S)
+    got = out_f64(out)
+    if tokens is not None:
+        got = got[tokens]
+    err = oracle.normwise_rel_err(got, ref)
+    say(f"  normwise rel err {err:.3e} (tol {TOL[inp.dtype]})")
+    assert err <= TOL[inp.dtype]
+    assert np.all(np.isfinite(got))
+
+
+CASES = [  # T, E, H, I, k, routing
+    (37, 16, 256, 384, 3, "normal"),
+    (5, 4, 128, 128, 4, "normal"),
+    (200, 8, 512, 256, 2, "zipf"),
+    (1, 1, 256, 128, 1, "normal"),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "f32"])
+@pytest.mark.parametrize("block_m", [1, 16, 64, 128])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "T{}_E{}_H{}_I{}_k{}_{}".format(*c))
+def test_small_ragged_parity(case, block_m, dtype):
+    T, E, H, I, k, routing = case
+    say(f"ffn small {dtype} T={T} E={E} H={H} I={I} k={k} {routing} block_m={block_m}")
+    inp = make_inputs(T, E, H, I, k, dtype=dtype, routing=routing, seed=T + E + block_m,
+                      device="cuda")
+    ids, w, al, out = gpu_forward(inp, block_m)
+    ids_o, w_o, ref = oracle_forward(inp)
+    check_routing(ids, w, ids_o, w_o)
+    check_align(al, ids_o, E, block_m, inp.S)
+    err = oracle.normwise_rel_err(out_f64(out), ref)
+    say(f"  normwise rel err {err:.3e}")
+    assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_renormalized_weights(dtype):
+    inp = make_inputs(24, 16, 256, 256, 4, dtype=dtype, routing="normal", seed=3, device="cuda")
+    say(f"ffn renormalize {dtype}")
+    ids, w, al, out = gpu_forward(inp, 16, renormalize=True)
+    ids_o, w_o, ref = oracle_forward(inp, renormalize=True)
+    check_routing(ids, w, ids_o, w_o)
+    assert oracle.normwise_rel_err(out_f64(out), ref) <= TOL[dtype]
+
+
+def test_all_tokens_to_one_expert_many_groups():
+    # one expert holds every token: blocks of 256 slots, four 64-token groups each
+    T, E, H, I, k = 300, 4, 256, 256, 1
+    L = np.full((T, E), -1.0, np.float32)
+    L[:, 2] = 1.0
+    inp = make_inputs(T, E, H, I, k, dtype="bf16", seed=9, device="cuda", logits=L)
+    say("ffn one hot expert, block_m=256")
+    ids, w, al, out = gpu_forward(inp, 256)
+    _, _, ref = oracle_forward(inp)
+    assert oracle.normwise_rel_err(out_f64(out), ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_determinism_stages_remap_and_guards(dtype):
+    m = moe()
+    inp = make_inputs(40, 16, 512, 256, 4, dtype=dtype, routing="zipf", seed=4, device="cuda")
+    say(f"ffn determinism/stages/remap/guards {dtype}")
+    M = 16
+    ids, w = m.route_topk(inp.logits, inp.k)
+    sid, be, npad = m.align_block(ids, inp.E, M)
+    call = (lambda **kw: m.ffn_fp8(inp.x, inp.w1, inp.w1_scale, inp.w2, inp.w2_scale, ids, w,
+                                   sid, be, npad, M, **kw)) if dtype == "fp8" else \
+        (lambda **kw: m.ffn_bf16(inp.x, inp.w1, inp.w2, ids, w, sid, be, npad, M, **kw))
+    a = call()
+    b = call()
+    c = call(flags=m.NO_XCD_REMAP)
+    ws = m.alloc_workspace(inp.T, inp.E, inp.H, inp.I, inp.k, M,
+                           m.MOE_DTYPE_FP8 if dtype == "fp8" else m.MOE_DTYPE_BF16, "cuda")
+    guard = torch.full((inp.T * inp.H + 2 * 64,), 0x7F7F, dtype=torch.int16, device="cuda")
+    d = guard[64:64 + inp.T * inp.H].view(torch.bfloat16).view(inp.T, inp.H)
+    call(flags=m.STAGE_FC1, workspace=ws, out=d)
+    call(flags=m.STAGE_FC2, workspace=ws, out=d)
+    call(flags=m.STAGE_COMBINE, workspace=ws, out=d)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), d.view(torch.int16))
+    g = guard.cpu().numpy()
+    assert np.all(g[:64] == 0x7F7F) and np.all(g[64 + inp.T * inp.H:] == 0x7F7F)
+
+
+def test_token_permutation():
+    inp = make_inputs(48, 16, 256, 256, 4, dtype="bf16", routing="normal", seed=8, device="cuda")
+    say("ffn token permutation")
+    _, _, _, out = gpu_forward(inp, 16)
+    perm = torch.from_numpy(np.random.default_rng(1).permutation(inp.T)).cuda()
+    inp_p = make_inputs(48, 16, 256, 256, 4, dtype="bf16", seed=8, device="cuda",
+                        logits=inp.host_logits()[perm.cpu().numpy()])
+    inp_p.x = inp.x[perm].contiguous()
+    inp_p.w1, inp_p.w2 = inp.w1, inp.w2
+    _, _, _, out_p = gpu_forward(inp_p, 16)
+    err = oracle.normwise_rel_err(out_f64(out_p), out_f64(out)[perm.cpu().numpy()])
+    assert err <= 1e-6
+
+
+def test_empty_batch():
+    m = moe()
+    say("ffn T=0")
+    inp = make_inputs(1, 4, 128, 128, 2, dtype="bf16", seed=0, device="cuda")
+    x = inp.x[:0]
+    ids = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    w = torch.empty((0, 2), dtype=torch.float32, device="cuda")
+    sid, be, npad = m.align_block(ids, 4, 16)
+    out = m.ffn_bf16(x, inp.w1, inp.w2, ids, w, sid, be, npad, 16)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 128)
