@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed region, copy a buffer of this many MiB 3 times "
+                         "(a plain copy kernel of known size, to calibrate HBM counters)")
     return ap.parse_args()
 
 
@@ -185,6 +188,14 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     fc1_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]))
+
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # algorithmic work (active experts from this run's routing)
     ids_h = ids.cpu().numpy()
