@@ -9,18 +9,24 @@
 // experts and FP8 scales are applied around the fp32 accumulator (section 3.1).
 // V100 fork article, "wall 2": silu_and_mul sits between FC1 and FC2.
 //
-// Design (MI355X): FC1 and FC2 are weight streams. The work of a projection
-// is a list of units (aligned block b, 16-row weight tile r); the list length
-// comes from num_padded on the device, so the host never synchronises. A
-// persistent grid sized to the resident capacity gives every wave one
-// contiguous, equal share of the list; with the XCD remap on, the waves of one
-// XCD (workgroup id mod 8) own one contiguous share, so each XCD's L2 serves a
-// contiguous slice of (expert, rows). Per unit a wave streams its 16 weight
-// rows straight from HBM into MFMA A-fragments (64 contiguous bytes per row per
-// load instruction), gathers the block's token rows into B-fragments (L2
-// resident) and accumulates 16x16 tiles with v_mfma; no LDS, no barriers.
-// FC1 interleaves 8 gate rows and the matching 8 up rows in one tile, so
-// SiLU(gate)*up is formed in registers after one lane swap.
+// Design (MI355X). FC1 and FC2 are weight streams; one persistent launch per
+// projection. The work list is made of quads: 4 consecutive 16-row weight
+// tiles of one aligned block (one tile per wave of a 256-thread workgroup).
+// Its length comes from num_padded on the device, so the host never waits.
+// Workgroups own contiguous equal shares of the list; with the XCD remap the
+// workgroups of one XCD (id mod 8) own one contiguous eighth, so each XCD's L2
+// serves a contiguous slice of (expert, rows). A quad never straddles blocks,
+// so its mode is uniform across the workgroup:
+//  * cold (block holds <= 8 tokens): each wave streams its 16 rows on its own
+//    as two "half-split" 8-row MFMA tiles that read whole 128-byte lines with
+//    non-temporal loads, and gathers the few token rows straight from L2;
+//  * hot (> 8 tokens): the workgroup stages the block's token rows in LDS,
+//    256 bytes of K at a time, double buffered; each wave streams its 16 rows
+//    in the plain 16x16 MFMA layout, reading next chunk's weights while it
+//    multiplies the current one, and takes B fragments from LDS, so the
+//    activations cross L2 once per quad instead of once per wave.
+// FC1 pairs gate rows with the matching up rows inside each tile so that
+// SiLU(gate) * up is formed in registers.
 #include "moe_common.h"
 #include "moe_launch.h"
 
@@ -30,19 +36,22 @@
 
 namespace moe {
 
+constexpr int kColdMax = 8;     // a block with at most this many tokens is cold
+constexpr int kHotTok = 64;     // tokens per pass of a hot quad (4 MFMA column tiles)
+constexpr int kHotChunk = 256;  // bytes of K per staged chunk (both dtypes)
+constexpr int kLdsRow = kHotChunk + 16;  // padded LDS row: conflict-free B reads
+
 // ------------------------------------------------- work partitioning ---
 
-struct WaveRange {
-  long u0, u1;
+struct Share {
+  long q0, q1;
 };
 
-__device__ __forceinline__ WaveRange wave_range(long total, int remap) {
+__device__ __forceinline__ Share wg_share(long total, int remap) {
   int wg = blockIdx.x;
   const int G = gridDim.x;
   if (remap && (G & 7) == 0) wg = (wg & 7) * (G >> 3) + (wg >> 3);
-  const long wave = (long)wg * 4 + (threadIdx.x >> 6);
-  const long W = (long)G * 4;
-  return {total * wave / W, total * (wave + 1) / W};
+  return {total * wg / G, total * (wg + 1) / G};
 }
 
 // Number of real (non-sentinel) entries of block b; they form a prefix.
@@ -58,101 +67,263 @@ __device__ __forceinline__ int block_valid(const int32_t* __restrict__ sorted_id
   return m;
 }
 
-// Slot of column (lane & 15) of token tile t of the group starting at t0.
-__device__ __forceinline__ void group_slots(const int32_t* __restrict__ sorted_ids, int b, int M,
-                                            int S, int m_valid, int t0, int (&slot)[4]) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int i = t0 + t * 16 + (lane & 15);
-    slot[t] = i < m_valid ? sorted_ids[(size_t)b * M + i] : S;
-  }
-}
-
-// ------------------------------------------------------- bf16 K loop ---
-// acc[t] += A(16 rows, this lane: a_ptr) . B_t(16 tokens, this lane: b_ptr[t])
-// over K elements; one k-step is 32 elements (64 bytes per row).
-template <int MT, int U>
-__device__ __forceinline__ void kloop_bf16(const uint16_t* __restrict__ a_ptr,
-                                           const uint16_t* const (&b_ptr)[4], const bool (&ok)[4],
-                                           int K, f32x4 (&acc)[4]) {
-  const int nks = K >> 5;
-  int ks = 0;
-  for (; ks + U <= nks; ks += U) {
-    bf16x8 a[U], b[MT][U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) a[u] = *(const bf16x8*)(a_ptr + (size_t)(ks + u) * 32);
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        b[t][u] = bf16x8{};
-        if (ok[t]) b[t][u] = *(const bf16x8*)(b_ptr[t] + (size_t)(ks + u) * 32);
-      }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int t = 0; t < MT; ++t) acc[t] = mfma_bf16(a[u], b[t][u], acc[t]);
-  }
-  for (; ks < nks; ++ks) {
-    const bf16x8 a = *(const bf16x8*)(a_ptr + (size_t)ks * 32);
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      bf16x8 b{};
-      if (ok[t]) b = *(const bf16x8*)(b_ptr[t] + (size_t)ks * 32);
-      acc[t] = mfma_bf16(a, b, acc[t]);
-    }
-  }
-}
-
-// -------------------------------------------------------- fp8 K loop ---
-// One k-step is 128 e4m3 bytes per row. A lane's 32 operand bytes are the
-// 16 bytes at 16*g and the 16 bytes at 64 + 16*g of the step (g = lane >> 4),
-// so each load instruction reads 64 contiguous bytes per row; B uses the same
-// placement, which keeps every product paired with its own k.
-__device__ __forceinline__ i32x8 load_fp8_frag(const uint8_t* __restrict__ p) {
-  const u32x4 lo = *(const u32x4*)p;
-  const u32x4 hi = *(const u32x4*)(p + 64);
-  return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-               (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-}
-
-template <int MT, int U>
-__device__ __forceinline__ void kloop_fp8(const uint8_t* __restrict__ a_ptr,
-                                          const uint8_t* const (&b_ptr)[4], const bool (&ok)[4],
-                                          int K, f32x4 (&acc)[4]) {
-  const int nks = K >> 7;
-  int ks = 0;
-  for (; ks + U <= nks; ks += U) {
-    i32x8 a[U], b[MT][U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) a[u] = load_fp8_frag(a_ptr + (size_t)(ks + u) * 128);
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        b[t][u] = i32x8{};
-        if (ok[t]) b[t][u] = load_fp8_frag(b_ptr[t] + (size_t)(ks + u) * 128);
-      }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int t = 0; t < MT; ++t) acc[t] = mfma_fp8(a[u], b[t][u], acc[t]);
-  }
-  for (; ks < nks; ++ks) {
-    const i32x8 a = load_fp8_frag(a_ptr + (size_t)ks * 128);
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      i32x8 b{};
-      if (ok[t]) b = load_fp8_frag(b_ptr[t] + (size_t)ks * 128);
-      acc[t] = mfma_fp8(a, b, acc[t]);
-    }
-  }
-}
-
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
-// ---------------------------------------------------------- FC1 bf16 ---
+// -------------------------------------------------- operand fragments ---
+// bf16: one 16-byte load feeds v_mfma_f32_16x16x32_bf16 (8 elements/lane).
+// fp8 : 32 bytes per lane feed v_mfma_scale_f32_16x16x128_f8f6f4; the two
+//       16-byte halves sit `step` bytes apart (the same placement in A and B,
+//       so every product pairs equal k).
+
+template <bool FP8>
+struct Frag;
+template <>
+struct Frag<false> {
+  bf16x8 v;
+  __device__ __forceinline__ void load_nt(const uint8_t* p, int) {
+    v = __builtin_nontemporal_load((const bf16x8*)p);
+  }
+  __device__ __forceinline__ void load(const uint8_t* p, int) { v = *(const bf16x8*)p; }
+  __device__ __forceinline__ void load_lo(const uint8_t* p) { v = *(const bf16x8*)p; }
+  __device__ __forceinline__ void lds(const uint8_t* p, int) { v = *(const bf16x8*)p; }
+  __device__ __forceinline__ void zero() { v = bf16x8{}; }
+};
+template <>
+struct Frag<true> {
+  i32x8 v;
+  __device__ __forceinline__ void set(const u32x4& lo, const u32x4& hi) {
+    v = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+  __device__ __forceinline__ void load_nt(const uint8_t* p, int step) {
+    set(__builtin_nontemporal_load((const u32x4*)p), __builtin_nontemporal_load((const u32x4*)(p + step)));
+  }
+  __device__ __forceinline__ void load(const uint8_t* p, int step) {
+    set(*(const u32x4*)p, *(const u32x4*)(p + step));
+  }
+  // the first half only; the second is absent (a trailing half chunk)
+  __device__ __forceinline__ void load_lo(const uint8_t* p) { set(*(const u32x4*)p, u32x4{0, 0, 0, 0}); }
+  __device__ __forceinline__ void lds(const uint8_t* p, int step) {
+    set(*(const u32x4*)p, *(const u32x4*)(p + step));
+  }
+  __device__ __forceinline__ void zero() { v = i32x8{}; }
+};
+
+__device__ __forceinline__ f32x4 mfma(const Frag<false>& a, const Frag<false>& b, const f32x4& c) {
+  return mfma_bf16(a.v, b.v, c);
+}
+__device__ __forceinline__ f32x4 mfma(const Frag<true>& a, const Frag<true>& b, const f32x4& c) {
+  return mfma_fp8(a.v, b.v, c);
+}
+
+// ------------------------------------------------ cold: half-split tiles ---
+// A tile of 8 weight rows in which MFMA A-rows i and i+8 hold the SAME weight
+// row (i & 7): A-row i < 8 carries the first 64 bytes of each 128-byte line of
+// that row, A-row i >= 8 the second 64 bytes; B-columns j < 8 / j >= 8 carry
+// the first / second halves of token (j & 7). The diagonal 8x8 blocks of D
+// are the two half-sums and D[i][j] + D[i+8][j+8] the full dot product, while
+// every load instruction reads 8 rows x one whole 128-byte line (lane l: row
+// l & 7, half (l & 15) >> 3, 16 bytes at k-group l >> 4), so the weights can
+// be loaded non-temporally without fetching any line twice. A k-chunk is one
+// line (bf16) or two lines (fp8, `step` = 128) of each row. After the sum lane
+// l in 0..7 holds tile rows 0..3 and lane l in 16..23 tile rows 4..7 (D row
+// 4*(l >> 4) + r), both for token (l & 7).
+
+template <bool FP8>
+struct Cold {
+  static constexpr int kChunk = FP8 ? 256 : 128;
+  static constexpr int kStep = 128;
+  static constexpr int U = FP8 ? 1 : 2;  // k-chunks per pipeline group
+};
+
+__device__ __forceinline__ int half_split_off() {
+  const int lane = threadIdx.x & 63;
+  return ((lane & 15) >> 3) * 64 + (lane >> 4) * 16;
+}
+
+template <bool FP8>
+struct ColdGroup {
+  static constexpr int U = Cold<FP8>::U;
+  Frag<FP8> p[U], q[U], b[U];
+  __device__ __forceinline__ void issue(const uint8_t* __restrict__ ap,
+                                        const uint8_t* __restrict__ aq,
+                                        const uint8_t* __restrict__ bp, bool ok, int c) {
+    constexpr int CH = Cold<FP8>::kChunk, ST = Cold<FP8>::kStep;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      p[u].load_nt(ap + (size_t)(c + u) * CH, ST);
+      q[u].load_nt(aq + (size_t)(c + u) * CH, ST);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      b[u].zero();
+      if (ok) b[u].load(bp + (size_t)(c + u) * CH, ST);
+    }
+  }
+  __device__ __forceinline__ void compute(f32x4& accp, f32x4& accq) const {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      accp = mfma(p[u], b[u], accp);
+      accq = mfma(q[u], b[u], accq);
+    }
+  }
+};
+
+// accp/accq += tiles P/Q (this lane: ap, aq) . the token tile (this lane: bp,
+// loaded only if ok) over kbytes bytes of every row. Two register groups
+// alternate: the next group's loads are issued before the current group's
+// MFMAs, so with in-order load counters they stay in flight meanwhile.
+template <bool FP8>
+__device__ __forceinline__ void cold_kloop(const uint8_t* __restrict__ ap,
+                                           const uint8_t* __restrict__ aq,
+                                           const uint8_t* __restrict__ bp, bool ok, int kbytes,
+                                           f32x4& accp, f32x4& accq) {
+  constexpr int CH = Cold<FP8>::kChunk, ST = Cold<FP8>::kStep, U = Cold<FP8>::U;
+  const int nch = kbytes / CH;
+  const int ngrp = nch / U;
+  ColdGroup<FP8> g0, g1;
+  if (ngrp > 0) g0.issue(ap, aq, bp, ok, 0);
+  int g = 0;
+  for (; g + 1 < ngrp; g += 2) {
+    g1.issue(ap, aq, bp, ok, (g + 1) * U);
+    g0.compute(accp, accq);
+    if (g + 2 < ngrp) g0.issue(ap, aq, bp, ok, (g + 2) * U);
+    g1.compute(accp, accq);
+  }
+  if (g < ngrp) g0.compute(accp, accq);
+  for (int c = ngrp * U; c < nch; ++c) {
+    Frag<FP8> fp, fq, fb;
+    fp.load_nt(ap + (size_t)c * CH, ST);
+    fq.load_nt(aq + (size_t)c * CH, ST);
+    fb.zero();
+    if (ok) fb.load(bp + (size_t)c * CH, ST);
+    accp = mfma(fp, fb, accp);
+    accq = mfma(fq, fb, accq);
+  }
+  if (FP8 && (kbytes % CH) != 0) {  // trailing 128 bytes: one line per row
+    Frag<FP8> fp, fq, fb;
+    fp.load_lo(ap + (size_t)nch * CH);
+    fq.load_lo(aq + (size_t)nch * CH);
+    fb.zero();
+    if (ok) fb.load_lo(bp + (size_t)nch * CH);
+    accp = mfma(fp, fb, accp);
+    accq = mfma(fq, fb, accq);
+  }
+}
+
+// Full dot products of a half-split tile: lanes 0..7 and 16..23 hold them.
+__device__ __forceinline__ f32x4 diag_sum(const f32x4& a) {
+  const int src = ((threadIdx.x & 63) + 40) & 63;
+  f32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = a[i] + __shfl(a[i], src);
+  return r;
+}
+
+// ------------------------------------------- hot: LDS-staged activations ---
+// Plain 16x16 layout: lane l holds A row (l & 15) and B column (l & 15), k-group
+// l >> 4; D rows 4*(l >> 4) + i, column l & 15. A chunk of 256 bytes of K is
+// 4 (bf16) or 2 (fp8) MFMA k-steps; within a k-step of `kstep` bytes a lane
+// takes 16 bytes at 16*g (bf16: kstep = 64) or 16 bytes at 16*g and at
+// 64 + 16*g (fp8: kstep = 128), in A, in B and in LDS alike.
+
+template <bool FP8>
+struct Hot {
+  static constexpr int kKstep = FP8 ? 128 : 64;
+  static constexpr int kSteps = kHotChunk / kKstep;  // MFMA k-steps per chunk
+};
+
+template <bool FP8>
+struct HotA {
+  Frag<FP8> f[Hot<FP8>::kSteps];
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ a, int chunk) {
+#pragma unroll
+    for (int s = 0; s < Hot<FP8>::kSteps; ++s)
+      f[s].load(a + (size_t)chunk * kHotChunk + s * Hot<FP8>::kKstep, 64);
+  }
+  // trailing half chunk (fp8 only: 128 bytes = one k-step)
+  __device__ __forceinline__ void load_tail(const uint8_t* __restrict__ a, int chunk) {
+    f[0].load(a + (size_t)chunk * kHotChunk, 64);
+#pragma unroll
+    for (int s = 1; s < Hot<FP8>::kSteps; ++s) f[s].zero();
+  }
+};
+
+// One chunk of MFMAs: A from registers, B fragments from the LDS buffer.
+template <bool FP8, int MT>
+__device__ __forceinline__ void hot_compute(const HotA<FP8>& a, const uint8_t* __restrict__ buf,
+                                            f32x4 (&acc)[4]) {
+  const int lane = threadIdx.x & 63;
+  const uint8_t* base = buf + (lane & 15) * kLdsRow + (lane >> 4) * 16;
+#pragma unroll
+  for (int s = 0; s < Hot<FP8>::kSteps; ++s)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      Frag<FP8> b;
+      b.lds(base + t * 16 * kLdsRow + s * Hot<FP8>::kKstep, 64);
+      acc[t] = mfma(a.f[s], b, acc[t]);
+    }
+}
+
+// Staging: 256 threads move 64 token rows x 256 bytes (4 x 16 bytes each).
+struct Stage {
+  u32x4 v[4];
+  const uint8_t* src[4];  // this thread's 4 source rows (+ its byte offset), or null
+  __device__ __forceinline__ void load(int chunk, int kbytes) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = u32x4{0, 0, 0, 0};
+      const int off = chunk * kHotChunk + (threadIdx.x & 15) * 16;
+      if (src[i] && off < kbytes) v[i] = *(const u32x4*)(src[i] + off);
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* __restrict__ buf) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *(u32x4*)(buf + ((threadIdx.x >> 4) + 16 * i) * kLdsRow + (threadIdx.x & 15) * 16) = v[i];
+  }
+};
+
+// acc[t] += A (16 rows: this lane's a) . B (token tile t from the staged
+// rows) over kbytes of K. `stage` holds this thread's source rows. All 256
+// threads of the workgroup call this together.
+template <bool FP8, int MT>
+__device__ __forceinline__ void hot_kloop(const uint8_t* __restrict__ a, Stage& stage, int kbytes,
+                                          uint8_t* __restrict__ lds, f32x4 (&acc)[4]) {
+  uint8_t* buf0 = lds;
+  uint8_t* buf1 = lds + kHotTok * kLdsRow;
+  const int nch = (kbytes + kHotChunk - 1) / kHotChunk;
+  const bool tail = (kbytes % kHotChunk) != 0;  // fp8 only: last chunk is 128 bytes
+  HotA<FP8> a0, a1;
+  stage.load(0, kbytes);
+  if (tail && nch == 1) a0.load_tail(a, 0);
+  else a0.load(a, 0);
+  stage.store(buf0);
+  __syncthreads();
+  int c = 0;
+  for (; c + 1 < nch; c += 2) {
+    // chunk c from buf0 / a0 while chunk c+1 loads into buf1 / a1
+    stage.load(c + 1, kbytes);
+    if (tail && c + 2 == nch) a1.load_tail(a, c + 1);
+    else a1.load(a, c + 1);
+    hot_compute<FP8, MT>(a0, buf0, acc);
+    stage.store(buf1);
+    __syncthreads();
+    if (c + 2 < nch) {
+      stage.load(c + 2, kbytes);
+      if (tail && c + 3 == nch) a0.load_tail(a, c + 2);
+      else a0.load(a, c + 2);
+    }
+    hot_compute<FP8, MT>(a1, buf1, acc);
+    if (c + 2 < nch) stage.store(buf0);
+    __syncthreads();
+  }
+  if (c < nch) {
+    hot_compute<FP8, MT>(a0, buf0, acc);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- FC1 ---
 
 struct Fc1Args {
   const void* x;       // bf16 [T,H] (bf16 path) or e4m3 codes [T,H] (fp8 path)
@@ -166,100 +337,98 @@ struct Fc1Args {
   void* h;             // bf16 [S, I] (bf16 path) or f32 [S, I] (fp8 path)
 };
 
-template <int MT>
-__device__ __forceinline__ void fc1_bf16_group(const Fc1Args& p, int e, int r, const int (&slot)[4]) {
-  const int lane = threadIdx.x & 63, g = lane >> 4, rho = lane & 15;
-  const int row = rho < 8 ? (r * 8 + rho) : (p.I + r * 8 + rho - 8);
-  const uint16_t* a_ptr =
-      (const uint16_t*)p.w1 + ((size_t)e * 2 * p.I + row) * p.H + 8 * g;
-  const uint16_t* b_ptr[4];
-  bool ok[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    ok[t] = t < MT && slot[t] < p.S;
-    b_ptr[t] = (const uint16_t*)p.x + (size_t)(ok[t] ? slot[t] / p.k : 0) * p.H + 8 * g;
-  }
-  f32x4 acc[4] = {};
-  kloop_bf16<MT, 8 / MT>(a_ptr, b_ptr, ok, p.H, acc);
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    f32x4 o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = __shfl_xor(acc[t][i], 32);
-    if (lane < 32 && ok[t]) {
-      uint32_t hb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16_rne(silu_mul(acc[t][i], o[i]));
-      *(u32x2*)((uint16_t*)p.h + (size_t)slot[t] * p.I + r * 8 + 4 * g) =
-          u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
-    }
-  }
-}
-
-template <int MT>
-__device__ __forceinline__ void fc1_fp8_group(const Fc1Args& p, int e, int r, const int (&slot)[4]) {
-  const int lane = threadIdx.x & 63, g = lane >> 4, rho = lane & 15;
-  const int row = rho < 8 ? (r * 8 + rho) : (p.I + r * 8 + rho - 8);
-  const uint8_t* a_ptr = (const uint8_t*)p.w1 + ((size_t)e * 2 * p.I + row) * p.H + 16 * g;
-  const uint8_t* b_ptr[4];
-  bool ok[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    ok[t] = t < MT && slot[t] < p.S;
-    b_ptr[t] = (const uint8_t*)p.x + (size_t)(ok[t] ? slot[t] / p.k : 0) * p.H + 16 * g;
-  }
-  f32x4 acc[4] = {};
-  kloop_fp8<MT, (MT == 1 ? 4 : (MT == 2 ? 2 : 1))>(a_ptr, b_ptr, ok, p.H, acc);
-  // this lane's D rows: 4*g + i; gate rows for g < 2, up rows for g >= 2
-  const int nrow0 = (g < 2) ? (r * 8 + 4 * g) : (p.I + r * 8 + 4 * (g - 2));
-  const f32x4 ws = *(const f32x4*)(p.w1s + (size_t)e * 2 * p.I + nrow0);
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const float xs = ok[t] ? p.xs[slot[t] / p.k] : 0.f;
-    f32x4 v, o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = acc[t][i] * ws[i] * xs;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = __shfl_xor(v[i], 32);
-    if (lane < 32 && ok[t]) {
-      f32x4 hv;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hv[i] = silu_mul(v[i], o[i]);
-      *(f32x4*)((float*)p.h + (size_t)slot[t] * p.I + r * 8 + 4 * g) = hv;
-    }
-  }
-}
-
+// Store SiLU(g)*u for 4 consecutive h columns of one slot.
 template <bool FP8>
-__global__ __launch_bounds__(256) void fc1_kernel(Fc1Args p) {
-  const int M = 1 << p.log2m;
-  const int nb = p.num_padded[0] >> p.log2m;
-  const int n_rt = p.I >> 3;
-  const WaveRange wr = wave_range((long)nb * n_rt, p.remap);
-  int cur_b = -1, e = 0, m_valid = 0;
-  for (long u = wr.u0; u < wr.u1; ++u) {
-    const int b = (int)(u / n_rt), r = (int)(u % n_rt);
-    if (b != cur_b) {
-      cur_b = b;
-      e = p.block_expert[b];
-      m_valid = block_valid(p.sorted_ids, b, M, p.S);
-    }
-    for (int t0 = 0; t0 < m_valid; t0 += 64) {
-      int slot[4];
-      group_slots(p.sorted_ids, b, M, p.S, m_valid, t0, slot);
-      const int mt = min(4, (m_valid - t0 + 15) >> 4);
-      if (FP8) {
-        if (mt == 1) fc1_fp8_group<1>(p, e, r, slot);
-        else if (mt == 2) fc1_fp8_group<2>(p, e, r, slot);
-        else if (mt == 3) fc1_fp8_group<3>(p, e, r, slot);
-        else fc1_fp8_group<4>(p, e, r, slot);
-      } else {
-        if (mt == 1) fc1_bf16_group<1>(p, e, r, slot);
-        else if (mt == 2) fc1_bf16_group<2>(p, e, r, slot);
-        else if (mt == 3) fc1_bf16_group<3>(p, e, r, slot);
-        else fc1_bf16_group<4>(p, e, r, slot);
+__device__ __forceinline__ void store_h(const Fc1Args& p, int slot, int col, const f32x4& g,
+                                        const f32x4& u) {
+  if (FP8) {
+    f32x4 hv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hv[i] = silu_mul(g[i], u[i]);
+    *(f32x4*)((float*)p.h + (size_t)slot * p.I + col) = hv;
+  } else {
+    uint32_t hb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16_rne(silu_mul(g[i], u[i]));
+    *(u32x2*)((uint16_t*)p.h + (size_t)slot * p.I + col) =
+        u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+  }
+}
+
+// Cold FC1 tile r (h columns [8r, 8r+8)): P = gate rows [8r, 8r+8), Q = the
+// matching up rows [I+8r, I+8r+8). After the diagonal sums a lane holds g and
+// u of the same (column, token).
+template <bool FP8>
+__device__ __forceinline__ void fc1_cold(const Fc1Args& p, int e, int r, int b, int M, int m) {
+  const int lane = threadIdx.x & 63;
+  const size_t rowb = (size_t)p.H * (FP8 ? 1 : 2);
+  const int off = half_split_off();
+  const uint8_t* w = (const uint8_t*)p.w1 + (size_t)e * 2 * p.I * rowb;
+  const uint8_t* ap = w + (size_t)(r * 8 + (lane & 7)) * rowb + off;
+  const uint8_t* aq = w + (size_t)(p.I + r * 8 + (lane & 7)) * rowb + off;
+  const int ti = lane & 7;
+  const int slot = ti < m ? p.sorted_ids[(size_t)b * M + ti] : p.S;
+  const bool ok = slot < p.S;
+  const uint8_t* bp = (const uint8_t*)p.x + (size_t)(ok ? slot / p.k : 0) * rowb + off;
+  f32x4 accp = {}, accq = {};
+  cold_kloop<FP8>(ap, aq, bp, ok, (int)rowb, accp, accq);
+  f32x4 g = diag_sum(accp), u = diag_sum(accq);
+  const bool holder = (lane & 8) == 0 && lane < 32;  // lanes 0..7, 16..23
+  const int col = r * 8 + 4 * (lane >> 4);
+  if (holder && ok) {
+    if (FP8) {
+      const float xs = p.xs[slot / p.k];
+      const f32x4 sg = *(const f32x4*)(p.w1s + (size_t)e * 2 * p.I + col);
+      const f32x4 su = *(const f32x4*)(p.w1s + (size_t)e * 2 * p.I + p.I + col);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        g[i] *= sg[i] * xs;
+        u[i] *= su[i] * xs;
       }
     }
+    store_h<FP8>(p, slot, col, g, u);
+  }
+}
+
+// Hot FC1 tile r: rows 0..7 of the 16-row tile are gate rows [8r, 8r+8),
+// rows 8..15 the matching up rows; lanes l and l^32 hold g and u of the same
+// (column, token) after the MFMAs.
+template <bool FP8, int MT>
+__device__ __forceinline__ void fc1_hot_pass(const Fc1Args& p, int e, int r, int b, int M, int m,
+                                             int t0, uint8_t* lds) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, rho = lane & 15;
+  const size_t rowb = (size_t)p.H * (FP8 ? 1 : 2);
+  const int wrow = rho < 8 ? (r * 8 + rho) : (p.I + r * 8 + rho - 8);
+  const uint8_t* a = (const uint8_t*)p.w1 + ((size_t)e * 2 * p.I + wrow) * rowb + 16 * g;
+  Stage st;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ti = t0 + (threadIdx.x >> 4) + 16 * i;
+    const int slot = ti < m ? p.sorted_ids[(size_t)b * M + ti] : p.S;
+    st.src[i] = slot < p.S ? (const uint8_t*)p.x + (size_t)(slot / p.k) * rowb : nullptr;
+  }
+  f32x4 acc[4] = {};
+  hot_kloop<FP8, MT>(a, st, (int)rowb, lds, acc);
+  f32x4 sc = {1.f, 1.f, 1.f, 1.f};
+  if (FP8) {
+    const int srow = g < 2 ? (r * 8 + 4 * g) : (p.I + r * 8 + 4 * (g - 2));
+    sc = *(const f32x4*)(p.w1s + (size_t)e * 2 * p.I + srow);
+  }
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int ti = t0 + 16 * t + rho;
+    const int slot = ti < m ? p.sorted_ids[(size_t)b * M + ti] : p.S;
+    const bool ok = slot < p.S;
+    f32x4 v = acc[t];
+    if (FP8) {
+      const float xs = ok ? p.xs[slot / p.k] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] *= sc[i] * xs;
+    }
+    f32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = __shfl_xor(v[i], 32);
+    if (lane < 32 && ok) store_h<FP8>(p, slot, r * 8 + 4 * g, v, o);
   }
 }
 
@@ -277,68 +446,124 @@ struct Fc2Args {
   float* y;            // f32 [S, H]
 };
 
-template <int MT, bool FP8>
-__device__ __forceinline__ void fc2_group(const Fc2Args& p, int e, int r, const int (&slot)[4]) {
-  const int lane = threadIdx.x & 63, g = lane >> 4, rho = lane & 15;
-  const size_t arow = (size_t)e * p.H + r * 16 + rho;
-  bool ok[4];
+// Cold FC2 tile r: P = output rows [16r, 16r+8), Q = [16r+8, 16r+16).
+template <bool FP8>
+__device__ __forceinline__ void fc2_cold(const Fc2Args& p, int e, int r, int b, int M, int m) {
+  const int lane = threadIdx.x & 63;
+  const size_t rowb = (size_t)p.I * (FP8 ? 1 : 2);
+  const int off = half_split_off();
+  const uint8_t* w = (const uint8_t*)p.w2 + (size_t)e * p.H * rowb;
+  const uint8_t* ap = w + (size_t)(r * 16 + (lane & 7)) * rowb + off;
+  const uint8_t* aq = w + (size_t)(r * 16 + 8 + (lane & 7)) * rowb + off;
+  const int ti = lane & 7;
+  const int slot = ti < m ? p.sorted_ids[(size_t)b * M + ti] : p.S;
+  const bool ok = slot < p.S;
+  const uint8_t* bp = (const uint8_t*)p.h + (size_t)(ok ? slot : 0) * rowb + off;
+  f32x4 accp = {}, accq = {};
+  cold_kloop<FP8>(ap, aq, bp, ok, (int)rowb, accp, accq);
+  f32x4 vp = diag_sum(accp), vq = diag_sum(accq);
+  const bool holder = (lane & 8) == 0 && lane < 32;
+  const int row = r * 16 + 4 * (lane >> 4);
+  if (holder && ok) {
+    if (FP8) {
+      const float hs = p.hs[slot];
+      const f32x4 sp = *(const f32x4*)(p.w2s + (size_t)e * p.H + row);
+      const f32x4 sq = *(const f32x4*)(p.w2s + (size_t)e * p.H + row + 8);
 #pragma unroll
-  for (int t = 0; t < 4; ++t) ok[t] = t < MT && slot[t] < p.S;
-  f32x4 acc[4] = {};
-  if (FP8) {
-    const uint8_t* a_ptr = (const uint8_t*)p.w2 + arow * p.I + 16 * g;
-    const uint8_t* b_ptr[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      b_ptr[t] = (const uint8_t*)p.h + (size_t)(ok[t] ? slot[t] : 0) * p.I + 16 * g;
-    kloop_fp8<MT, (MT == 1 ? 4 : (MT == 2 ? 2 : 1))>(a_ptr, b_ptr, ok, p.I, acc);
-  } else {
-    const uint16_t* a_ptr = (const uint16_t*)p.w2 + arow * p.I + 8 * g;
-    const uint16_t* b_ptr[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      b_ptr[t] = (const uint16_t*)p.h + (size_t)(ok[t] ? slot[t] : 0) * p.I + 8 * g;
-    kloop_bf16<MT, 8 / MT>(a_ptr, b_ptr, ok, p.I, acc);
+      for (int i = 0; i < 4; ++i) {
+        vp[i] *= sp[i] * hs;
+        vq[i] *= sq[i] * hs;
+      }
+    }
+    float* yr = p.y + (size_t)slot * p.H + row;
+    *(f32x4*)yr = vp;
+    *(f32x4*)(yr + 8) = vq;
   }
-  f32x4 ws = {1.f, 1.f, 1.f, 1.f};
-  if (FP8) ws = *(const f32x4*)(p.w2s + (size_t)e * p.H + r * 16 + 4 * g);
+}
+
+// Hot FC2 tile r: output rows [16r, 16r+16).
+template <bool FP8, int MT>
+__device__ __forceinline__ void fc2_hot_pass(const Fc2Args& p, int e, int r, int b, int M, int m,
+                                             int t0, uint8_t* lds) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, rho = lane & 15;
+  const size_t rowb = (size_t)p.I * (FP8 ? 1 : 2);
+  const uint8_t* a = (const uint8_t*)p.w2 + ((size_t)e * p.H + r * 16 + rho) * rowb + 16 * g;
+  Stage st;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ti = t0 + (threadIdx.x >> 4) + 16 * i;
+    const int slot = ti < m ? p.sorted_ids[(size_t)b * M + ti] : p.S;
+    st.src[i] = slot < p.S ? (const uint8_t*)p.h + (size_t)slot * rowb : nullptr;
+  }
+  f32x4 acc[4] = {};
+  hot_kloop<FP8, MT>(a, st, (int)rowb, lds, acc);
+  const int row = r * 16 + 4 * g;
+  f32x4 sc = {1.f, 1.f, 1.f, 1.f};
+  if (FP8) sc = *(const f32x4*)(p.w2s + (size_t)e * p.H + row);
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
-    if (!ok[t]) continue;
-    f32x4 v = acc[t];
-    if (FP8) {
-      const float hs = p.hs[slot[t]];
+    const int ti = t0 + 16 * t + rho;
+    const int slot = ti < m ? p.sorted_ids[(size_t)b * M + ti] : p.S;
+    if (slot < p.S) {
+      f32x4 v = acc[t];
+      if (FP8) {
+        const float hs = p.hs[slot];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = v[i] * ws[i] * hs;
+        for (int i = 0; i < 4; ++i) v[i] *= sc[i] * hs;
+      }
+      *(f32x4*)(p.y + (size_t)slot * p.H + row) = v;
     }
-    *(f32x4*)(p.y + (size_t)slot[t] * p.H + r * 16 + 4 * g) = v;
+  }
+}
+
+// ------------------------------------------------- persistent kernels ---
+
+template <bool FP8, typename Args, void (*Cold_)(const Args&, int, int, int, int, int),
+          void (*H1)(const Args&, int, int, int, int, int, int, uint8_t*),
+          void (*H2)(const Args&, int, int, int, int, int, int, uint8_t*),
+          void (*H3)(const Args&, int, int, int, int, int, int, uint8_t*),
+          void (*H4)(const Args&, int, int, int, int, int, int, uint8_t*)>
+__device__ __forceinline__ void run_quads(const Args& p, int n_rt, uint8_t* lds) {
+  const int M = 1 << p.log2m;
+  const int nb = p.num_padded[0] >> p.log2m;
+  const int qpb = n_rt >> 2;  // quads per block (n_rt is a multiple of 4)
+  const Share sh = wg_share((long)nb * qpb, p.remap);
+  const int w = threadIdx.x >> 6;
+  int cur_b = -1, e = 0, m = 0;
+  for (long qd = sh.q0; qd < sh.q1; ++qd) {  // uniform across the workgroup
+    const int b = (int)(qd / qpb);
+    const int r = (int)(qd % qpb) * 4 + w;
+    if (b != cur_b) {
+      cur_b = b;
+      e = p.block_expert[b];
+      m = block_valid(p.sorted_ids, b, M, p.S);
+    }
+    if (m <= kColdMax) {
+      Cold_(p, e, r, b, M, m);
+    } else {
+      for (int t0 = 0; t0 < m; t0 += kHotTok) {
+        const int mt = min(4, (m - t0 + 15) >> 4);
+        if (mt == 1) H1(p, e, r, b, M, m, t0, lds);
+        else if (mt == 2) H2(p, e, r, b, M, m, t0, lds);
+        else if (mt == 3) H3(p, e, r, b, M, m, t0, lds);
+        else H4(p, e, r, b, M, m, t0, lds);
+      }
+    }
   }
 }
 
 template <bool FP8>
+__global__ __launch_bounds__(256) void fc1_kernel(Fc1Args p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kHotTok * kLdsRow];
+  run_quads<FP8, Fc1Args, fc1_cold<FP8>, fc1_hot_pass<FP8, 1>, fc1_hot_pass<FP8, 2>,
+            fc1_hot_pass<FP8, 3>, fc1_hot_pass<FP8, 4>>(p, p.I >> 3, lds);
+}
+
+template <bool FP8>
 __global__ __launch_bounds__(256) void fc2_kernel(Fc2Args p) {
-  const int M = 1 << p.log2m;
-  const int nb = p.num_padded[0] >> p.log2m;
-  const int n_rt = p.H >> 4;
-  const WaveRange wr = wave_range((long)nb * n_rt, p.remap);
-  int cur_b = -1, e = 0, m_valid = 0;
-  for (long u = wr.u0; u < wr.u1; ++u) {
-    const int b = (int)(u / n_rt), r = (int)(u % n_rt);
-    if (b != cur_b) {
-      cur_b = b;
-      e = p.block_expert[b];
-      m_valid = block_valid(p.sorted_ids, b, M, p.S);
-    }
-    for (int t0 = 0; t0 < m_valid; t0 += 64) {
-      int slot[4];
-      group_slots(p.sorted_ids, b, M, p.S, m_valid, t0, slot);
-      const int mt = min(4, (m_valid - t0 + 15) >> 4);
-      if (mt == 1) fc2_group<1, FP8>(p, e, r, slot);
-      else if (mt == 2) fc2_group<2, FP8>(p, e, r, slot);
-      else if (mt == 3) fc2_group<3, FP8>(p, e, r, slot);
-      else fc2_group<4, FP8>(p, e, r, slot);
-    }
-  }
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kHotTok * kLdsRow];
+  run_quads<FP8, Fc2Args, fc2_cold<FP8>, fc2_hot_pass<FP8, 1>, fc2_hot_pass<FP8, 2>,
+            fc2_hot_pass<FP8, 3>, fc2_hot_pass<FP8, 4>>(p, p.H >> 4, lds);
 }
 
 // ----------------------------------------------- per-row FP8 quantiser ---
