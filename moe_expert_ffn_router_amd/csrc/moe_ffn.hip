@@ -566,6 +566,256 @@ __global__ __launch_bounds__(256) void fc2_kernel(Fc2Args p) {
             fc2_hot_pass<FP8, 3>, fc2_hot_pass<FP8, 4>>(p, p.H >> 4, lds);
 }
 
+// ------------------------------------------- dense tiles (big blocks) ---
+// For blocks of 128..256 tokens (prefill) the projection is a real grouped
+// GEMM: a workgroup multiplies a 128-row weight tile by the block's 128-token
+// tile, both staged through LDS 64 k-elements (128 bytes) at a time, double
+// buffered; its 4 waves each own 64 rows x 64 tokens (4 x 4 MFMA 16x16x32
+// tiles). Units (block, 128-row tile) are ordered expert by expert, row tile
+// by row tile with the expert's blocks innermost, and dealt round-robin to a
+// virtual workgroup index that is laid out XCD by XCD: the blocks of one
+// expert that share a weight tile run at the same time on the same XCD, so
+// the tile crosses HBM once and L2 serves the rest.
+
+constexpr int kDRows = 128;   // weight rows per unit
+constexpr int kDTok = 128;    // tokens per unit
+constexpr int kDChunk = 128;  // bytes of K per staged chunk (64 bf16)
+constexpr int kDPitch = kDChunk + 16;
+constexpr int kDTile = kDRows * kDPitch;  // bytes of one staged operand tile
+
+// First block and length of the run of blocks with expert e containing bn
+// (block_expert is non-decreasing). Wave-wide probes of 64 blocks.
+__device__ __forceinline__ void find_run(const int32_t* __restrict__ block_expert, int nb, int bn,
+                                         int e, int& fb, int& q) {
+  const int lane = threadIdx.x & 63;
+  int lo = bn;
+  for (;;) {
+    const int i = lo - 64 + lane;
+    const uint64_t m = __ballot(i >= 0 && block_expert[i] == e);
+    if (m == ~0ull) {
+      lo -= 64;
+      continue;
+    }
+    lo = lo - 64 + (63 - __clzll(~m)) + 1;
+    break;
+  }
+  int hi = bn + 1;
+  for (;;) {
+    const int i = hi + lane;
+    const uint64_t m = __ballot(i < nb && block_expert[i] == e);
+    if (m == ~0ull) {
+      hi += 64;
+      continue;
+    }
+    hi += __ffsll((long long)~m) - 1;
+    break;
+  }
+  fb = lo;
+  q = hi - lo;
+}
+
+// This workgroup's virtual index: consecutive virtual indices share an XCD.
+__device__ __forceinline__ int virtual_wg(int remap) {
+  const int wg = blockIdx.x, G = gridDim.x;
+  if (!remap || (G & 7) != 0) return wg;
+  return (wg & 7) * (G >> 3) + (wg >> 3);
+}
+
+struct DenseStage {
+  u32x4 a[4], b[4];
+  const uint8_t* arow[4];  // this thread's 4 weight rows (+ its 16-byte column)
+  const uint8_t* brow[4];  // this thread's 4 token rows, null past the block
+  __device__ __forceinline__ void load(int c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = *(const u32x4*)(arow[i] + (size_t)c * kDChunk);
+      b[i] = u32x4{0, 0, 0, 0};
+      if (brow[i]) b[i] = *(const u32x4*)(brow[i] + (size_t)c * kDChunk);
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* __restrict__ buf) const {
+    const int r0 = threadIdx.x >> 3, col = (threadIdx.x & 7) * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *(u32x4*)(buf + (r0 + 32 * i) * kDPitch + col) = a[i];
+      *(u32x4*)(buf + kDTile + (r0 + 32 * i) * kDPitch + col) = b[i];
+    }
+  }
+};
+
+// acc[i][j] += A rows (64*wr + 16i ..) . B tokens (64*wc + 16j ..) of one chunk
+__device__ __forceinline__ void dense_compute(const uint8_t* __restrict__ buf, int wr, int wc,
+                                              f32x4 (&acc)[4][4]) {
+  const int lane = threadIdx.x & 63;
+  const uint8_t* pa = buf + (64 * wr + (lane & 15)) * kDPitch + (lane >> 4) * 16;
+  const uint8_t* pb = buf + kDTile + (64 * wc + (lane & 15)) * kDPitch + (lane >> 4) * 16;
+#pragma unroll
+  for (int s = 0; s < kDChunk / 64; ++s) {
+    bf16x8 fa[4], fb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8*)(pa + i * 16 * kDPitch + s * 64);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = *(const bf16x8*)(pb + j * 16 * kDPitch + s * 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(fa[i], fb[j], acc[i][j]);
+  }
+}
+
+// The whole K loop of one unit; every thread of the workgroup takes part.
+// Two register stages alternate with two LDS buffers: while chunk c is
+// multiplied out of LDS, chunk c+1 waits in registers to be stored and chunk
+// c+2 is being loaded, so every global load has two iterations to land.
+__device__ __forceinline__ void dense_kloop(DenseStage& s0, DenseStage& s1, int kbytes,
+                                            bool active, int wr, int wc,
+                                            uint8_t* __restrict__ lds, f32x4 (&acc)[4][4]) {
+  uint8_t* buf0 = lds;
+  uint8_t* buf1 = lds + 2 * kDTile;
+  const int nch = kbytes / kDChunk;
+  s0.load(0);
+  if (nch > 1) s1.load(1);
+  s0.store(buf0);
+  __syncthreads();
+  int c = 0;
+  for (; c + 1 < nch; c += 2) {
+    // chunk c in buf0, chunk c+1 in flight in s1
+    if (c + 2 < nch) s0.load(c + 2);
+    if (active) dense_compute(buf0, wr, wc, acc);
+    s1.store(buf1);
+    __syncthreads();
+    // chunk c+1 in buf1, chunk c+2 in flight in s0
+    if (c + 3 < nch) s1.load(c + 3);
+    if (active) dense_compute(buf1, wr, wc, acc);
+    if (c + 2 < nch) s0.store(buf0);
+    __syncthreads();
+  }
+  if (c < nch) {
+    if (active) dense_compute(buf0, wr, wc, acc);
+    __syncthreads();
+  }
+}
+
+// Map unit u of the (expert, row tile, block) order to (row tile r, block b).
+struct UnitMap {
+  int nb, n_rt;
+  int run_b0 = 0, run_q = 0, e = 0;
+  long run_u0 = 0, run_u1 = 0;
+  __device__ __forceinline__ void locate(const int32_t* __restrict__ block_expert, long u, int& r,
+                                         int& b) {
+    if (u >= run_u1 || u < run_u0) {
+      const int bn = (int)(u / n_rt);
+      e = block_expert[bn];
+      find_run(block_expert, nb, bn, e, run_b0, run_q);
+      run_u0 = (long)run_b0 * n_rt;
+      run_u1 = run_u0 + (long)run_q * n_rt;
+    }
+    const long loc = u - run_u0;
+    r = (int)(loc / run_q);
+    b = run_b0 + (int)(loc % run_q);
+  }
+};
+
+__global__ __launch_bounds__(256) void dense_fc1_kernel(Fc1Args p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kDTile];
+  const int M = 1 << p.log2m;
+  const int nb = p.num_padded[0] >> p.log2m;
+  const int n_rt = (2 * p.I) / kDRows;  // 64 gate + 64 up rows per unit
+  const long units = (long)nb * n_rt;
+  const int w = threadIdx.x >> 6, wr = w & 1, wc = w >> 1, lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const size_t rowb = (size_t)p.H * 2;
+  UnitMap um{nb, n_rt};
+  for (long u = virtual_wg(p.remap); u < units; u += gridDim.x) {
+    int r, b;
+    um.locate(p.block_expert, u, r, b);
+    const int e = um.e;
+    for (int t0 = 0; t0 < M; t0 += kDTok) {
+      const int m = block_valid(p.sorted_ids, b, M, p.S) - t0;
+      if (m <= 0) break;
+      DenseStage st;
+      const int r0 = threadIdx.x >> 3, col = (threadIdx.x & 7) * 16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rho = r0 + 32 * i, tt = rho >> 4, wi = rho & 15;
+        const int wrow = wi < 8 ? (r * 64 + tt * 8 + wi) : (p.I + r * 64 + tt * 8 + wi - 8);
+        st.arow[i] = (const uint8_t*)p.w1 + ((size_t)e * 2 * p.I + wrow) * rowb + col;
+        const int slot = rho < m ? p.sorted_ids[(size_t)b * M + t0 + rho] : p.S;
+        st.brow[i] = slot < p.S ? (const uint8_t*)p.x + (size_t)(slot / p.k) * rowb + col : nullptr;
+      }
+      f32x4 acc[4][4] = {};
+      const bool active = 64 * wc < m;
+      DenseStage st1 = st;
+      dense_kloop(st, st1, (int)rowb, active, wr, wc, lds, acc);
+      if (!active) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ti = 64 * wc + 16 * j + (lane & 15);
+        const int slot = ti < m ? p.sorted_ids[(size_t)b * M + t0 + ti] : p.S;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f32x4 o;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) o[q] = __shfl_xor(acc[i][j][q], 32);
+          if (lane < 32 && slot < p.S) {
+            const int colh = r * 64 + (4 * wr + i) * 8 + 4 * g;
+            uint32_t hb[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) hb[q] = f32_to_bf16_rne(silu_mul(acc[i][j][q], o[q]));
+            *(u32x2*)((uint16_t*)p.h + (size_t)slot * p.I + colh) =
+                u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+          }
+        }
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void dense_fc2_kernel(Fc2Args p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kDTile];
+  const int M = 1 << p.log2m;
+  const int nb = p.num_padded[0] >> p.log2m;
+  const int n_rt = p.H / kDRows;
+  const long units = (long)nb * n_rt;
+  const int w = threadIdx.x >> 6, wr = w & 1, wc = w >> 1, lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const size_t rowb = (size_t)p.I * 2;
+  UnitMap um{nb, n_rt};
+  for (long u = virtual_wg(p.remap); u < units; u += gridDim.x) {
+    int r, b;
+    um.locate(p.block_expert, u, r, b);
+    const int e = um.e;
+    for (int t0 = 0; t0 < M; t0 += kDTok) {
+      const int m = block_valid(p.sorted_ids, b, M, p.S) - t0;
+      if (m <= 0) break;
+      DenseStage st;
+      const int r0 = threadIdx.x >> 3, col = (threadIdx.x & 7) * 16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rho = r0 + 32 * i;
+        st.arow[i] = (const uint8_t*)p.w2 + ((size_t)e * p.H + r * kDRows + rho) * rowb + col;
+        const int slot = rho < m ? p.sorted_ids[(size_t)b * M + t0 + rho] : p.S;
+        st.brow[i] = slot < p.S ? (const uint8_t*)p.h + (size_t)slot * rowb + col : nullptr;
+      }
+      f32x4 acc[4][4] = {};
+      const bool active = 64 * wc < m;
+      DenseStage st1 = st;
+      dense_kloop(st, st1, (int)rowb, active, wr, wc, lds, acc);
+      if (!active) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ti = 64 * wc + 16 * j + (lane & 15);
+        const int slot = ti < m ? p.sorted_ids[(size_t)b * M + t0 + ti] : p.S;
+        if (slot < p.S) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            *(f32x4*)(p.y + (size_t)slot * p.H + r * kDRows + 64 * wr + 16 * i + 4 * g) = acc[i][j];
+        }
+      }
+    }
+  }
+}
+
 // ----------------------------------------------- per-row FP8 quantiser ---
 // One wave per row: absmax, scale = absmax/448 (1 for a zero row), then
 // code = e4m3fn(v / scale); both divisions are correctly rounded fp32.
@@ -816,16 +1066,23 @@ hipError_t launch_ffn_bf16(const FfnProblem& p, hipStream_t stream) {
   void* h = (char*)p.workspace + L.h_off;
   float* y = (float*)((char*)p.workspace + L.y_off);
   hipError_t err;
+  const bool dense = p.block_m >= kDTok;  // prefill-sized blocks: grouped GEMM tiles
   if (st & MOE_FFN_STAGE_FC1) {
     Fc1Args a{p.x, nullptr, p.w1, nullptr, p.sorted_ids, p.block_expert, p.num_padded,
               p.H, p.I, p.k, S, log2m, remap, h};
-    fc1_kernel<false><<<persistent_grid(fc1_kernel<false>, 0), 256, 0, stream>>>(a);
+    if (dense)
+      dense_fc1_kernel<<<persistent_grid(dense_fc1_kernel, 4), 256, 0, stream>>>(a);
+    else
+      fc1_kernel<false><<<persistent_grid(fc1_kernel<false>, 0), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_FC2) {
     Fc2Args a{h, nullptr, p.w2, nullptr, p.sorted_ids, p.block_expert, p.num_padded,
               p.H, p.I, S, log2m, remap, y};
-    fc2_kernel<false><<<persistent_grid(fc2_kernel<false>, 1), 256, 0, stream>>>(a);
+    if (dense)
+      dense_fc2_kernel<<<persistent_grid(dense_fc2_kernel, 5), 256, 0, stream>>>(a);
+    else
+      fc2_kernel<false><<<persistent_grid(fc2_kernel<false>, 1), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_COMBINE) return launch_combine(p, L, true, stream);
