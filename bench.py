@@ -34,7 +34,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, help="workload number 1..5 (default 2)")
-    ap.add_argument("--block-m", type=int, default=64)
+    ap.add_argument("--block-m", type=int, default=0,
+                    help="block size; 0 = moe_default_block_m for the workload")
     ap.add_argument("--flags", type=int, default=0, help="extra moe_ffn flags (e.g. 256 = no XCD remap)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -137,7 +138,8 @@ def main():
     torch.cuda.set_device(0)
     cfg = CONFIGS[args.config]
     inp = config_inputs(args.config, device="cuda")
-    T, E, H, I, k, M = inp.T, inp.E, inp.H, inp.I, inp.k, args.block_m
+    T, E, H, I, k = inp.T, inp.E, inp.H, inp.I, inp.k
+    M = args.block_m or moe.default_block_m(T, E, k)
     S = T * k
     dev = inp.x.device
     dt_code = {"f32": moe.MOE_DTYPE_F32, "bf16": moe.MOE_DTYPE_BF16, "fp8": moe.MOE_DTYPE_FP8}[inp.dtype]

@@ -127,10 +127,20 @@ moe_status moe_align_block(const int32_t* topk_ids, int T, int k, int E, int blo
                            moe_stream_t stream);
 
 /*
+ * Block size suggested for a batch: 256 when the average number of slots per
+ * expert, T*k/E, is at least 128 (prefill-sized blocks: the FFN then runs
+ * grouped-GEMM tiles of 256 weight rows x 256 tokens), else 64 (decode: the
+ * FFN streams weight tiles and shares up to 64 tokens of a block per tile).
+ * Any power of two in [1, 256] is valid for every entry point; this one only
+ * picks the fast regime. Returns 0 for invalid T, E or k.
+ */
+int moe_default_block_m(int T, int E, int k);
+
+/*
  * Bytes of device workspace the FFN needs (dtype = MOE_DTYPE_*). Base must be
  * 256-byte aligned; its contents need no initialisation. Layout, S = T*k,
  * each region starting at the next 256-byte boundary after the previous one:
- *   bf16: h bf16 [S, I] | y f32 [S, H]
+ *   bf16: h bf16 [S, I] | y bf16 [S, H]
  *   fp8 : h f32 [S, I] | hq e4m3 [S, I] | hs f32 [S] | xq e4m3 [T, H] |
  *         xs f32 [T] | y f32 [S, H]
  *   f32 : h f32 [S, I] | y f32 [S, H]

@@ -32,8 +32,8 @@ NO_XCD_REMAP = 1 << 8
 ABI_VERSION = 1
 
 EXPORTS = ("moe_status_str", "moe_abi_version", "moe_route_topk", "moe_align_capacity",
-           "moe_align_block", "moe_ffn_workspace_bytes", "moe_ffn_bf16", "moe_ffn_fp8",
-           "moe_ffn_f32")
+           "moe_align_block", "moe_default_block_m", "moe_ffn_workspace_bytes", "moe_ffn_bf16",
+           "moe_ffn_fp8", "moe_ffn_f32")
 
 
 class MoEError(RuntimeError):
@@ -47,7 +47,7 @@ class MoEError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
-                          "(or python -m moe_expert_ffn_router_amd.build)")
+                          "(or python moe_expert_ffn_router_amd/build.py)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, U, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
     lib.moe_status_str.restype = ctypes.c_char_p
@@ -60,6 +60,8 @@ def _load() -> ctypes.CDLL:
     lib.moe_align_capacity.argtypes = [I, I, I, I]
     lib.moe_align_block.restype = I
     lib.moe_align_block.argtypes = [P, I, I, I, I, P, P, P, P]
+    lib.moe_default_block_m.restype = I
+    lib.moe_default_block_m.argtypes = [I, I, I]
     lib.moe_ffn_workspace_bytes.restype = Z
     lib.moe_ffn_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     ffn_tail = [P, P, P, P, P, I, I, I, I, I, I, U, P, Z, P, P]
@@ -127,6 +129,11 @@ def route_topk(logits: torch.Tensor, k: int, renormalize: bool = False, out=None
 
 def align_capacity(T: int, k: int, E: int, block_m: int) -> int:
     return int(lib.moe_align_capacity(T, k, E, block_m))
+
+
+def default_block_m(T: int, E: int, k: int) -> int:
+    """moe_default_block_m: the block size of the fast regime for this batch."""
+    return int(lib.moe_default_block_m(T, E, k))
 
 
 def align_block(topk_ids: torch.Tensor, E: int, block_m: int, out=None, stream=None):
@@ -234,10 +241,13 @@ def ffn_f32(x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert, num_pad
     return out
 
 
-def forward(x, logits, w1, w2, k: int, block_m: int = 64, renormalize: bool = False,
+def forward(x, logits, w1, w2, k: int, block_m: Optional[int] = None, renormalize: bool = False,
             w1_scale=None, w2_scale=None, flags: int = 0, stream=None):
-    """route_topk -> align_block -> ffn_{f32,bf16,fp8}, dtype taken from w1."""
+    """route_topk -> align_block -> ffn_{f32,bf16,fp8}, dtype taken from w1;
+    block_m defaults to moe_default_block_m."""
     E = w1.shape[0]
+    if block_m is None:
+        block_m = default_block_m(x.shape[0], E, k)
     ids, wts = route_topk(logits, k, renormalize, stream=stream)
     sorted_ids, block_expert, num_padded = align_block(ids, E, block_m, stream=stream)
     if w1.dtype in (torch.uint8, torch.float8_e4m3fn):

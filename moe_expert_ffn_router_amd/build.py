@@ -1,6 +1,6 @@
 """Build libmoe.so in-tree with hipcc for gfx950.
 
-    python -m moe_expert_ffn_router_amd.build      (or __graft_entry__.build())
+    python moe_expert_ffn_router_amd/build.py      (or __graft_entry__.build())
 
 Every call recompiles. Flags: one target (gfx950); packed-fp32 instructions
 disabled; fp32 division and sqrt correctly rounded (the FP8 quantiser's

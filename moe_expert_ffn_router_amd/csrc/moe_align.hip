@@ -23,7 +23,7 @@ namespace moe {
 constexpr int kAlignWaves = 8;
 constexpr int kAlignThreads = kAlignWaves * kWave;
 constexpr int kAlignMaxE = 1024;
-constexpr int kAlignUnroll = 4;
+constexpr int kAlignUnroll = 16;
 
 __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     const int32_t* __restrict__ ids, int S, int E, int log2m, int cap,

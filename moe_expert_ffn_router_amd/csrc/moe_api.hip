@@ -120,6 +120,11 @@ MOE_EXPORT moe_status moe_align_block(const int32_t* topk_ids, int T, int k, int
                                       block_expert, num_padded, (hipStream_t)stream));
 }
 
+MOE_EXPORT int moe_default_block_m(int T, int E, int k) {
+  if (check_common(T, E, k) != MOE_OK) return 0;
+  return (long)T * k >= 128L * E ? 256 : 64;
+}
+
 MOE_EXPORT size_t moe_ffn_workspace_bytes(int T, int E, int H, int I, int k, int block_m,
                                           int dtype) {
   (void)E;

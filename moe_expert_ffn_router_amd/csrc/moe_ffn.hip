@@ -39,7 +39,11 @@ namespace moe {
 constexpr int kColdMax = 8;     // a block with at most this many tokens is cold
 constexpr int kHotTok = 64;     // tokens per pass of a hot quad (4 MFMA column tiles)
 constexpr int kHotChunk = 256;  // bytes of K per staged chunk (both dtypes)
-constexpr int kLdsRow = kHotChunk + 16;  // padded LDS row: conflict-free B reads
+// LDS rows are 256 bytes, unpadded: 16-byte column c of row r sits at column
+// c ^ (r & 7), so the staging stores and the MFMA fragment reads (rows
+// r0..r0+15 at one column) hit distinct banks.
+constexpr int kLdsRow = kHotChunk;
+__device__ __forceinline__ int hswz(int row, int col16) { return row * kLdsRow + ((col16 ^ (row & 7)) << 4); }
 
 // ------------------------------------------------- work partitioning ---
 
@@ -249,19 +253,26 @@ struct HotA {
 };
 
 // One chunk of MFMAs: A from registers, B fragments from the LDS buffer.
+// A B fragment of k-step s takes the 16-byte column s*kKstep/16 + g (and, for
+// fp8, the column 4 further); fragment rows are 16-aligned bases + (lane & 15),
+// so the swizzle term is lane & 7.
 template <bool FP8, int MT>
 __device__ __forceinline__ void hot_compute(const HotA<FP8>& a, const uint8_t* __restrict__ buf,
                                             f32x4 (&acc)[4]) {
   const int lane = threadIdx.x & 63;
-  const uint8_t* base = buf + (lane & 15) * kLdsRow + (lane >> 4) * 16;
+  const uint8_t* base = buf + (lane & 15) * kLdsRow;
+  const int x = lane & 7, g = lane >> 4;
 #pragma unroll
-  for (int s = 0; s < Hot<FP8>::kSteps; ++s)
+  for (int s = 0; s < Hot<FP8>::kSteps; ++s) {
+    const int c0 = ((s * Hot<FP8>::kKstep / 16 + g) ^ x) << 4;
+    const int c1 = ((s * Hot<FP8>::kKstep / 16 + 4 + g) ^ x) << 4;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       Frag<FP8> b;
-      b.lds(base + t * 16 * kLdsRow + s * Hot<FP8>::kKstep, 64);
+      b.lds(base + t * 16 * kLdsRow + c0, c1 - c0);
       acc[t] = mfma(a.f[s], b, acc[t]);
     }
+  }
 }
 
 // Staging: 256 threads move 64 token rows x 256 bytes (4 x 16 bytes each).
@@ -279,7 +290,7 @@ struct Stage {
   __device__ __forceinline__ void store(uint8_t* __restrict__ buf) const {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      *(u32x4*)(buf + ((threadIdx.x >> 4) + 16 * i) * kLdsRow + (threadIdx.x & 15) * 16) = v[i];
+      *(u32x4*)(buf + hswz((threadIdx.x >> 4) + 16 * i, threadIdx.x & 15)) = v[i];
   }
 };
 
@@ -443,8 +454,20 @@ struct Fc2Args {
   const int32_t* block_expert;
   const int32_t* num_padded;
   int H, I, S, log2m, remap;
-  float* y;            // f32 [S, H]
+  void* y;             // per-slot FC2 output [S, H]: bf16 (bf16 path) or f32
+  int y_bf16;
 };
+
+// Store 4 consecutive FC2 outputs of one slot.
+__device__ __forceinline__ void store_y(const Fc2Args& p, int slot, int row, const f32x4& v) {
+  if (p.y_bf16) {
+    *(u32x2*)((uint16_t*)p.y + (size_t)slot * p.H + row) =
+        u32x2{f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+              f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
+  } else {
+    *(f32x4*)((float*)p.y + (size_t)slot * p.H + row) = v;
+  }
+}
 
 // Cold FC2 tile r: P = output rows [16r, 16r+8), Q = [16r+8, 16r+16).
 template <bool FP8>
@@ -475,9 +498,8 @@ __device__ __forceinline__ void fc2_cold(const Fc2Args& p, int e, int r, int b, 
         vq[i] *= sq[i] * hs;
       }
     }
-    float* yr = p.y + (size_t)slot * p.H + row;
-    *(f32x4*)yr = vp;
-    *(f32x4*)(yr + 8) = vq;
+    store_y(p, slot, row, vp);
+    store_y(p, slot, row + 8, vq);
   }
 }
 
@@ -511,7 +533,7 @@ __device__ __forceinline__ void fc2_hot_pass(const Fc2Args& p, int e, int r, int
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] *= sc[i] * hs;
       }
-      *(f32x4*)(p.y + (size_t)slot * p.H + row) = v;
+      store_y(p, slot, row, v);
     }
   }
 }
@@ -567,21 +589,114 @@ __global__ __launch_bounds__(256) void fc2_kernel(Fc2Args p) {
 }
 
 // ------------------------------------------- dense tiles (big blocks) ---
-// For blocks of 128..256 tokens (prefill) the projection is a real grouped
-// GEMM: a workgroup multiplies a 128-row weight tile by the block's 128-token
-// tile, both staged through LDS 64 k-elements (128 bytes) at a time, double
-// buffered; its 4 waves each own 64 rows x 64 tokens (4 x 4 MFMA 16x16x32
-// tiles). Units (block, 128-row tile) are ordered expert by expert, row tile
-// by row tile with the expert's blocks innermost, and dealt round-robin to a
-// virtual workgroup index that is laid out XCD by XCD: the blocks of one
-// expert that share a weight tile run at the same time on the same XCD, so
-// the tile crosses HBM once and L2 serves the rest.
+// For blocks of up to 256 tokens (prefill) the projection is a real grouped
+// GEMM: a 512-thread workgroup multiplies a 256-row weight tile by the block's
+// 256-token tile, both staged through LDS 64 k-elements (128 bytes) at a time,
+// double buffered (144 KB, one workgroup per CU). Its 8 waves each own 64 rows
+// x 128 tokens (4 x 8 MFMA 16x16x32 tiles, 128 accumulators), so each staged
+// byte feeds 64..128 MFMAs per k-step. Units (block, 256-row tile) are ordered
+// expert by expert, row tile by row tile with the expert's blocks innermost,
+// and dealt round-robin to a virtual workgroup index laid out XCD by XCD, so
+// blocks of one expert that share a weight tile run together on one XCD and
+// the tile crosses HBM once.
 
-constexpr int kDRows = 128;   // weight rows per unit
-constexpr int kDTok = 128;    // tokens per unit
-constexpr int kDChunk = 128;  // bytes of K per staged chunk (64 bf16)
-constexpr int kDPitch = kDChunk + 16;
-constexpr int kDTile = kDRows * kDPitch;  // bytes of one staged operand tile
+constexpr int kDRows = 256;   // weight rows per unit
+constexpr int kDTok = 256;    // tokens per unit
+constexpr int kDThreads = 512;
+constexpr int kDChunk = 128;  // bytes of K per stage (64 bf16, two MFMA k-steps) = one LDS row
+constexpr int kDStages = 2;   // LDS double buffer
+constexpr int kDTile = kDRows * kDChunk;   // bytes of one staged operand tile (32 KB)
+constexpr int kDStage = 2 * kDTile;        // A tile + B tile
+// LDS rows are 128 bytes (8 columns of 16 bytes) with no padding; column c of
+// row r sits at column c ^ (r & 7), conflict-free for the MFMA fragment
+// reads (16 consecutive rows, one column) on gfx950.
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Staging by direct-to-LDS loads: one load instruction of a wave writes 1 KB
+// of LDS in lane order (lane l -> bytes 16 l..16 l+15), i.e. 8 whole LDS rows,
+// and reads 8 whole 128-byte lines. Wave w stages rows [32 w, 32 w + 32) of
+// each operand with 4 instructions; lane l fills physical column l & 7 of row
+// l >> 3 of its 8-row group, so it loads the logical column (l & 7) ^ (l >> 3).
+// Token groups lying wholly past the block's tokens are not loaded (their
+// MFMA columns are never stored).
+struct DenseStage {
+  const uint8_t* arow[4];  // this lane's source weight rows (+ logical column)
+  const uint8_t* brow[4];  // this lane's source token rows (+ logical column)
+  int bgroups;             // this wave's token groups holding real tokens (0..4)
+  __device__ __forceinline__ void issue(uint8_t* __restrict__ stage, int c) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint8_t* da = stage + (32 * w + 8 * i) * kDChunk;
+      __builtin_amdgcn_global_load_lds((const void*)(arow[i] + (size_t)c * kDChunk), (lds_ptr_t)da,
+                                       16, 0, 0);
+      if (i < bgroups)
+        __builtin_amdgcn_global_load_lds((const void*)(brow[i] + (size_t)c * kDChunk),
+                                         (lds_ptr_t)(da + kDTile), 16, 0, 0);
+    }
+  }
+  __device__ __forceinline__ int loads() const { return 4 + bgroups; }
+};
+
+// Row of this lane in staging instruction i, and its logical 16-byte column.
+__device__ __forceinline__ int dstage_row(int i) {
+  return 32 * (threadIdx.x >> 6) + 8 * i + ((threadIdx.x & 63) >> 3);
+}
+__device__ __forceinline__ int dstage_col() {
+  const int l = threadIdx.x & 63;
+  return ((l & 7) ^ (l >> 3)) * 16;
+}
+// Number of 8-row token groups of wave w holding at least one of the m tokens.
+__device__ __forceinline__ int dstage_bgroups(int m) {
+  const int first = 32 * (threadIdx.x >> 6);
+  return max(0, min(4, (m - first + 7) >> 3));
+}
+
+// acc[i][j] += A rows (64*wr + 16i ..) . B tokens (128*wc + 16j ..) for the
+// two MFMA k-steps of one stage: per k-step all 12 fragments are read, then
+// 32 MFMAs run on them.
+__device__ __forceinline__ void dense_compute(const uint8_t* __restrict__ stage, int wr, int wc,
+                                              f32x4 (&acc)[4][8]) {
+  const int lane = threadIdx.x & 63;
+  // fragment rows are 16-aligned bases + (lane & 15), so row & 7 == lane & 7
+  const uint8_t* pa = stage + (64 * wr + (lane & 15)) * kDChunk;
+  const uint8_t* pb = stage + kDTile + (128 * wc + (lane & 15)) * kDChunk;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int cs = (((s << 2) + (lane >> 4)) ^ (lane & 7)) << 4;
+    bf16x8 fa[4], fb[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8*)(pa + i * 16 * kDChunk + cs);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) fb[j] = *(const bf16x8*)(pb + j * 16 * kDChunk + cs);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i][j] = mfma_bf16(fa[i], fb[j], acc[i][j]);
+  }
+}
+
+// Wait until at most n direct-to-LDS loads of this wave are outstanding.
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0xF70); }
+
+// The whole K loop of one unit; all 512 threads take part. While chunk c is
+// multiplied out of one stage, chunk c+1 streams into the other.
+__device__ __forceinline__ void dense_kloop(const DenseStage& st, int kbytes, bool active, int wr,
+                                            int wc, uint8_t* __restrict__ lds, f32x4 (&acc)[4][8]) {
+  const int nch = kbytes / kDChunk;
+  // stage addresses are computed from the LDS base so they stay in the LDS
+  // address space
+  st.issue(lds, 0);
+  wait_vm0();
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    if (c + 1 < nch) st.issue(lds + ((c + 1) & 1) * kDStage, c + 1);
+    if (active) dense_compute(lds + (c & 1) * kDStage, wr, wc, acc);
+    wait_vm0();
+    __syncthreads();
+  }
+}
 
 // First block and length of the run of blocks with expert e containing bn
 // (block_expert is non-decreasing). Wave-wide probes of 64 blocks.
@@ -621,81 +736,6 @@ __device__ __forceinline__ int virtual_wg(int remap) {
   return (wg & 7) * (G >> 3) + (wg >> 3);
 }
 
-struct DenseStage {
-  u32x4 a[4], b[4];
-  const uint8_t* arow[4];  // this thread's 4 weight rows (+ its 16-byte column)
-  const uint8_t* brow[4];  // this thread's 4 token rows, null past the block
-  __device__ __forceinline__ void load(int c) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[i] = *(const u32x4*)(arow[i] + (size_t)c * kDChunk);
-      b[i] = u32x4{0, 0, 0, 0};
-      if (brow[i]) b[i] = *(const u32x4*)(brow[i] + (size_t)c * kDChunk);
-    }
-  }
-  __device__ __forceinline__ void store(uint8_t* __restrict__ buf) const {
-    const int r0 = threadIdx.x >> 3, col = (threadIdx.x & 7) * 16;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *(u32x4*)(buf + (r0 + 32 * i) * kDPitch + col) = a[i];
-      *(u32x4*)(buf + kDTile + (r0 + 32 * i) * kDPitch + col) = b[i];
-    }
-  }
-};
-
-// acc[i][j] += A rows (64*wr + 16i ..) . B tokens (64*wc + 16j ..) of one chunk
-__device__ __forceinline__ void dense_compute(const uint8_t* __restrict__ buf, int wr, int wc,
-                                              f32x4 (&acc)[4][4]) {
-  const int lane = threadIdx.x & 63;
-  const uint8_t* pa = buf + (64 * wr + (lane & 15)) * kDPitch + (lane >> 4) * 16;
-  const uint8_t* pb = buf + kDTile + (64 * wc + (lane & 15)) * kDPitch + (lane >> 4) * 16;
-#pragma unroll
-  for (int s = 0; s < kDChunk / 64; ++s) {
-    bf16x8 fa[4], fb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8*)(pa + i * 16 * kDPitch + s * 64);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fb[j] = *(const bf16x8*)(pb + j * 16 * kDPitch + s * 64);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(fa[i], fb[j], acc[i][j]);
-  }
-}
-
-// The whole K loop of one unit; every thread of the workgroup takes part.
-// Two register stages alternate with two LDS buffers: while chunk c is
-// multiplied out of LDS, chunk c+1 waits in registers to be stored and chunk
-// c+2 is being loaded, so every global load has two iterations to land.
-__device__ __forceinline__ void dense_kloop(DenseStage& s0, DenseStage& s1, int kbytes,
-                                            bool active, int wr, int wc,
-                                            uint8_t* __restrict__ lds, f32x4 (&acc)[4][4]) {
-  uint8_t* buf0 = lds;
-  uint8_t* buf1 = lds + 2 * kDTile;
-  const int nch = kbytes / kDChunk;
-  s0.load(0);
-  if (nch > 1) s1.load(1);
-  s0.store(buf0);
-  __syncthreads();
-  int c = 0;
-  for (; c + 1 < nch; c += 2) {
-    // chunk c in buf0, chunk c+1 in flight in s1
-    if (c + 2 < nch) s0.load(c + 2);
-    if (active) dense_compute(buf0, wr, wc, acc);
-    s1.store(buf1);
-    __syncthreads();
-    // chunk c+1 in buf1, chunk c+2 in flight in s0
-    if (c + 3 < nch) s1.load(c + 3);
-    if (active) dense_compute(buf1, wr, wc, acc);
-    if (c + 2 < nch) s0.store(buf0);
-    __syncthreads();
-  }
-  if (c < nch) {
-    if (active) dense_compute(buf0, wr, wc, acc);
-    __syncthreads();
-  }
-}
-
 // Map unit u of the (expert, row tile, block) order to (row tile r, block b).
 struct UnitMap {
   int nb, n_rt;
@@ -716,13 +756,13 @@ struct UnitMap {
   }
 };
 
-__global__ __launch_bounds__(256) void dense_fc1_kernel(Fc1Args p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kDTile];
+__global__ __launch_bounds__(kDThreads) void dense_fc1_kernel(Fc1Args p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kDStages * kDStage];
   const int M = 1 << p.log2m;
   const int nb = p.num_padded[0] >> p.log2m;
-  const int n_rt = (2 * p.I) / kDRows;  // 64 gate + 64 up rows per unit
+  const int n_rt = (2 * p.I) / kDRows;  // 128 gate + 128 up rows per unit
   const long units = (long)nb * n_rt;
-  const int w = threadIdx.x >> 6, wr = w & 1, wc = w >> 1, lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6, wr = w & 3, wc = w >> 2, lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const size_t rowb = (size_t)p.H * 2;
   UnitMap um{nb, n_rt};
@@ -730,27 +770,29 @@ __global__ __launch_bounds__(256) void dense_fc1_kernel(Fc1Args p) {
     int r, b;
     um.locate(p.block_expert, u, r, b);
     const int e = um.e;
-    for (int t0 = 0; t0 < M; t0 += kDTok) {
-      const int m = block_valid(p.sorted_ids, b, M, p.S) - t0;
-      if (m <= 0) break;
+    const int mb = block_valid(p.sorted_ids, b, M, p.S);
+    for (int t0 = 0; t0 < mb; t0 += kDTok) {
+      const int m = mb - t0;
       DenseStage st;
-      const int r0 = threadIdx.x >> 3, col = (threadIdx.x & 7) * 16;
+      const int col = dstage_col();
+      const int slot0 = p.sorted_ids[(size_t)b * M + t0];  // a valid row for idle columns
+      st.bgroups = dstage_bgroups(m);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int rho = r0 + 32 * i, tt = rho >> 4, wi = rho & 15;
-        const int wrow = wi < 8 ? (r * 64 + tt * 8 + wi) : (p.I + r * 64 + tt * 8 + wi - 8);
+        // unit rows: 16-row MFMA tiles of 8 gate rows + the matching 8 up rows
+        const int rho = dstage_row(i), tt = rho >> 4, wi = rho & 15;
+        const int wrow = wi < 8 ? (r * 128 + tt * 8 + wi) : (p.I + r * 128 + tt * 8 + wi - 8);
         st.arow[i] = (const uint8_t*)p.w1 + ((size_t)e * 2 * p.I + wrow) * rowb + col;
-        const int slot = rho < m ? p.sorted_ids[(size_t)b * M + t0 + rho] : p.S;
-        st.brow[i] = slot < p.S ? (const uint8_t*)p.x + (size_t)(slot / p.k) * rowb + col : nullptr;
+        const int slot = rho < m ? p.sorted_ids[(size_t)b * M + t0 + rho] : slot0;
+        st.brow[i] = (const uint8_t*)p.x + (size_t)(slot / p.k) * rowb + col;
       }
-      f32x4 acc[4][4] = {};
-      const bool active = 64 * wc < m;
-      DenseStage st1 = st;
-      dense_kloop(st, st1, (int)rowb, active, wr, wc, lds, acc);
+      f32x4 acc[4][8] = {};
+      const bool active = 128 * wc < m;
+      dense_kloop(st, (int)rowb, active, wr, wc, lds, acc);
       if (!active) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ti = 64 * wc + 16 * j + (lane & 15);
+      for (int j = 0; j < 8; ++j) {
+        const int ti = 128 * wc + 16 * j + (lane & 15);
         const int slot = ti < m ? p.sorted_ids[(size_t)b * M + t0 + ti] : p.S;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -758,7 +800,7 @@ __global__ __launch_bounds__(256) void dense_fc1_kernel(Fc1Args p) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) o[q] = __shfl_xor(acc[i][j][q], 32);
           if (lane < 32 && slot < p.S) {
-            const int colh = r * 64 + (4 * wr + i) * 8 + 4 * g;
+            const int colh = r * 128 + (4 * wr + i) * 8 + 4 * g;
             uint32_t hb[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) hb[q] = f32_to_bf16_rne(silu_mul(acc[i][j][q], o[q]));
@@ -771,13 +813,13 @@ __global__ __launch_bounds__(256) void dense_fc1_kernel(Fc1Args p) {
   }
 }
 
-__global__ __launch_bounds__(256) void dense_fc2_kernel(Fc2Args p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kDTile];
+__global__ __launch_bounds__(kDThreads) void dense_fc2_kernel(Fc2Args p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kDStages * kDStage];
   const int M = 1 << p.log2m;
   const int nb = p.num_padded[0] >> p.log2m;
-  const int n_rt = p.H / kDRows;
+  const int n_rt = (p.H + kDRows - 1) / kDRows;  // the last row tile may be partial
   const long units = (long)nb * n_rt;
-  const int w = threadIdx.x >> 6, wr = w & 1, wc = w >> 1, lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6, wr = w & 3, wc = w >> 2, lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const size_t rowb = (size_t)p.I * 2;
   UnitMap um{nb, n_rt};
@@ -785,31 +827,35 @@ __global__ __launch_bounds__(256) void dense_fc2_kernel(Fc2Args p) {
     int r, b;
     um.locate(p.block_expert, u, r, b);
     const int e = um.e;
-    for (int t0 = 0; t0 < M; t0 += kDTok) {
-      const int m = block_valid(p.sorted_ids, b, M, p.S) - t0;
-      if (m <= 0) break;
+    const int mb = block_valid(p.sorted_ids, b, M, p.S);
+    for (int t0 = 0; t0 < mb; t0 += kDTok) {
+      const int m = mb - t0;
       DenseStage st;
-      const int r0 = threadIdx.x >> 3, col = (threadIdx.x & 7) * 16;
+      const int col = dstage_col();
+      const int slot0 = p.sorted_ids[(size_t)b * M + t0];  // a valid row for idle columns
+      st.bgroups = dstage_bgroups(m);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int rho = r0 + 32 * i;
-        st.arow[i] = (const uint8_t*)p.w2 + ((size_t)e * p.H + r * kDRows + rho) * rowb + col;
-        const int slot = rho < m ? p.sorted_ids[(size_t)b * M + t0 + rho] : p.S;
-        st.brow[i] = slot < p.S ? (const uint8_t*)p.h + (size_t)slot * rowb + col : nullptr;
+        const int rho = dstage_row(i);
+        const int wrow = min(r * kDRows + rho, p.H - 1);  // rows past H: loaded, never stored
+        st.arow[i] = (const uint8_t*)p.w2 + ((size_t)e * p.H + wrow) * rowb + col;
+        const int slot = rho < m ? p.sorted_ids[(size_t)b * M + t0 + rho] : slot0;
+        st.brow[i] = (const uint8_t*)p.h + (size_t)slot * rowb + col;
       }
-      f32x4 acc[4][4] = {};
-      const bool active = 64 * wc < m;
-      DenseStage st1 = st;
-      dense_kloop(st, st1, (int)rowb, active, wr, wc, lds, acc);
+      f32x4 acc[4][8] = {};
+      const bool active = 128 * wc < m;
+      dense_kloop(st, (int)rowb, active, wr, wc, lds, acc);
       if (!active) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ti = 64 * wc + 16 * j + (lane & 15);
+      for (int j = 0; j < 8; ++j) {
+        const int ti = 128 * wc + 16 * j + (lane & 15);
         const int slot = ti < m ? p.sorted_ids[(size_t)b * M + t0 + ti] : p.S;
         if (slot < p.S) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            *(f32x4*)(p.y + (size_t)slot * p.H + r * kDRows + 64 * wr + 16 * i + 4 * g) = acc[i][j];
+          for (int i = 0; i < 4; ++i) {
+            const int row = r * kDRows + 64 * wr + 16 * i + 4 * g;
+            if (row < p.H) store_y(p, slot, row, acc[i][j]);
+          }
         }
       }
     }
@@ -869,8 +915,11 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const InT* __restrict__
 
 // ----------------------------------------------------------- combine ---
 // out[t, n] = sum_j w[t, j] * y[t*k + j, n], fp32 in j order, one rounding.
-template <typename OutT>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
+__device__ __forceinline__ void load8y(const float* p, float (&v)[8]) { load8(p, v); }
+__device__ __forceinline__ void load8y(const uint16_t* p, float (&v)[8]) { load8(p, v); }
+
+template <typename YT, typename OutT>
+__global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
                                                       const float* __restrict__ w, int T, int H,
                                                       int k, OutT* __restrict__ out) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
@@ -880,13 +929,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   float acc[8] = {};
   for (int j = 0; j < k; ++j) {
     const float wj = w[(size_t)t * k + j];
-    const float* yr = y + ((size_t)t * k + j) * H + n;
-    const f32x4 a = *(const f32x4*)yr, b = *(const f32x4*)(yr + 4);
+    float v[8];
+    load8y(y + ((size_t)t * k + j) * H + n, v);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[q] += wj * a[q];
-      acc[4 + q] += wj * b[q];
-    }
+    for (int q = 0; q < 8; ++q) acc[q] += wj * v[q];
   }
   if constexpr (sizeof(OutT) == 2) {
     u32x4 o;
@@ -999,7 +1045,7 @@ FfnWorkspace ffn_workspace_layout(int T, int H, int I, int k, int dtype) {
     put(L.xq_off, L.xq_bytes, (size_t)T * H);
     put(L.xs_off, L.xs_bytes, (size_t)T * 4);
   }
-  put(L.y_off, L.y_bytes, S * H * 4);
+  put(L.y_off, L.y_bytes, S * H * (dtype == MOE_DTYPE_BF16 ? 2 : 4));
   L.total = o;
   return L;
 }
@@ -1007,7 +1053,7 @@ FfnWorkspace ffn_workspace_layout(int T, int H, int I, int k, int dtype) {
 // Resident-capacity grid of a persistent kernel on the current device,
 // rounded down to a multiple of 8 (one share per XCD). Cached per device.
 template <typename K>
-static int persistent_grid(K kernel, int slot) {
+static int persistent_grid(K kernel, int slot, int threads = 256) {
   static std::mutex mu;
   static int cache[64][8];
   int dev = 0;
@@ -1018,7 +1064,7 @@ static int persistent_grid(K kernel, int slot) {
     int cus = 0, occ = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, 256, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, 0) != hipSuccess ||
         occ < 1)
       occ = 1;
     c = cus * occ;
@@ -1038,22 +1084,25 @@ static unsigned stages(unsigned flags) {
   return s ? s : (MOE_FFN_STAGE_FC1 | MOE_FFN_STAGE_FC2 | MOE_FFN_STAGE_COMBINE);
 }
 
-static hipError_t launch_combine(const FfnProblem& p, const FfnWorkspace& L, bool bf16_out,
+static hipError_t launch_combine(const FfnProblem& p, const FfnWorkspace& L, int dtype,
                                  hipStream_t stream) {
-  const float* y = (const float*)((char*)p.workspace + L.y_off);
+  const void* y = (const char*)p.workspace + L.y_off;
   if (p.H % 8 == 0) {
     const long n = (long)p.T * (p.H / 8);
     const dim3 grid((unsigned)((n + 255) / 256));
-    if (bf16_out)
-      combine_kernel<uint16_t><<<grid, 256, 0, stream>>>(y, p.topk_weights, p.T, p.H, p.k,
-                                                         (uint16_t*)p.out);
+    if (dtype == MOE_DTYPE_BF16)
+      combine_kernel<uint16_t, uint16_t><<<grid, 256, 0, stream>>>(
+          (const uint16_t*)y, p.topk_weights, p.T, p.H, p.k, (uint16_t*)p.out);
+    else if (dtype == MOE_DTYPE_FP8)
+      combine_kernel<float, uint16_t><<<grid, 256, 0, stream>>>(
+          (const float*)y, p.topk_weights, p.T, p.H, p.k, (uint16_t*)p.out);
     else
-      combine_kernel<float><<<grid, 256, 0, stream>>>(y, p.topk_weights, p.T, p.H, p.k,
-                                                      (float*)p.out);
+      combine_kernel<float, float><<<grid, 256, 0, stream>>>((const float*)y, p.topk_weights, p.T,
+                                                             p.H, p.k, (float*)p.out);
   } else {
     const long n = (long)p.T * p.H;
     combine_f32_scalar_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(
-        y, p.topk_weights, p.T, p.H, p.k, (float*)p.out);
+        (const float*)y, p.topk_weights, p.T, p.H, p.k, (float*)p.out);
   }
   return hipGetLastError();
 }
@@ -1066,26 +1115,26 @@ hipError_t launch_ffn_bf16(const FfnProblem& p, hipStream_t stream) {
   void* h = (char*)p.workspace + L.h_off;
   float* y = (float*)((char*)p.workspace + L.y_off);
   hipError_t err;
-  const bool dense = p.block_m >= kDTok;  // prefill-sized blocks: grouped GEMM tiles
+  const bool dense = p.block_m >= 128;  // prefill-sized blocks: grouped GEMM tiles
   if (st & MOE_FFN_STAGE_FC1) {
     Fc1Args a{p.x, nullptr, p.w1, nullptr, p.sorted_ids, p.block_expert, p.num_padded,
               p.H, p.I, p.k, S, log2m, remap, h};
     if (dense)
-      dense_fc1_kernel<<<persistent_grid(dense_fc1_kernel, 4), 256, 0, stream>>>(a);
+      dense_fc1_kernel<<<persistent_grid(dense_fc1_kernel, 4, kDThreads), kDThreads, 0, stream>>>(a);
     else
       fc1_kernel<false><<<persistent_grid(fc1_kernel<false>, 0), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_FC2) {
     Fc2Args a{h, nullptr, p.w2, nullptr, p.sorted_ids, p.block_expert, p.num_padded,
-              p.H, p.I, S, log2m, remap, y};
+              p.H, p.I, S, log2m, remap, y, 1};
     if (dense)
-      dense_fc2_kernel<<<persistent_grid(dense_fc2_kernel, 5), 256, 0, stream>>>(a);
+      dense_fc2_kernel<<<persistent_grid(dense_fc2_kernel, 5, kDThreads), kDThreads, 0, stream>>>(a);
     else
       fc2_kernel<false><<<persistent_grid(fc2_kernel<false>, 1), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  if (st & MOE_FFN_STAGE_COMBINE) return launch_combine(p, L, true, stream);
+  if (st & MOE_FFN_STAGE_COMBINE) return launch_combine(p, L, MOE_DTYPE_BF16, stream);
   return hipSuccess;
 }
 
@@ -1115,11 +1164,11 @@ hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
     quant_rows_kernel<float><<<(S + 3) / 4, 256, 0, stream>>>(h, S, p.I, hq, hs);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     Fc2Args a{hq, hs, p.w2, p.w2_scale, p.sorted_ids, p.block_expert, p.num_padded,
-              p.H, p.I, S, log2m, remap, y};
+              p.H, p.I, S, log2m, remap, y, 0};
     fc2_kernel<true><<<persistent_grid(fc2_kernel<true>, 3), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  if (st & MOE_FFN_STAGE_COMBINE) return launch_combine(p, L, true, stream);
+  if (st & MOE_FFN_STAGE_COMBINE) return launch_combine(p, L, MOE_DTYPE_FP8, stream);
   return hipSuccess;
 }
 
@@ -1143,7 +1192,7 @@ hipError_t launch_ffn_f32(const FfnProblem& p, hipStream_t stream) {
                                              y);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  if (st & MOE_FFN_STAGE_COMBINE) return launch_combine(p, L, false, stream);
+  if (st & MOE_FFN_STAGE_COMBINE) return launch_combine(p, L, MOE_DTYPE_F32, stream);
   return hipSuccess;
 }
 

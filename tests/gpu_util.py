@@ -11,7 +11,6 @@ from synth import config_inputs, make_inputs  # noqa: F401
 
 TOL = {"f32": 1e-4, "bf16": 1e-2, "fp8": 5e-2}   # normwise max relative error of the output
 WEIGHT_ATOL = 1e-5                               # router weights, absolute
-BENCH_BLOCK_M = 64                               # the block size bench.py times
 
 
 def say(msg: str) -> None:
@@ -46,8 +45,15 @@ def oracle_forward(inp, tokens=None, renormalize=False):
     return ids, w, out
 
 
-def gpu_forward(inp, block_m=BENCH_BLOCK_M, renormalize=False, flags=0):
+def bench_block_m(inp) -> int:
+    """The block size bench.py times for this workload."""
+    return moe().default_block_m(inp.T, inp.E, inp.k)
+
+
+def gpu_forward(inp, block_m=None, renormalize=False, flags=0):
     m = moe()
+    if block_m is None:
+        block_m = bench_block_m(inp)
     ids, w = m.route_topk(inp.logits, inp.k, renormalize)
     sid, be, npad = m.align_block(ids, inp.E, block_m)
     if inp.dtype == "fp8":

@@ -125,11 +125,20 @@ def test_fp8_scale_pointers_validated():
     assert call_fp8(s2=P + 4) == ALIGN
 
 
+def test_default_block_m():
+    f = lib.moe_default_block_m
+    assert f(16, 64, 8) == 64          # decode: 2 slots per expert
+    assert f(64, 128, 8) == 64
+    assert f(4096, 128, 8) == 256      # prefill: 256 slots per expert
+    assert f(16, 1, 8) == 0            # k > E
+    assert f(2048, 128, 8) == 256 and f(2047, 128, 8) == 64
+
+
 def test_workspace_bytes():
     ws = lib.moe_ffn_workspace_bytes
     S, H, I = 16 * 8, 4096, 1536
     bf = ws(16, 64, H, I, 8, 64, 1)
-    assert bf >= S * I * 2 + S * H * 4 and bf % 256 == 0
+    assert bf >= S * I * 2 + S * H * 2 and bf % 256 == 0      # h, y bf16
     f8 = ws(16, 64, H, I, 8, 64, 2)
     assert f8 >= S * I * 4 + S * I + S * 4 + 16 * H + 16 * 4 + S * H * 4
     assert ws(16, 64, H, I, 8, 64, 7) == 0

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from synth import make_inputs
-from tests.gpu_util import (BENCH_BLOCK_M, TOL, cfg_inputs, check_align, check_routing, gpu_forward,
+from tests.gpu_util import (TOL, bench_block_m, cfg_inputs, check_align, check_routing, gpu_forward,
                             moe, oracle_forward, out_f64, say)
 
 pytestmark = pytest.mark.gpu
@@ -19,13 +19,14 @@ SAMPLE = {4: [0, 1, 17, 31, 42, 63], 5: [0, 1, 2, 511, 1000, 2047, 3000, 4095]}
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
 def test_config_parity(n):
     inp = cfg_inputs(n)
+    bm = bench_block_m(inp)
     say(f"ffn config {n} ({inp.dtype}) T={inp.T} E={inp.E} H={inp.H} I={inp.I} k={inp.k} "
-        f"block_m={BENCH_BLOCK_M}")
-    ids, w, al, out = gpu_forward(inp, BENCH_BLOCK_M)
+        f"block_m={bm}")
+    ids, w, al, out = gpu_forward(inp, bm)
     tokens = SAMPLE.get(n)
     ids_o, w_o, ref = oracle_forward(inp, tokens)
     check_routing(ids, w, ids_o, w_o)
-    check_align(al, ids_o, inp.E, BENCH_BLOCK_M, inp.S)
+    check_align(al, ids_o, inp.E, bm, inp.S)
     got = out_f64(out)
     if tokens is not None:
         got = got[tokens]
