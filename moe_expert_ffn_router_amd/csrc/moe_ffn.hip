@@ -346,6 +346,7 @@ struct Fc1Args {
   const int32_t* num_padded;
   int H, I, k, S, log2m, remap;
   void* h;             // bf16 [S, I] (bf16 path) or f32 [S, I] (fp8 path)
+  int* queue;          // dense kernels: kQueues work counters, zero at launch
 };
 
 // Store SiLU(g)*u for 4 consecutive h columns of one slot.
@@ -456,6 +457,7 @@ struct Fc2Args {
   int H, I, S, log2m, remap;
   void* y;             // per-slot FC2 output [S, H]: bf16 (bf16 path) or f32
   int y_bf16;
+  int* queue;          // dense kernels: kQueues work counters, zero at launch
 };
 
 // Store 4 consecutive FC2 outputs of one slot.
@@ -591,8 +593,10 @@ __global__ __launch_bounds__(256) void fc2_kernel(Fc2Args p) {
 // ------------------------------------------- dense tiles (big blocks) ---
 // For blocks of up to 256 tokens (prefill) the projection is a real grouped
 // GEMM: a 512-thread workgroup multiplies a 256-row weight tile by the block's
-// 256-token tile, both staged through LDS 64 k-elements (128 bytes) at a time,
-// double buffered (144 KB, one workgroup per CU). Its 8 waves each own 64 rows
+// 256-token tile, both staged through LDS 64 k-elements (128 bytes) at a time.
+// Weight tiles stream from HBM and get three LDS stages (two chunks in
+// flight while one is multiplied); token tiles come from the caches and get
+// two; together 160 KB, one workgroup per CU. Its 8 waves each own 64 rows
 // x 128 tokens (4 x 8 MFMA 16x16x32 tiles, 128 accumulators), so each staged
 // byte feeds 64..128 MFMAs per k-step. Units (block, 256-row tile) are ordered
 // expert by expert, row tile by row tile with the expert's blocks innermost,
@@ -604,9 +608,11 @@ constexpr int kDRows = 256;   // weight rows per unit
 constexpr int kDTok = 256;    // tokens per unit
 constexpr int kDThreads = 512;
 constexpr int kDChunk = 128;  // bytes of K per stage (64 bf16, two MFMA k-steps) = one LDS row
-constexpr int kDStages = 2;   // LDS double buffer
-constexpr int kDTile = kDRows * kDChunk;   // bytes of one staged operand tile (32 KB)
-constexpr int kDStage = 2 * kDTile;        // A tile + B tile
+constexpr int kDTile = kDRows * kDChunk;  // bytes of one staged operand tile (32 KB)
+constexpr int kDAStages = 3;              // weight-tile ring
+constexpr int kDBStages = 2;              // token-tile ring
+constexpr int kDLds = (kDAStages + kDBStages) * kDTile;
+constexpr int kDALoads = 4;  // direct-to-LDS loads per wave for one weight tile
 // LDS rows are 128 bytes (8 columns of 16 bytes) with no padding; column c of
 // row r sits at column c ^ (r & 7), conflict-free for the MFMA fragment
 // reads (16 consecutive rows, one column) on gfx950.
@@ -624,19 +630,21 @@ struct DenseStage {
   const uint8_t* arow[4];  // this lane's source weight rows (+ logical column)
   const uint8_t* brow[4];  // this lane's source token rows (+ logical column)
   int bgroups;             // this wave's token groups holding real tokens (0..4)
-  __device__ __forceinline__ void issue(uint8_t* __restrict__ stage, int c) const {
+  __device__ __forceinline__ void issue_a(uint8_t* __restrict__ tile, int c) const {
     const int w = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint8_t* da = stage + (32 * w + 8 * i) * kDChunk;
-      __builtin_amdgcn_global_load_lds((const void*)(arow[i] + (size_t)c * kDChunk), (lds_ptr_t)da,
-                                       16, 0, 0);
+    for (int i = 0; i < kDALoads; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(arow[i] + (size_t)c * kDChunk),
+                                       (lds_ptr_t)(tile + (32 * w + 8 * i) * kDChunk), 16, 0, 0);
+  }
+  __device__ __forceinline__ void issue_b(uint8_t* __restrict__ tile, int c) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
       if (i < bgroups)
         __builtin_amdgcn_global_load_lds((const void*)(brow[i] + (size_t)c * kDChunk),
-                                         (lds_ptr_t)(da + kDTile), 16, 0, 0);
-    }
+                                         (lds_ptr_t)(tile + (32 * w + 8 * i) * kDChunk), 16, 0, 0);
   }
-  __device__ __forceinline__ int loads() const { return 4 + bgroups; }
 };
 
 // Row of this lane in staging instruction i, and its logical 16-byte column.
@@ -653,49 +661,132 @@ __device__ __forceinline__ int dstage_bgroups(int m) {
   return max(0, min(4, (m - first + 7) >> 3));
 }
 
-// acc[i][j] += A rows (64*wr + 16i ..) . B tokens (128*wc + 16j ..) for the
-// two MFMA k-steps of one stage: per k-step all 12 fragments are read, then
-// 32 MFMAs run on them.
-__device__ __forceinline__ void dense_compute(const uint8_t* __restrict__ stage, int wr, int wc,
+// acc[i][j] += A rows (64*wr + 16i ..) . B tokens (128*wc + 16j ..), j < NJ,
+// for the two MFMA k-steps of one chunk: per k-step the fragments are read,
+// then the MFMAs run on them. Waves whose tokens end early use NJ < 8.
+template <int NJ>
+__device__ __forceinline__ void dense_compute(const uint8_t* __restrict__ ta,
+                                              const uint8_t* __restrict__ tb, int wr, int wc,
                                               f32x4 (&acc)[4][8]) {
   const int lane = threadIdx.x & 63;
   // fragment rows are 16-aligned bases + (lane & 15), so row & 7 == lane & 7
-  const uint8_t* pa = stage + (64 * wr + (lane & 15)) * kDChunk;
-  const uint8_t* pb = stage + kDTile + (128 * wc + (lane & 15)) * kDChunk;
+  const uint8_t* pa = ta + (64 * wr + (lane & 15)) * kDChunk;
+  const uint8_t* pb = tb + (128 * wc + (lane & 15)) * kDChunk;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int cs = (((s << 2) + (lane >> 4)) ^ (lane & 7)) << 4;
-    bf16x8 fa[4], fb[8];
+    bf16x8 fa[4], fb[NJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8*)(pa + i * 16 * kDChunk + cs);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) fb[j] = *(const bf16x8*)(pb + j * 16 * kDChunk + cs);
+    for (int j = 0; j < NJ; ++j) fb[j] = *(const bf16x8*)(pb + j * 16 * kDChunk + cs);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i][j] = mfma_bf16(fa[i], fb[j], acc[i][j]);
   }
 }
 
-// Wait until at most n direct-to-LDS loads of this wave are outstanding.
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0xF70); }
+// Wait until at most N vector-memory loads of this wave are outstanding
+// (s_waitcnt with expcnt and lgkmcnt left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0xF70 | N);
+}
 
 // The whole K loop of one unit; all 512 threads take part. While chunk c is
-// multiplied out of one stage, chunk c+1 streams into the other.
-__device__ __forceinline__ void dense_kloop(const DenseStage& st, int kbytes, bool active, int wr,
+// multiplied, the token tile of chunk c+1 and the weight tiles of chunks c+1
+// and c+2 are in flight. Loads retire in issue order, so waiting for all but
+// the newest weight tile's loads leaves chunk c+1 complete. nj = 16-token
+// groups of this wave holding tokens (0 = idle wave, which only stages).
+__device__ __forceinline__ void dense_kloop(const DenseStage& st, int kbytes, int nj, int wr,
                                             int wc, uint8_t* __restrict__ lds, f32x4 (&acc)[4][8]) {
-  const int nch = kbytes / kDChunk;
-  // stage addresses are computed from the LDS base so they stay in the LDS
+  const int nch = kbytes / kDChunk;  // at least 2 (K >= 128)
+  // tile addresses are computed from the LDS base so they stay in the LDS
   // address space
-  st.issue(lds, 0);
-  wait_vm0();
+  uint8_t* const ra = lds;
+  uint8_t* const rb = lds + kDAStages * kDTile;
+  st.issue_a(ra, 0);
+  st.issue_b(rb, 0);
+  st.issue_a(ra + kDTile, 1);
+  wait_vm<kDALoads>();
   __syncthreads();
+  int ia = 0;  // weight stage of chunk c
   for (int c = 0; c < nch; ++c) {
-    if (c + 1 < nch) st.issue(lds + ((c + 1) & 1) * kDStage, c + 1);
-    if (active) dense_compute(lds + (c & 1) * kDStage, wr, wc, acc);
-    wait_vm0();
+    const int ia2 = ia == 0 ? 2 : ia - 1;  // weight stage of chunk c+2
+    if (c + 1 < nch) st.issue_b(rb + ((c + 1) & 1) * kDTile, c + 1);
+    if (c + 2 < nch) st.issue_a(ra + ia2 * kDTile, c + 2);
+    const uint8_t* ta = ra + ia * kDTile;
+    const uint8_t* tb = rb + (c & 1) * kDTile;
+    if (nj > 4)
+      dense_compute<8>(ta, tb, wr, wc, acc);
+    else if (nj > 2)
+      dense_compute<4>(ta, tb, wr, wc, acc);
+    else if (nj > 0)
+      dense_compute<2>(ta, tb, wr, wc, acc);
+    if (c + 2 < nch)
+      wait_vm<kDALoads>();
+    else
+      wait_vm<0>();
     __syncthreads();
+    ia = ia == 2 ? 0 : ia + 1;
   }
+}
+
+// Unit scheduler of the dense kernels. The unit list is cut into 8 contiguous
+// shares, one per XCD; a workgroup takes the next unit of its own XCD's share
+// from an atomic counter and, when that share is drained, helps with the
+// others. Taking units in list order keeps the blocks that share a weight
+// tile running side by side on one XCD, so the tile is fetched from HBM once
+// and served to the partner from L2. Which workgroup computes a unit never
+// changes the result. With remap off, units are dealt round-robin instead.
+constexpr int kQueues = 8;
+
+__device__ __forceinline__ int hw_xcc_id() {
+  int v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & (kQueues - 1);
+}
+
+struct DenseSched {
+  int* cnt;  // kQueues counters, zero at launch
+  int units, per, q0, qi, next_static;
+  bool dyn;
+  __device__ DenseSched(int* c, int n, int remap)
+      : cnt(c), units(n), per((n + kQueues - 1) / kQueues), q0(hw_xcc_id()), qi(0),
+        next_static(blockIdx.x), dyn(remap != 0) {}
+  // Next unit of this workgroup, or -1. Uses the first 4 bytes of the (idle)
+  // staging LDS to broadcast the pick.
+  __device__ __forceinline__ int next(uint8_t* __restrict__ lds) {
+    if (!dyn) {
+      const int u = next_static;
+      next_static += gridDim.x;
+      return u < units ? u : -1;
+    }
+    if (threadIdx.x == 0) {
+      int u = -1;
+      for (; qi < kQueues; ++qi) {
+        const int q = (q0 + qi) & (kQueues - 1);
+        const int lo = q * per, n = min(units, lo + per) - lo;
+        if (n <= 0) continue;
+        const int t = atomicAdd(cnt + q, 1);
+        if (t < n) {
+          u = lo + t;
+          break;
+        }
+      }
+      *(volatile int*)lds = u;
+    }
+    __syncthreads();
+    const int u = *(volatile int*)lds;
+    __syncthreads();
+    return u;
+  }
+};
+
+__global__ void zero_counters_kernel(int* __restrict__ c, int n) {
+  if ((int)threadIdx.x < n) c[threadIdx.x] = 0;
 }
 
 // First block and length of the run of blocks with expert e containing bn
@@ -729,19 +820,12 @@ __device__ __forceinline__ void find_run(const int32_t* __restrict__ block_exper
   q = hi - lo;
 }
 
-// This workgroup's virtual index: consecutive virtual indices share an XCD.
-__device__ __forceinline__ int virtual_wg(int remap) {
-  const int wg = blockIdx.x, G = gridDim.x;
-  if (!remap || (G & 7) != 0) return wg;
-  return (wg & 7) * (G >> 3) + (wg >> 3);
-}
-
 // Map unit u of the (expert, row tile, block) order to (row tile r, block b).
 struct UnitMap {
   int nb, n_rt;
   int run_b0 = 0, run_q = 0, e = 0;
   long run_u0 = 0, run_u1 = 0;
-  __device__ __forceinline__ void locate(const int32_t* __restrict__ block_expert, long u, int& r,
+  __device__ __forceinline__ void locate(const int32_t* __restrict__ block_expert, int u, int& r,
                                          int& b) {
     if (u >= run_u1 || u < run_u0) {
       const int bn = (int)(u / n_rt);
@@ -757,16 +841,17 @@ struct UnitMap {
 };
 
 __global__ __launch_bounds__(kDThreads) void dense_fc1_kernel(Fc1Args p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kDStages * kDStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kDLds];
   const int M = 1 << p.log2m;
   const int nb = p.num_padded[0] >> p.log2m;
   const int n_rt = (2 * p.I) / kDRows;  // 128 gate + 128 up rows per unit
-  const long units = (long)nb * n_rt;
+  const int units = nb * n_rt;
   const int w = threadIdx.x >> 6, wr = w & 3, wc = w >> 2, lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const size_t rowb = (size_t)p.H * 2;
   UnitMap um{nb, n_rt};
-  for (long u = virtual_wg(p.remap); u < units; u += gridDim.x) {
+  DenseSched sched(p.queue, units, p.remap);
+  for (int u; (u = sched.next(lds)) >= 0;) {
     int r, b;
     um.locate(p.block_expert, u, r, b);
     const int e = um.e;
@@ -787,9 +872,9 @@ __global__ __launch_bounds__(kDThreads) void dense_fc1_kernel(Fc1Args p) {
         st.brow[i] = (const uint8_t*)p.x + (size_t)(slot / p.k) * rowb + col;
       }
       f32x4 acc[4][8] = {};
-      const bool active = 128 * wc < m;
-      dense_kloop(st, (int)rowb, active, wr, wc, lds, acc);
-      if (!active) continue;
+      const int nj = min(8, max(0, (m - 128 * wc + 15) >> 4));
+      dense_kloop(st, (int)rowb, nj, wr, wc, lds, acc);
+      if (nj == 0) continue;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int ti = 128 * wc + 16 * j + (lane & 15);
@@ -814,16 +899,17 @@ __global__ __launch_bounds__(kDThreads) void dense_fc1_kernel(Fc1Args p) {
 }
 
 __global__ __launch_bounds__(kDThreads) void dense_fc2_kernel(Fc2Args p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kDStages * kDStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kDLds];
   const int M = 1 << p.log2m;
   const int nb = p.num_padded[0] >> p.log2m;
   const int n_rt = (p.H + kDRows - 1) / kDRows;  // the last row tile may be partial
-  const long units = (long)nb * n_rt;
+  const int units = nb * n_rt;
   const int w = threadIdx.x >> 6, wr = w & 3, wc = w >> 2, lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const size_t rowb = (size_t)p.I * 2;
   UnitMap um{nb, n_rt};
-  for (long u = virtual_wg(p.remap); u < units; u += gridDim.x) {
+  DenseSched sched(p.queue, units, p.remap);
+  for (int u; (u = sched.next(lds)) >= 0;) {
     int r, b;
     um.locate(p.block_expert, u, r, b);
     const int e = um.e;
@@ -843,9 +929,9 @@ __global__ __launch_bounds__(kDThreads) void dense_fc2_kernel(Fc2Args p) {
         st.brow[i] = (const uint8_t*)p.h + (size_t)slot * rowb + col;
       }
       f32x4 acc[4][8] = {};
-      const bool active = 128 * wc < m;
-      dense_kloop(st, (int)rowb, active, wr, wc, lds, acc);
-      if (!active) continue;
+      const int nj = min(8, max(0, (m - 128 * wc + 15) >> 4));
+      dense_kloop(st, (int)rowb, nj, wr, wc, lds, acc);
+      if (nj == 0) continue;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int ti = 128 * wc + 16 * j + (lane & 15);
@@ -1046,6 +1132,7 @@ FfnWorkspace ffn_workspace_layout(int T, int H, int I, int k, int dtype) {
     put(L.xs_off, L.xs_bytes, (size_t)T * 4);
   }
   put(L.y_off, L.y_bytes, S * H * (dtype == MOE_DTYPE_BF16 ? 2 : 4));
+  put(L.q_off, L.q_bytes, S ? 2 * kQueues * sizeof(int) : 0);
   L.total = o;
   return L;
 }
@@ -1114,11 +1201,16 @@ hipError_t launch_ffn_bf16(const FfnProblem& p, hipStream_t stream) {
   const int S = p.T * p.k, log2m = ilog2(p.block_m);
   void* h = (char*)p.workspace + L.h_off;
   float* y = (float*)((char*)p.workspace + L.y_off);
+  int* queue = (int*)((char*)p.workspace + L.q_off);  // FC1: [0, 8), FC2: [8, 16)
   hipError_t err;
   const bool dense = p.block_m >= 128;  // prefill-sized blocks: grouped GEMM tiles
+  if (dense && (st & (MOE_FFN_STAGE_FC1 | MOE_FFN_STAGE_FC2))) {
+    zero_counters_kernel<<<1, 64, 0, stream>>>(queue, 2 * kQueues);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   if (st & MOE_FFN_STAGE_FC1) {
     Fc1Args a{p.x, nullptr, p.w1, nullptr, p.sorted_ids, p.block_expert, p.num_padded,
-              p.H, p.I, p.k, S, log2m, remap, h};
+              p.H, p.I, p.k, S, log2m, remap, h, queue};
     if (dense)
       dense_fc1_kernel<<<persistent_grid(dense_fc1_kernel, 4, kDThreads), kDThreads, 0, stream>>>(a);
     else
@@ -1127,7 +1219,7 @@ hipError_t launch_ffn_bf16(const FfnProblem& p, hipStream_t stream) {
   }
   if (st & MOE_FFN_STAGE_FC2) {
     Fc2Args a{h, nullptr, p.w2, nullptr, p.sorted_ids, p.block_expert, p.num_padded,
-              p.H, p.I, S, log2m, remap, y, 1};
+              p.H, p.I, S, log2m, remap, y, 1, queue + kQueues};
     if (dense)
       dense_fc2_kernel<<<persistent_grid(dense_fc2_kernel, 5, kDThreads), kDThreads, 0, stream>>>(a);
     else
@@ -1156,7 +1248,7 @@ hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
                                                                    p.H, xq, xs);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     Fc1Args a{xq, xs, p.w1, p.w1_scale, p.sorted_ids, p.block_expert, p.num_padded,
-              p.H, p.I, p.k, S, log2m, remap, h};
+              p.H, p.I, p.k, S, log2m, remap, h, nullptr};
     fc1_kernel<true><<<persistent_grid(fc1_kernel<true>, 2), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
@@ -1164,7 +1256,7 @@ hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
     quant_rows_kernel<float><<<(S + 3) / 4, 256, 0, stream>>>(h, S, p.I, hq, hs);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     Fc2Args a{hq, hs, p.w2, p.w2_scale, p.sorted_ids, p.block_expert, p.num_padded,
-              p.H, p.I, S, log2m, remap, y, 0};
+              p.H, p.I, S, log2m, remap, y, 0, nullptr};
     fc2_kernel<true><<<persistent_grid(fc2_kernel<true>, 3), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }

@@ -22,7 +22,8 @@ struct FfnWorkspace {
   size_t hs_off, hs_bytes;  // fp8: per-slot scale of h [S]
   size_t xq_off, xq_bytes;  // fp8: e4m3 codes of x [T, H]
   size_t xs_off, xs_bytes;  // fp8: per-token scale of x [T]
-  size_t y_off, y_bytes;    // per-slot FC2 output, f32 [S, H]
+  size_t y_off, y_bytes;    // per-slot FC2 output [S, H]: bf16 (bf16), f32 (fp8, f32)
+  size_t q_off, q_bytes;    // work counters of the dense kernels, int32 [16]
   size_t total;
 };
 FfnWorkspace ffn_workspace_layout(int T, int H, int I, int k, int dtype);
