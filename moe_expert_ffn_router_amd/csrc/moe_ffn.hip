@@ -695,6 +695,19 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0xF70 | N);
 }
 
+// Workgroup barrier for the staging ring: waits for this wave's LDS reads
+// (lgkmcnt 0), so the stage it read may be refilled, then meets the other
+// waves, each of which has already waited for its own loads of the next
+// stage. __syncthreads would also drain the loads still in flight for later
+// stages (its fences wait for vmcnt 0, which tracks direct-to-LDS loads);
+// compiler-only fences keep LDS accesses from being moved across instead.
+__device__ __forceinline__ void ring_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt: no wait
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // The whole K loop of one unit; all 512 threads take part. While chunk c is
 // multiplied, the token tile of chunk c+1 and the weight tiles of chunks c+1
 // and c+2 are in flight. Loads retire in issue order, so waiting for all but
@@ -711,7 +724,7 @@ __device__ __forceinline__ void dense_kloop(const DenseStage& st, int kbytes, in
   st.issue_b(rb, 0);
   st.issue_a(ra + kDTile, 1);
   wait_vm<kDALoads>();
-  __syncthreads();
+  ring_barrier();
   int ia = 0;  // weight stage of chunk c
   for (int c = 0; c < nch; ++c) {
     const int ia2 = ia == 0 ? 2 : ia - 1;  // weight stage of chunk c+2
@@ -729,7 +742,7 @@ __device__ __forceinline__ void dense_kloop(const DenseStage& st, int kbytes, in
       wait_vm<kDALoads>();
     else
       wait_vm<0>();
-    __syncthreads();
+    ring_barrier();
     ia = ia == 2 ? 0 : ia + 1;
   }
 }
@@ -776,10 +789,10 @@ struct DenseSched {
           break;
         }
       }
-      *(volatile int*)lds = u;
+      *(volatile __attribute__((address_space(3))) int*)lds = u;
     }
     __syncthreads();
-    const int u = *(volatile int*)lds;
+    const int u = *(volatile __attribute__((address_space(3))) int*)lds;
     __syncthreads();
     return u;
   }
