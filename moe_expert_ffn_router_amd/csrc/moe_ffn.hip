@@ -680,6 +680,9 @@ __device__ __forceinline__ void dense_compute(const uint8_t* __restrict__ ta,
     for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8*)(pa + i * 16 * kDChunk + cs);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) fb[j] = *(const bf16x8*)(pb + j * 16 * kDChunk + cs);
+    // all reads of the k-step are issued before its first MFMA, so their
+    // latencies overlap instead of one read per 4 MFMAs
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
