@@ -371,27 +371,30 @@ __device__ __forceinline__ void store_h(const Fc1Args& p, int slot, int col, con
 // matching up rows [I+8r, I+8r+8). After the diagonal sums a lane holds g and
 // u of the same (column, token).
 template <bool FP8>
-__device__ __forceinline__ void fc1_cold(const Fc1Args& p, int e, int r, int b, int M, int m) {
+__device__ __forceinline__ void fc1_cold(const Fc1Args& p, int e, int r, int slot) {
   const int lane = threadIdx.x & 63;
   const size_t rowb = (size_t)p.H * (FP8 ? 1 : 2);
   const int off = half_split_off();
   const uint8_t* w = (const uint8_t*)p.w1 + (size_t)e * 2 * p.I * rowb;
   const uint8_t* ap = w + (size_t)(r * 8 + (lane & 7)) * rowb + off;
   const uint8_t* aq = w + (size_t)(p.I + r * 8 + (lane & 7)) * rowb + off;
-  const int ti = lane & 7;
-  const int slot = ti < m ? p.sorted_ids[(size_t)b * M + ti] : p.S;
   const bool ok = slot < p.S;
   const uint8_t* bp = (const uint8_t*)p.x + (size_t)(ok ? slot / p.k : 0) * rowb + off;
+  const bool holder = (lane & 8) == 0 && lane < 32;  // lanes 0..7, 16..23
+  const int col = r * 8 + 4 * (lane >> 4);
+  // epilogue scales are fetched before the K loop so their latency is hidden
+  float xs = 1.f;
+  f32x4 sg = {1.f, 1.f, 1.f, 1.f}, su = sg;
+  if (FP8 && holder && ok) {
+    xs = p.xs[slot / p.k];
+    sg = *(const f32x4*)(p.w1s + (size_t)e * 2 * p.I + col);
+    su = *(const f32x4*)(p.w1s + (size_t)e * 2 * p.I + p.I + col);
+  }
   f32x4 accp = {}, accq = {};
   cold_kloop<FP8>(ap, aq, bp, ok, (int)rowb, accp, accq);
   f32x4 g = diag_sum(accp), u = diag_sum(accq);
-  const bool holder = (lane & 8) == 0 && lane < 32;  // lanes 0..7, 16..23
-  const int col = r * 8 + 4 * (lane >> 4);
   if (holder && ok) {
     if (FP8) {
-      const float xs = p.xs[slot / p.k];
-      const f32x4 sg = *(const f32x4*)(p.w1s + (size_t)e * 2 * p.I + col);
-      const f32x4 su = *(const f32x4*)(p.w1s + (size_t)e * 2 * p.I + p.I + col);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         g[i] *= sg[i] * xs;
@@ -473,27 +476,30 @@ __device__ __forceinline__ void store_y(const Fc2Args& p, int slot, int row, con
 
 // Cold FC2 tile r: P = output rows [16r, 16r+8), Q = [16r+8, 16r+16).
 template <bool FP8>
-__device__ __forceinline__ void fc2_cold(const Fc2Args& p, int e, int r, int b, int M, int m) {
+__device__ __forceinline__ void fc2_cold(const Fc2Args& p, int e, int r, int slot) {
   const int lane = threadIdx.x & 63;
   const size_t rowb = (size_t)p.I * (FP8 ? 1 : 2);
   const int off = half_split_off();
   const uint8_t* w = (const uint8_t*)p.w2 + (size_t)e * p.H * rowb;
   const uint8_t* ap = w + (size_t)(r * 16 + (lane & 7)) * rowb + off;
   const uint8_t* aq = w + (size_t)(r * 16 + 8 + (lane & 7)) * rowb + off;
-  const int ti = lane & 7;
-  const int slot = ti < m ? p.sorted_ids[(size_t)b * M + ti] : p.S;
   const bool ok = slot < p.S;
   const uint8_t* bp = (const uint8_t*)p.h + (size_t)(ok ? slot : 0) * rowb + off;
+  const bool holder = (lane & 8) == 0 && lane < 32;
+  const int row = r * 16 + 4 * (lane >> 4);
+  // epilogue scales are fetched before the K loop so their latency is hidden
+  float hs = 1.f;
+  f32x4 sp = {1.f, 1.f, 1.f, 1.f}, sq = sp;
+  if (FP8 && holder && ok) {
+    hs = p.hs[slot];
+    sp = *(const f32x4*)(p.w2s + (size_t)e * p.H + row);
+    sq = *(const f32x4*)(p.w2s + (size_t)e * p.H + row + 8);
+  }
   f32x4 accp = {}, accq = {};
   cold_kloop<FP8>(ap, aq, bp, ok, (int)rowb, accp, accq);
   f32x4 vp = diag_sum(accp), vq = diag_sum(accq);
-  const bool holder = (lane & 8) == 0 && lane < 32;
-  const int row = r * 16 + 4 * (lane >> 4);
   if (holder && ok) {
     if (FP8) {
-      const float hs = p.hs[slot];
-      const f32x4 sp = *(const f32x4*)(p.w2s + (size_t)e * p.H + row);
-      const f32x4 sq = *(const f32x4*)(p.w2s + (size_t)e * p.H + row + 8);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         vp[i] *= sp[i] * hs;
@@ -542,7 +548,14 @@ __device__ __forceinline__ void fc2_hot_pass(const Fc2Args& p, int e, int r, int
 
 // ------------------------------------------------- persistent kernels ---
 
-template <bool FP8, typename Args, void (*Cold_)(const Args&, int, int, int, int, int),
+// Work list: (block, quad of 4 consecutive tiles), one quad per workgroup
+// step, wave w taking tile 4q + w. With HOT, a block of up to 8 tokens runs
+// one cold pass and a bigger block the LDS-staged passes. Without HOT every
+// block runs cold passes of 8 tokens: the host picks that launch when blocks
+// of more than 8 tokens are unlikely (T <= 16 tokens), where it needs far
+// fewer registers, so more waves stream weights at once; it stays correct for
+// any block, reading the weights once per 8 tokens.
+template <bool FP8, bool HOT, typename Args, void (*Cold_)(const Args&, int, int, int),
           void (*H1)(const Args&, int, int, int, int, int, int, uint8_t*),
           void (*H2)(const Args&, int, int, int, int, int, int, uint8_t*),
           void (*H3)(const Args&, int, int, int, int, int, int, uint8_t*),
@@ -553,7 +566,9 @@ __device__ __forceinline__ void run_quads(const Args& p, int n_rt, uint8_t* lds)
   const int qpb = n_rt >> 2;  // quads per block (n_rt is a multiple of 4)
   const Share sh = wg_share((long)nb * qpb, p.remap);
   const int w = threadIdx.x >> 6;
+  const int ti = threadIdx.x & 7;  // cold tiles: lane l serves token l & 7 of a pass
   int cur_b = -1, e = 0, m = 0;
+  int cslot = 0;  // this lane's slot in the block's first cold pass (S: none)
   for (long qd = sh.q0; qd < sh.q1; ++qd) {  // uniform across the workgroup
     const int b = (int)(qd / qpb);
     const int r = (int)(qd % qpb) * 4 + w;
@@ -561,10 +576,9 @@ __device__ __forceinline__ void run_quads(const Args& p, int n_rt, uint8_t* lds)
       cur_b = b;
       e = p.block_expert[b];
       m = block_valid(p.sorted_ids, b, M, p.S);
+      cslot = ti < m ? p.sorted_ids[(size_t)b * M + ti] : p.S;
     }
-    if (m <= kColdMax) {
-      Cold_(p, e, r, b, M, m);
-    } else {
+    if (HOT && m > kColdMax) {
       for (int t0 = 0; t0 < m; t0 += kHotTok) {
         const int mt = min(4, (m - t0 + 15) >> 4);
         if (mt == 1) H1(p, e, r, b, M, m, t0, lds);
@@ -572,21 +586,27 @@ __device__ __forceinline__ void run_quads(const Args& p, int n_rt, uint8_t* lds)
         else if (mt == 3) H3(p, e, r, b, M, m, t0, lds);
         else H4(p, e, r, b, M, m, t0, lds);
       }
+    } else {
+      for (int t0 = 0; t0 < m; t0 += kColdMax) {
+        const int slot =
+            t0 == 0 ? cslot : (t0 + ti < m ? p.sorted_ids[(size_t)b * M + t0 + ti] : p.S);
+        Cold_(p, e, r, slot);
+      }
     }
   }
 }
 
-template <bool FP8>
+template <bool FP8, bool HOT>
 __global__ __launch_bounds__(256) void fc1_kernel(Fc1Args p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kHotTok * kLdsRow];
-  run_quads<FP8, Fc1Args, fc1_cold<FP8>, fc1_hot_pass<FP8, 1>, fc1_hot_pass<FP8, 2>,
+  __shared__ __attribute__((aligned(16))) uint8_t lds[HOT ? 2 * kHotTok * kLdsRow : 16];
+  run_quads<FP8, HOT, Fc1Args, fc1_cold<FP8>, fc1_hot_pass<FP8, 1>, fc1_hot_pass<FP8, 2>,
             fc1_hot_pass<FP8, 3>, fc1_hot_pass<FP8, 4>>(p, p.I >> 3, lds);
 }
 
-template <bool FP8>
+template <bool FP8, bool HOT>
 __global__ __launch_bounds__(256) void fc2_kernel(Fc2Args p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kHotTok * kLdsRow];
-  run_quads<FP8, Fc2Args, fc2_cold<FP8>, fc2_hot_pass<FP8, 1>, fc2_hot_pass<FP8, 2>,
+  __shared__ __attribute__((aligned(16))) uint8_t lds[HOT ? 2 * kHotTok * kLdsRow : 16];
+  run_quads<FP8, HOT, Fc2Args, fc2_cold<FP8>, fc2_hot_pass<FP8, 1>, fc2_hot_pass<FP8, 2>,
             fc2_hot_pass<FP8, 3>, fc2_hot_pass<FP8, 4>>(p, p.H >> 4, lds);
 }
 
@@ -1158,7 +1178,7 @@ FfnWorkspace ffn_workspace_layout(int T, int H, int I, int k, int dtype) {
 template <typename K>
 static int persistent_grid(K kernel, int slot, int threads = 256) {
   static std::mutex mu;
-  static int cache[64][8];
+  static int cache[64][16];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   std::lock_guard<std::mutex> lock(mu);
@@ -1220,6 +1240,7 @@ hipError_t launch_ffn_bf16(const FfnProblem& p, hipStream_t stream) {
   int* queue = (int*)((char*)p.workspace + L.q_off);  // FC1: [0, 8), FC2: [8, 16)
   hipError_t err;
   const bool dense = p.block_m >= 128;  // prefill-sized blocks: grouped GEMM tiles
+  const bool hot = p.T > 2 * kColdMax;  // see run_quads
   if (dense && (st & (MOE_FFN_STAGE_FC1 | MOE_FFN_STAGE_FC2))) {
     zero_counters_kernel<<<1, 64, 0, stream>>>(queue, 2 * kQueues);
     if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -1229,8 +1250,10 @@ hipError_t launch_ffn_bf16(const FfnProblem& p, hipStream_t stream) {
               p.H, p.I, p.k, S, log2m, remap, h, queue};
     if (dense)
       dense_fc1_kernel<<<persistent_grid(dense_fc1_kernel, 4, kDThreads), kDThreads, 0, stream>>>(a);
+    else if (hot)
+      fc1_kernel<false, true><<<persistent_grid(fc1_kernel<false, true>, 0), 256, 0, stream>>>(a);
     else
-      fc1_kernel<false><<<persistent_grid(fc1_kernel<false>, 0), 256, 0, stream>>>(a);
+      fc1_kernel<false, false><<<persistent_grid(fc1_kernel<false, false>, 6), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_FC2) {
@@ -1238,8 +1261,10 @@ hipError_t launch_ffn_bf16(const FfnProblem& p, hipStream_t stream) {
               p.H, p.I, S, log2m, remap, y, 1, queue + kQueues};
     if (dense)
       dense_fc2_kernel<<<persistent_grid(dense_fc2_kernel, 5, kDThreads), kDThreads, 0, stream>>>(a);
+    else if (hot)
+      fc2_kernel<false, true><<<persistent_grid(fc2_kernel<false, true>, 1), 256, 0, stream>>>(a);
     else
-      fc2_kernel<false><<<persistent_grid(fc2_kernel<false>, 1), 256, 0, stream>>>(a);
+      fc2_kernel<false, false><<<persistent_grid(fc2_kernel<false, false>, 7), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_COMBINE) return launch_combine(p, L, MOE_DTYPE_BF16, stream);
@@ -1258,6 +1283,7 @@ hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
   uint8_t* xq = (uint8_t*)(ws + L.xq_off);
   float* xs = (float*)(ws + L.xs_off);
   float* y = (float*)(ws + L.y_off);
+  const bool hot = p.T > 2 * kColdMax;  // see run_quads
   hipError_t err;
   if (st & MOE_FFN_STAGE_FC1) {
     quant_rows_kernel<uint16_t><<<(p.T + 3) / 4, 256, 0, stream>>>((const uint16_t*)p.x, p.T,
@@ -1265,7 +1291,10 @@ hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
     Fc1Args a{xq, xs, p.w1, p.w1_scale, p.sorted_ids, p.block_expert, p.num_padded,
               p.H, p.I, p.k, S, log2m, remap, h, nullptr};
-    fc1_kernel<true><<<persistent_grid(fc1_kernel<true>, 2), 256, 0, stream>>>(a);
+    if (hot)
+      fc1_kernel<true, true><<<persistent_grid(fc1_kernel<true, true>, 2), 256, 0, stream>>>(a);
+    else
+      fc1_kernel<true, false><<<persistent_grid(fc1_kernel<true, false>, 8), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_FC2) {
@@ -1273,7 +1302,10 @@ hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
     Fc2Args a{hq, hs, p.w2, p.w2_scale, p.sorted_ids, p.block_expert, p.num_padded,
               p.H, p.I, S, log2m, remap, y, 0, nullptr};
-    fc2_kernel<true><<<persistent_grid(fc2_kernel<true>, 3), 256, 0, stream>>>(a);
+    if (hot)
+      fc2_kernel<true, true><<<persistent_grid(fc2_kernel<true, true>, 3), 256, 0, stream>>>(a);
+    else
+      fc2_kernel<true, false><<<persistent_grid(fc2_kernel<true, false>, 9), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_COMBINE) return launch_combine(p, L, MOE_DTYPE_FP8, stream);

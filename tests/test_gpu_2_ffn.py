@@ -41,6 +41,10 @@ CASES = [  # T, E, H, I, k, routing
     (5, 4, 128, 128, 4, "normal"),
     (200, 8, 512, 256, 2, "zipf"),
     (1, 1, 256, 128, 1, "normal"),
+    # at most 16 tokens: the launch without LDS-staged passes, here with blocks
+    # of 9..16 tokens that it serves in two 8-token passes
+    (16, 2, 256, 128, 2, "normal"),
+    (12, 3, 384, 256, 2, "zipf"),
 ]
 
 
