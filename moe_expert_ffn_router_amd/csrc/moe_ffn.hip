@@ -58,6 +58,39 @@ __device__ __forceinline__ Share wg_share(long total, int remap) {
   return {total * wg / G, total * (wg + 1) / G};
 }
 
+// Dynamic scheduler of streaming launches that mix hot and cold blocks (their
+// quads differ in cost, so equal static shares would leave workgroups idle
+// while others still hold slow quads). Workgroup g starts with unit v(g), its
+// XCD-remapped index; every later unit comes from one global counter (zero at
+// launch). The next pick is requested as soon as a unit starts, so the
+// atomic's latency hides under the unit's streaming; it is published to the
+// workgroup through one of two LDS words, alternating, with one barrier.
+// Which workgroup computes a unit never changes the result.
+struct QuadQueue {
+  int* cnt;
+  int total, nxt = 0, par = 0;
+  __device__ QuadQueue(int* c, int n, int remap) : cnt(c), total(n) {}
+  __device__ __forceinline__ int first(int remap) {
+    int wg = blockIdx.x;
+    const int G = gridDim.x;
+    if (remap && (G & 7) == 0) wg = (wg & 7) * (G >> 3) + (wg >> 3);
+    prefetch(wg);
+    return wg < total ? wg : -1;
+  }
+  __device__ __forceinline__ void prefetch(int cur) {
+    if (threadIdx.x == 0 && cur < total) nxt = (int)gridDim.x + atomicAdd(cnt, 1);
+  }
+  // All threads call it after finishing a unit.
+  __device__ __forceinline__ int next(volatile __attribute__((address_space(3))) int* slots) {
+    if (threadIdx.x == 0) slots[par] = nxt;
+    __syncthreads();
+    const int u = slots[par];
+    par ^= 1;
+    prefetch(u);
+    return u < total ? u : -1;
+  }
+};
+
 // Number of real (non-sentinel) entries of block b; they form a prefix.
 __device__ __forceinline__ int block_valid(const int32_t* __restrict__ sorted_ids, int b, int M,
                                            int S) {
@@ -346,7 +379,7 @@ struct Fc1Args {
   const int32_t* num_padded;
   int H, I, k, S, log2m, remap;
   void* h;             // bf16 [S, I] (bf16 path) or f32 [S, I] (fp8 path)
-  int* queue;          // dense kernels: kQueues work counters, zero at launch
+  int* queue;          // work counters, zero at launch (dense and hot launches)
 };
 
 // Store SiLU(g)*u for 4 consecutive h columns of one slot.
@@ -460,7 +493,7 @@ struct Fc2Args {
   int H, I, S, log2m, remap;
   void* y;             // per-slot FC2 output [S, H]: bf16 (bf16 path) or f32
   int y_bf16;
-  int* queue;          // dense kernels: kQueues work counters, zero at launch
+  int* queue;          // work counters, zero at launch (dense and hot launches)
 };
 
 // Store 4 consecutive FC2 outputs of one slot.
@@ -560,18 +593,17 @@ template <bool FP8, bool HOT, typename Args, void (*Cold_)(const Args&, int, int
           void (*H2)(const Args&, int, int, int, int, int, int, uint8_t*),
           void (*H3)(const Args&, int, int, int, int, int, int, uint8_t*),
           void (*H4)(const Args&, int, int, int, int, int, int, uint8_t*)>
-__device__ __forceinline__ void run_quads(const Args& p, int n_rt, uint8_t* lds) {
-  const int M = 1 << p.log2m;
-  const int nb = p.num_padded[0] >> p.log2m;
-  const int qpb = n_rt >> 2;  // quads per block (n_rt is a multiple of 4)
-  const Share sh = wg_share((long)nb * qpb, p.remap);
-  const int w = threadIdx.x >> 6;
-  const int ti = threadIdx.x & 7;  // cold tiles: lane l serves token l & 7 of a pass
+struct QuadRunner {
+  const Args& p;
+  int M, w, ti;
   int cur_b = -1, e = 0, m = 0;
   int cslot = 0;  // this lane's slot in the block's first cold pass (S: none)
-  for (long qd = sh.q0; qd < sh.q1; ++qd) {  // uniform across the workgroup
-    const int b = (int)(qd / qpb);
-    const int r = (int)(qd % qpb) * 4 + w;
+  uint8_t* lds;
+  __device__ QuadRunner(const Args& a, uint8_t* l)
+      : p(a), M(1 << a.log2m), w(threadIdx.x >> 6), ti(threadIdx.x & 7), lds(l) {}
+  // quad q of block b: wave w takes tile 4q + w
+  __device__ __forceinline__ void run(int b, int q) {
+    const int r = q * 4 + w;
     if (b != cur_b) {
       cur_b = b;
       e = p.block_expert[b];
@@ -594,19 +626,50 @@ __device__ __forceinline__ void run_quads(const Args& p, int n_rt, uint8_t* lds)
       }
     }
   }
+};
+
+// Work list: (block, quad of 4 consecutive tiles), wave w of a workgroup
+// taking tile 4q + w. With HOT, a block of up to 8 tokens runs one cold pass
+// and a bigger block the LDS-staged passes. Without HOT every block runs cold
+// passes of 8 tokens: the host picks that launch when blocks of more than 8
+// tokens are unlikely (T <= 16 tokens), where it needs far fewer registers,
+// so more waves stream weights at once; it stays correct for any block,
+// reading the weights once per 8 tokens. With DYN, quads are handed out by a
+// QuadQueue, else each workgroup takes one contiguous equal share of the list.
+// Measured on skewed decode (mixed hot and cold blocks): FC2, whose hot quads
+// cost about twice a cold one, gains ~10% from DYN; FC1 (longer rows, hot
+// quads ~1.3x a cold one) loses ~5% with it, so only FC2 uses it.
+template <bool FP8, bool HOT, bool DYN, typename Args, void (*Cold_)(const Args&, int, int, int),
+          void (*H1)(const Args&, int, int, int, int, int, int, uint8_t*),
+          void (*H2)(const Args&, int, int, int, int, int, int, uint8_t*),
+          void (*H3)(const Args&, int, int, int, int, int, int, uint8_t*),
+          void (*H4)(const Args&, int, int, int, int, int, int, uint8_t*)>
+__device__ __forceinline__ void run_quads(const Args& p, int n_rt, uint8_t* lds) {
+  const int M = 1 << p.log2m;
+  const int nb = p.num_padded[0] >> p.log2m;
+  const int qpb = n_rt >> 2;  // quads per block (n_rt is a multiple of 4)
+  QuadRunner<FP8, HOT, Args, Cold_, H1, H2, H3, H4> qr(p, lds);
+  if constexpr (!DYN) {
+    const Share sh = wg_share((long)nb * qpb, p.remap);
+    for (long qd = sh.q0; qd < sh.q1; ++qd) qr.run((int)(qd / qpb), (int)(qd % qpb));
+  } else {
+    QuadQueue qq(p.queue, nb * qpb, p.remap);
+    auto* slots = (volatile __attribute__((address_space(3))) int*)(lds + 2 * kHotTok * kLdsRow);
+    for (int u = qq.first(p.remap); u >= 0; u = qq.next(slots)) qr.run(u / qpb, u % qpb);
+  }
 }
 
 template <bool FP8, bool HOT>
 __global__ __launch_bounds__(256) void fc1_kernel(Fc1Args p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[HOT ? 2 * kHotTok * kLdsRow : 16];
-  run_quads<FP8, HOT, Fc1Args, fc1_cold<FP8>, fc1_hot_pass<FP8, 1>, fc1_hot_pass<FP8, 2>,
+  __shared__ __attribute__((aligned(16))) uint8_t lds[HOT ? 2 * kHotTok * kLdsRow + 16 : 16];
+  run_quads<FP8, HOT, false, Fc1Args, fc1_cold<FP8>, fc1_hot_pass<FP8, 1>, fc1_hot_pass<FP8, 2>,
             fc1_hot_pass<FP8, 3>, fc1_hot_pass<FP8, 4>>(p, p.I >> 3, lds);
 }
 
 template <bool FP8, bool HOT>
 __global__ __launch_bounds__(256) void fc2_kernel(Fc2Args p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[HOT ? 2 * kHotTok * kLdsRow : 16];
-  run_quads<FP8, HOT, Fc2Args, fc2_cold<FP8>, fc2_hot_pass<FP8, 1>, fc2_hot_pass<FP8, 2>,
+  __shared__ __attribute__((aligned(16))) uint8_t lds[HOT ? 2 * kHotTok * kLdsRow + 16 : 16];
+  run_quads<FP8, HOT, HOT, Fc2Args, fc2_cold<FP8>, fc2_hot_pass<FP8, 1>, fc2_hot_pass<FP8, 2>,
             fc2_hot_pass<FP8, 3>, fc2_hot_pass<FP8, 4>>(p, p.H >> 4, lds);
 }
 
@@ -1241,7 +1304,7 @@ hipError_t launch_ffn_bf16(const FfnProblem& p, hipStream_t stream) {
   hipError_t err;
   const bool dense = p.block_m >= 128;  // prefill-sized blocks: grouped GEMM tiles
   const bool hot = p.T > 2 * kColdMax;  // see run_quads
-  if (dense && (st & (MOE_FFN_STAGE_FC1 | MOE_FFN_STAGE_FC2))) {
+  if ((dense || hot) && (st & (MOE_FFN_STAGE_FC1 | MOE_FFN_STAGE_FC2))) {
     zero_counters_kernel<<<1, 64, 0, stream>>>(queue, 2 * kQueues);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
@@ -1283,14 +1346,19 @@ hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
   uint8_t* xq = (uint8_t*)(ws + L.xq_off);
   float* xs = (float*)(ws + L.xs_off);
   float* y = (float*)(ws + L.y_off);
+  int* queue = (int*)(ws + L.q_off);    // FC1: [0, 8), FC2: [8, 16)
   const bool hot = p.T > 2 * kColdMax;  // see run_quads
   hipError_t err;
+  if (hot && (st & (MOE_FFN_STAGE_FC1 | MOE_FFN_STAGE_FC2))) {
+    zero_counters_kernel<<<1, 64, 0, stream>>>(queue, 2 * kQueues);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   if (st & MOE_FFN_STAGE_FC1) {
     quant_rows_kernel<uint16_t><<<(p.T + 3) / 4, 256, 0, stream>>>((const uint16_t*)p.x, p.T,
                                                                    p.H, xq, xs);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     Fc1Args a{xq, xs, p.w1, p.w1_scale, p.sorted_ids, p.block_expert, p.num_padded,
-              p.H, p.I, p.k, S, log2m, remap, h, nullptr};
+              p.H, p.I, p.k, S, log2m, remap, h, queue};
     if (hot)
       fc1_kernel<true, true><<<persistent_grid(fc1_kernel<true, true>, 2), 256, 0, stream>>>(a);
     else
@@ -1301,7 +1369,7 @@ hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
     quant_rows_kernel<float><<<(S + 3) / 4, 256, 0, stream>>>(h, S, p.I, hq, hs);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     Fc2Args a{hq, hs, p.w2, p.w2_scale, p.sorted_ids, p.block_expert, p.num_padded,
-              p.H, p.I, S, log2m, remap, y, 0, nullptr};
+              p.H, p.I, S, log2m, remap, y, 0, queue + kQueues};
     if (hot)
       fc2_kernel<true, true><<<persistent_grid(fc2_kernel<true, true>, 3), 256, 0, stream>>>(a);
     else
