@@ -1,7 +1,7 @@
 """Benchmark of the fused MoE expert FFN hot path on one MI355X.
 
-One step = one pass of the whole path over one batch: router softmax + top-k,
-token-to-expert alignment, FC1 (gate|up) + SiLU*up, FC2, top-k weighted
+One step = one pass of the whole path over one batch: router softmax + top-k
+and token-to-expert alignment (moe_route_align), FC1 (gate|up) + SiLU*up, FC2, top-k weighted
 combine, all in libmoe.so's HIP kernels on torch's current stream. Inputs and
 weights are resident in HBM before the timed region; outputs and workspace are
 allocated once, outside it.
@@ -171,8 +171,7 @@ def main():
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
 
     def step(i=None):
-        moe.route_topk(inp.logits, k, out=(ids, wts), stream=stream)
-        moe.align_block(ids, E, M, out=(sid, be, npad), stream=stream)
+        moe.route_align(inp.logits, k, M, out=(ids, wts, sid, be, npad), stream=stream)
         if i is not None:
             ev_a[i].record(stream)
         ffn(moe.STAGE_FC1)

@@ -127,6 +127,19 @@ moe_status moe_align_block(const int32_t* topk_ids, int T, int k, int E, int blo
                            moe_stream_t stream);
 
 /*
+ * Routing and alignment in one call: the same results as moe_route_topk
+ * followed by moe_align_block on its topk_ids (same passages, same argument
+ * meanings and limits). Batches of at most 8 tokens (and T * k <= 4096) run
+ * as a single one-workgroup launch that keeps the ids on chip between the two
+ * steps; larger batches run the two kernels. T == 0 still writes
+ * *num_padded = 0.
+ */
+moe_status moe_route_align(const float* logits, int T, int E, int k, int renormalize,
+                           int block_m, int32_t* topk_ids, float* topk_weights,
+                           int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
+                           moe_stream_t stream);
+
+/*
  * Block size suggested for a batch: 256 when the average number of slots per
  * expert, T*k/E, is at least 128 (prefill-sized blocks: the FFN then runs
  * grouped-GEMM tiles of 256 weight rows x 256 tokens), else 64 (decode: the

@@ -32,8 +32,8 @@ NO_XCD_REMAP = 1 << 8
 ABI_VERSION = 1
 
 EXPORTS = ("moe_status_str", "moe_abi_version", "moe_route_topk", "moe_align_capacity",
-           "moe_align_block", "moe_default_block_m", "moe_ffn_workspace_bytes", "moe_ffn_bf16",
-           "moe_ffn_fp8", "moe_ffn_f32")
+           "moe_align_block", "moe_route_align", "moe_default_block_m",
+           "moe_ffn_workspace_bytes", "moe_ffn_bf16", "moe_ffn_fp8", "moe_ffn_f32")
 
 
 class MoEError(RuntimeError):
@@ -60,6 +60,8 @@ def _load() -> ctypes.CDLL:
     lib.moe_align_capacity.argtypes = [I, I, I, I]
     lib.moe_align_block.restype = I
     lib.moe_align_block.argtypes = [P, I, I, I, I, P, P, P, P]
+    lib.moe_route_align.restype = I
+    lib.moe_route_align.argtypes = [P, I, I, I, I, I, P, P, P, P, P, P]
     lib.moe_default_block_m.restype = I
     lib.moe_default_block_m.argtypes = [I, I, I]
     lib.moe_ffn_workspace_bytes.restype = Z
@@ -154,6 +156,29 @@ def align_block(topk_ids: torch.Tensor, E: int, block_m: int, out=None, stream=N
     return sorted_ids, block_expert, num_padded
 
 
+def route_align(logits: torch.Tensor, k: int, block_m: int, renormalize: bool = False,
+                out=None, stream=None):
+    """Routing and alignment in one call (moe_route_align). logits [T, E] float32.
+    Returns (topk_ids, topk_weights, sorted_ids, block_expert, num_padded), or
+    fills `out`, a tuple of those five tensors."""
+    _need(logits, "logits", (torch.float32,))
+    T, E = logits.shape
+    dev = logits.device
+    if out is None:
+        cap = align_capacity(T, k, E, block_m)
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+        sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
+        block_expert = torch.empty(cap // max(block_m, 1), dtype=torch.int32, device=dev)
+        num_padded = torch.empty(1, dtype=torch.int32, device=dev)
+    else:
+        ids, wts, sorted_ids, block_expert, num_padded = out
+    _check(lib.moe_route_align(_ptr(logits), T, E, k, int(bool(renormalize)), block_m, _ptr(ids),
+                               _ptr(wts), _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded),
+                               _stream(stream)))
+    return ids, wts, sorted_ids, block_expert, num_padded
+
+
 # ----------------------------------------------------------------- FFN ---
 
 def workspace_bytes(T: int, E: int, H: int, I: int, k: int, block_m: int, dtype: int) -> int:
@@ -243,13 +268,13 @@ def ffn_f32(x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert, num_pad
 
 def forward(x, logits, w1, w2, k: int, block_m: Optional[int] = None, renormalize: bool = False,
             w1_scale=None, w2_scale=None, flags: int = 0, stream=None):
-    """route_topk -> align_block -> ffn_{f32,bf16,fp8}, dtype taken from w1;
-    block_m defaults to moe_default_block_m."""
+    """route_align -> ffn_{f32,bf16,fp8}, dtype taken from w1; block_m defaults
+    to moe_default_block_m."""
     E = w1.shape[0]
     if block_m is None:
         block_m = default_block_m(x.shape[0], E, k)
-    ids, wts = route_topk(logits, k, renormalize, stream=stream)
-    sorted_ids, block_expert, num_padded = align_block(ids, E, block_m, stream=stream)
+    ids, wts, sorted_ids, block_expert, num_padded = route_align(logits, k, block_m, renormalize,
+                                                                 stream=stream)
     if w1.dtype in (torch.uint8, torch.float8_e4m3fn):
         return ffn_fp8(x, w1, w1_scale, w2, w2_scale, ids, wts, sorted_ids, block_expert,
                        num_padded, block_m, flags, stream=stream)

@@ -17,6 +17,7 @@
 // slot order alone, so the output is identical on every run.
 #include "moe_common.h"
 #include "moe_launch.h"
+#include "moe_route_dev.h"
 
 namespace moe {
 
@@ -24,13 +25,16 @@ constexpr int kAlignWaves = 8;
 constexpr int kAlignThreads = kAlignWaves * kWave;
 constexpr int kAlignMaxE = 1024;
 constexpr int kAlignUnroll = 16;
+constexpr int kFuseMaxTokens = kAlignWaves;  // fused routing + alignment: one token per wave
+constexpr int kFuseMaxSlots = 4096;          // and ids that fit a 16 KB LDS table
 
-__global__ __launch_bounds__(kAlignThreads) void align_kernel(
-    const int32_t* __restrict__ ids, int S, int E, int log2m, int cap,
-    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
-    int32_t* __restrict__ num_padded) {
-  __shared__ int cnt[kAlignWaves][kAlignMaxE];  // per-wave histograms, then per-wave bases
-  __shared__ int off[kAlignMaxE + 1];           // padded exclusive offsets; off[E] = total
+// The whole alignment, run by one workgroup of kAlignThreads threads. ids may
+// live in global memory or in LDS; cnt and off are the workgroup's LDS tables.
+__device__ __forceinline__ void align_body(const int32_t* ids, int S, int E, int log2m, int cap,
+                                           int32_t* __restrict__ sorted_ids,
+                                           int32_t* __restrict__ block_expert,
+                                           int32_t* __restrict__ num_padded,
+                                           int (*cnt)[kAlignMaxE], int* off) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int M = 1 << log2m;
 
@@ -129,6 +133,75 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
       if (valid && rank == 0) cnt[w][e] = base + tot;
     }
   }
+}
+
+__global__ __launch_bounds__(kAlignThreads) void align_kernel(
+    const int32_t* __restrict__ ids, int S, int E, int log2m, int cap,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
+    int32_t* __restrict__ num_padded) {
+  __shared__ int cnt[kAlignWaves][kAlignMaxE];  // per-wave histograms, then per-wave bases
+  __shared__ int off[kAlignMaxE + 1];           // padded exclusive offsets; off[E] = total
+  align_body(ids, S, E, log2m, cap, sorted_ids, block_expert, num_padded, cnt, off);
+}
+
+// Routing and alignment of a small batch in one launch: wave w routes token w
+// (at most 8 tokens), keeping the ids in LDS as well, then the same workgroup
+// aligns them from LDS: one launch and one memory round trip less than the
+// two kernels. A wave that routes several tokens does them one after the
+// other (about 5 us each on MI355X), which costs more than the launch it
+// saves, so larger batches take the two kernels.
+template <int VPL>
+__global__ __launch_bounds__(kAlignThreads) void route_align_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int renorm,
+    int32_t* __restrict__ ids, float* __restrict__ wts, int log2m, int cap,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
+    int32_t* __restrict__ num_padded) {
+  __shared__ int cnt[kAlignWaves][kAlignMaxE];
+  __shared__ int off[kAlignMaxE + 1];
+  __shared__ int32_t ids_lds[kFuseMaxSlots];
+  const int t = threadIdx.x >> 6;
+  if (t < T) {  // uniform per wave
+    float v[VPL];
+    load_logits<VPL>(logits, t, E, v);
+    route_token<VPL>(v, t, E, k, renorm, ids, wts, ids_lds);
+  }
+  __syncthreads();
+  align_body(ids_lds, T * k, E, log2m, cap, sorted_ids, block_expert, num_padded, cnt, off);
+}
+
+static int ilog2_align(int block_m) {
+  int log2m = 0;
+  while ((1 << log2m) < block_m) ++log2m;
+  return log2m;
+}
+
+bool route_align_fusable(int T, int E, int k) {
+  (void)E;
+  return T <= kFuseMaxTokens && (long)T * k <= kFuseMaxSlots;
+}
+
+hipError_t launch_route_align(const float* logits, int T, int E, int k, int renorm,
+                              int32_t* ids, float* wts, int block_m, int cap,
+                              int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
+                              hipStream_t stream) {
+  const int log2m = ilog2_align(block_m);
+  const int vpl = (E + kWave - 1) / kWave;
+#define MOE_ROUTE_ALIGN(V)                                                               \
+  route_align_kernel<V><<<1, kAlignThreads, 0, stream>>>(logits, T, E, k, renorm, ids, wts, \
+                                                         log2m, cap, sorted_ids,            \
+                                                         block_expert, num_padded)
+  if (vpl <= 1)
+    MOE_ROUTE_ALIGN(1);
+  else if (vpl <= 2)
+    MOE_ROUTE_ALIGN(2);
+  else if (vpl <= 4)
+    MOE_ROUTE_ALIGN(4);
+  else if (vpl <= 8)
+    MOE_ROUTE_ALIGN(8);
+  else
+    MOE_ROUTE_ALIGN(16);
+#undef MOE_ROUTE_ALIGN
+  return hipGetLastError();
 }
 
 hipError_t launch_align(const int32_t* ids, int S, int E, int block_m, int cap,

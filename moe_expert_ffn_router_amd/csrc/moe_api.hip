@@ -120,6 +120,35 @@ MOE_EXPORT moe_status moe_align_block(const int32_t* topk_ids, int T, int k, int
                                       block_expert, num_padded, (hipStream_t)stream));
 }
 
+MOE_EXPORT moe_status moe_route_align(const float* logits, int T, int E, int k, int renormalize,
+                                      int block_m, int32_t* topk_ids, float* topk_weights,
+                                      int32_t* sorted_ids, int32_t* block_expert,
+                                      int32_t* num_padded, moe_stream_t stream) {
+  moe_status s = check_common(T, E, k);
+  if (s != MOE_OK) return s;
+  if (!is_pow2_le256(block_m)) return MOE_ERR_SHAPE;
+  const long S = (long)T * k;
+  const size_t cap = capacity(S, E, block_m);
+  if (!num_padded) return MOE_ERR_NULL;
+  if (T > 0 && (!logits || !topk_ids || !topk_weights)) return MOE_ERR_NULL;
+  if (cap > 0 && (!sorted_ids || !block_expert)) return MOE_ERR_NULL;
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4) ||
+      !aligned(sorted_ids, 4) || !aligned(block_expert, 4) || !aligned(num_padded, 4))
+    return MOE_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  if (moe::route_align_fusable(T, E, k))
+    return hip_status(moe::launch_route_align(logits, T, E, k, renormalize ? 1 : 0, topk_ids,
+                                              topk_weights, block_m, (int)cap, sorted_ids,
+                                              block_expert, num_padded, st));
+  if (T > 0) {
+    const hipError_t e = moe::launch_route_topk(logits, T, E, k, renormalize ? 1 : 0, topk_ids,
+                                                topk_weights, st);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  return hip_status(moe::launch_align(topk_ids, (int)S, E, block_m, (int)cap, sorted_ids,
+                                      block_expert, num_padded, st));
+}
+
 MOE_EXPORT int moe_default_block_m(int T, int E, int k) {
   if (check_common(T, E, k) != MOE_OK) return 0;
   return (long)T * k >= 128L * E ? 256 : 64;

@@ -49,17 +49,55 @@ __device__ __forceinline__ uint32_t f32_to_e4m3fn(float v) {
 }
 
 // ----------------------------------------------------- wave reductions ---
+// Partner exchange of step s of a wave64 reduction. Steps 0..3 are DPP moves
+// inside rows of 16 lanes (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror, row_mirror), each pairing the two halves of a group of 2,
+// 4, 8, 16 lanes; steps 4 and 5 pair lane l with l ^ 16 and l ^ 32 through
+// gfx950's v_permlane16_swap / v_permlane32_swap (swapping a register with a
+// copy of itself leaves, in lanes of even rows / the low half, the partner's
+// value in the second result and elsewhere in the first). Combining a value
+// with its partner's at every step leaves the same combination over all 64
+// lanes in every lane (bit-identical when the combination is commutative),
+// with no LDS traffic.
+template <int STEP>
+__device__ __forceinline__ int wave_partner(int v) {
+  if constexpr (STEP == 0) {
+    return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+  } else if constexpr (STEP == 1) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+  } else if constexpr (STEP == 2) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+  } else if constexpr (STEP == 3) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+  } else if constexpr (STEP == 4) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return ((threadIdx.x >> 4) & 1) == 0 ? (int)r[1] : (int)r[0];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (threadIdx.x & 32) == 0 ? (int)r[1] : (int)r[0];
+  }
+}
+template <int STEP>
+__device__ __forceinline__ float wave_partner(float v) {
+  return __int_as_float(wave_partner<STEP>(__float_as_int(v)));
+}
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
+  v = fmaxf(v, wave_partner<0>(v));
+  v = fmaxf(v, wave_partner<1>(v));
+  v = fmaxf(v, wave_partner<2>(v));
+  v = fmaxf(v, wave_partner<3>(v));
+  v = fmaxf(v, wave_partner<4>(v));
+  return fmaxf(v, wave_partner<5>(v));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v += wave_partner<0>(v);
+  v += wave_partner<1>(v);
+  v += wave_partner<2>(v);
+  v += wave_partner<3>(v);
+  v += wave_partner<4>(v);
+  return v + wave_partner<5>(v);
 }
 
 // ------------------------------------------------------------- MFMA ---

@@ -15,6 +15,14 @@ hipError_t launch_align(const int32_t* ids, int S, int E, int block_m, int cap,
                         int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
                         hipStream_t stream);
 
+// Routing + alignment in one single-workgroup launch; only for batches with
+// route_align_fusable(T, E, k).
+bool route_align_fusable(int T, int E, int k);
+hipError_t launch_route_align(const float* logits, int T, int E, int k, int renorm,
+                              int32_t* ids, float* wts, int block_m, int cap,
+                              int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
+                              hipStream_t stream);
+
 // Workspace carve-up shared by the FFN launchers and moe_ffn_workspace_bytes.
 struct FfnWorkspace {
   size_t h_off, h_bytes;    // h per slot: bf16 [S, I] (bf16), f32 [S, I] (fp8, f32)

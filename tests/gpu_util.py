@@ -54,8 +54,7 @@ def gpu_forward(inp, block_m=None, renormalize=False, flags=0):
     m = moe()
     if block_m is None:
         block_m = bench_block_m(inp)
-    ids, w = m.route_topk(inp.logits, inp.k, renormalize)
-    sid, be, npad = m.align_block(ids, inp.E, block_m)
+    ids, w, sid, be, npad = m.route_align(inp.logits, inp.k, block_m, renormalize)
     if inp.dtype == "fp8":
         out = m.ffn_fp8(inp.x, inp.w1, inp.w1_scale, inp.w2, inp.w2_scale, ids, w, sid, be, npad,
                         block_m, flags)

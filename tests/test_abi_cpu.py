@@ -58,6 +58,18 @@ def test_route_validation():
     assert f(None, 0, 8, 2, 0, None, None, None) == OK    # T = 0: nothing to do
 
 
+def test_route_align_validation():
+    f = lib.moe_route_align
+    assert f(P, 4, 0, 1, 0, 16, P, P, P, P, P, None) == SHAPE      # E < 1
+    assert f(P, 4, 8, 9, 0, 16, P, P, P, P, P, None) == SHAPE      # k > E
+    assert f(P, 4, 8, 2, 0, 12, P, P, P, P, P, None) == SHAPE      # block_m not a power of 2
+    assert f(None, 4, 8, 2, 0, 16, P, P, P, P, P, None) == NULL    # logits
+    assert f(P, 4, 8, 2, 0, 16, P, None, P, P, P, None) == NULL    # topk_weights
+    assert f(P, 4, 8, 2, 0, 16, P, P, None, P, P, None) == NULL    # sorted_ids
+    assert f(P, 4, 8, 2, 0, 16, P, P, P, P, None, None) == NULL    # num_padded
+    assert f(P, 4, 8, 2, 0, 16, P, P, P + 2, P, P, None) == ALIGN
+
+
 def test_align_validation_and_capacity():
     cap = lib.moe_align_capacity
     assert cap(16, 8, 64, 64) == 128 + 64 * 63           # S + min(E,S)(M-1), a multiple of M

@@ -101,3 +101,31 @@ def test_align_max_slots():
     real = sid[:n][sid[:n] < T * k]
     assert np.array_equal(real, order)
     assert np.all(np.diff(be[:n // M]) >= 0)
+
+
+@pytest.mark.parametrize("block_m", [1, 16, 64, 256])
+@pytest.mark.parametrize("T,E,k,kind", [
+    (1, 1, 1, "normal"), (8, 64, 8, "normal"), (5, 1024, 32, "normal"), (3, 65, 65, "ties"),
+    (8, 1024, 512, "ties"),                       # 4096 slots: the largest single-launch batch
+    (9, 64, 8, "normal"), (16, 64, 8, "normal"),  # larger batches: the two-kernel path
+    (64, 128, 8, "ties"), (300, 16, 4, "ties")])
+def test_route_align_matches_separate_calls(T, E, k, kind, block_m):
+    say(f"route_align T={T} E={E} k={k} {kind} block_m={block_m}")
+    L = torch.from_numpy(_logits(T, E, T * 7 + E, kind)).cuda()
+    for renorm in (False, True):
+        fused = moe().route_align(L, k, block_m, renorm)
+        ids, w = moe().route_topk(L, k, renorm)
+        sep = (ids, w) + tuple(moe().align_block(ids, E, block_m))
+        torch.cuda.synchronize()
+        for a, b in zip(fused, sep):
+            assert torch.equal(a, b)              # the same bits either way
+        ids_o, w_o = oracle.route(L.cpu().numpy(), k, renorm)
+        check_routing(fused[0], fused[1], ids_o, w_o)
+        check_align(fused[2:], ids_o, E, block_m, T * k)
+
+
+def test_route_align_empty_batch():
+    say("route_align T=0")
+    out = moe().route_align(torch.empty((0, 8), device="cuda"), 2, 16)
+    torch.cuda.synchronize()
+    assert out[0].shape == (0, 2) and int(out[4].item()) == 0
