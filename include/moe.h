@@ -24,7 +24,8 @@
  *  - Each call validates its arguments on the host, enqueues its kernels on
  *    `stream` (NULL = the null stream) and returns; it never synchronises the
  *    host, never allocates device memory and keeps no state between calls
- *    other than a per-device cache of the device's CU count.
+ *    other than a per-device cache of launch geometry (CU count and resident
+ *    workgroups per kernel).
  *  - On a bad argument nothing is launched and the status says why. A launch
  *    failure returns MOE_ERR_HIP. Faults inside a kernel surface at the
  *    caller's next synchronisation, as usual in HIP. Device-resident values
