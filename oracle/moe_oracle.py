@@ -151,7 +151,9 @@ def align(ids: np.ndarray, E: int, block_m: int
     s = t*k + j; for e = 0..E-1 in order, append the slots routed to e in
     ascending s, then pad the run to a multiple of block_m with the sentinel S.
     block_expert[b] is the expert owning block b; num_padded the total length.
-    Experts with no slot contribute nothing.
+    Experts with no slot contribute nothing. A slot whose id lies outside
+    [0, E) belongs to an expert served elsewhere (expert parallelism: this
+    shard holds experts 0..E-1 of its local numbering) and is left out.
     """
     flat = np.asarray(ids, dtype=np.int64).reshape(-1)
     S = flat.size
@@ -188,16 +190,23 @@ def swiglu_expert(w1e: np.ndarray, w2e: np.ndarray, xs: np.ndarray) -> np.ndarra
 
 def ffn(x: np.ndarray, get_w1: Callable[[int], np.ndarray],
         get_w2: Callable[[int], np.ndarray], ids: np.ndarray, weights: np.ndarray,
-        tokens: Optional[Iterable[int]] = None) -> np.ndarray:
+        tokens: Optional[Iterable[int]] = None, num_experts: Optional[int] = None
+        ) -> np.ndarray:
     """out[t] = sum_j weights[t, j] * expert_{ids[t, j]}(x[t]) for each token t in
     ``tokens`` (all by default), float64. ``get_w1(e)``/``get_w2(e)`` return the
-    expert's float64 weights. Rows of the result follow ``tokens``."""
+    expert's float64 weights. Rows of the result follow ``tokens``. With
+    ``num_experts``, slots whose id lies outside [0, num_experts) belong to
+    experts served elsewhere and add nothing: the result is this shard's
+    partial sum (expert parallelism, the per-rank share of the Vera Rubin
+    page's "Locality domain" comparison)."""
     x = np.asarray(x, dtype=np.float64)
     tok = np.arange(x.shape[0]) if tokens is None else np.asarray(list(tokens))
     k = ids.shape[1]
     Y = np.zeros((tok.size, k, x.shape[1]), dtype=np.float64)
     sub = ids[tok]
     for e in np.unique(sub):
+        if num_experts is not None and not 0 <= e < num_experts:
+            continue
         rows, js = np.nonzero(sub == e)
         Y[rows, js] = swiglu_expert(get_w1(int(e)), get_w2(int(e)), x[tok[rows]])
     w = np.asarray(weights, dtype=np.float64)[tok]
@@ -227,13 +236,15 @@ def quant_rows_e4m3(v: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
 
 def ffn_fp8(x_bits: np.ndarray, get_w1q: Callable[[int], np.ndarray], w1_scale: np.ndarray,
             get_w2q: Callable[[int], np.ndarray], w2_scale: np.ndarray, ids: np.ndarray,
-            weights: np.ndarray, tokens: Optional[Iterable[int]] = None) -> np.ndarray:
+            weights: np.ndarray, tokens: Optional[Iterable[int]] = None,
+            num_experts: Optional[int] = None) -> np.ndarray:
     """W8A8 FP8 variant, format-exact: the same codes and scales the GPU gets.
 
     W^[e, n, :] = dec(Wq[e, n, :]) * scale[e, n] (per output channel);
     x^_t = a_t * dec(q(x_t)) per token; h is computed in float64 from x^ and
     W1^, rounded to float32, then quantised per (token, expert) slot row the
-    same way before FC2; combine as in ``ffn``. ``x_bits`` are bfloat16 bits.
+    same way before FC2; combine as in ``ffn`` (``num_experts`` as there).
+    ``x_bits`` are bfloat16 bits.
     """
     x32 = bf16_bits_to_f64(x_bits).astype(np.float32)
     tok = np.arange(x32.shape[0]) if tokens is None else np.asarray(list(tokens))
@@ -245,6 +256,8 @@ def ffn_fp8(x_bits: np.ndarray, get_w1q: Callable[[int], np.ndarray], w1_scale: 
     sub = ids[tok]
     for e in np.unique(sub):
         e = int(e)
+        if num_experts is not None and not 0 <= e < num_experts:
+            continue
         w1 = e4m3fn_decode(get_w1q(e)) * np.asarray(w1_scale[e], np.float64)[:, None]
         w2 = e4m3fn_decode(get_w2q(e)) * np.asarray(w2_scale[e], np.float64)[:, None]
         I = w2.shape[1]
