@@ -37,6 +37,12 @@ def parse():
     ap.add_argument("--block-m", type=int, default=0,
                     help="block size; 0 = moe_default_block_m for the workload")
     ap.add_argument("--flags", type=int, default=0, help="extra moe_ffn flags (e.g. 256 = no XCD remap)")
+    ap.add_argument("--ep", type=int, default=1,
+                    help="time one expert-parallel rank's share: rank 0 of G holds experts "
+                         "[0, E/G); slots of the other experts are remote")
+    ap.add_argument("--tp", type=int, default=1,
+                    help="time one tensor-parallel rank's share: rank 0 of G holds the "
+                         "first I/G columns of every expert (FC2 gives a partial sum)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
@@ -139,6 +145,19 @@ def main():
     cfg = CONFIGS[args.config]
     inp = config_inputs(args.config, device="cuda")
     T, E, H, I, k = inp.T, inp.E, inp.H, inp.I, inp.k
+    Eg = E                                   # experts of the whole layer (routing)
+    w1, w2, s1, s2 = inp.w1, inp.w2, inp.w1_scale, inp.w2_scale
+    if args.ep > 1 and args.tp > 1:
+        sys.exit("bench.py: --ep and --tp are separate measurements")
+    if args.ep > 1:                          # rank 0 holds experts [0, E/G): local id = global id
+        E = Eg // args.ep
+        w1, w2 = w1[:E], w2[:E]
+        s1, s2 = (None, None) if s1 is None else (s1[:E], s2[:E])
+    if args.tp > 1:                          # rank 0 holds columns [0, I/G) of every expert
+        c = I // args.tp
+        w1 = torch.cat([w1[:, :c], w1[:, I:I + c]], 1).contiguous()
+        w2 = w2[:, :, :c].contiguous()
+        I = c
     M = args.block_m or moe.default_block_m(T, E, k)
     S = T * k
     dev = inp.x.device
@@ -158,12 +177,11 @@ def main():
     def ffn(flags):
         f = flags | args.flags
         if inp.dtype == "fp8":
-            moe.ffn_fp8(inp.x, inp.w1, inp.w1_scale, inp.w2, inp.w2_scale, ids, wts, sid, be, npad,
-                        M, f, ws, out)
+            moe.ffn_fp8(inp.x, w1, s1, w2, s2, ids, wts, sid, be, npad, M, f, ws, out)
         elif inp.dtype == "bf16":
-            moe.ffn_bf16(inp.x, inp.w1, inp.w2, ids, wts, sid, be, npad, M, f, ws, out)
+            moe.ffn_bf16(inp.x, w1, w2, ids, wts, sid, be, npad, M, f, ws, out)
         else:
-            moe.ffn_f32(inp.x, inp.w1, inp.w2, ids, wts, sid, be, npad, M, f, ws, out)
+            moe.ffn_f32(inp.x, w1, w2, ids, wts, sid, be, npad, M, f, ws, out)
 
     stream = torch.cuda.current_stream()
     n_ev = args.steps
@@ -171,7 +189,11 @@ def main():
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
 
     def step(i=None):
-        moe.route_align(inp.logits, k, M, out=(ids, wts, sid, be, npad), stream=stream)
+        if E == Eg:
+            moe.route_align(inp.logits, k, M, out=(ids, wts, sid, be, npad), stream=stream)
+        else:  # the rank routes over all experts and aligns its local ones
+            moe.route_topk(inp.logits, k, out=(ids, wts), stream=stream)
+            moe.align_block(ids, E, M, out=(sid, be, npad), stream=stream)
         if i is not None:
             ev_a[i].record(stream)
         ffn(moe.STAGE_FC1)
@@ -200,19 +222,21 @@ def main():
 
     # algorithmic work (active experts from this run's routing)
     ids_h = ids.cpu().numpy()
-    A = int(np.unique(ids_h).size)
+    A = int(np.unique(ids_h[ids_h < E]).size)       # active local experts
     bw = {"f32": 4, "bf16": 2, "fp8": 1}[inp.dtype]
     bx = {"f32": 4, "bf16": 2, "fp8": 2}[inp.dtype]
+    S_loc = int((ids_h < E).sum())                   # slots this GPU computes
     w_bytes = A * 3 * I * H * bw + (A * (2 * I + H) * 4 if inp.dtype == "fp8" else 0)
-    layer_bytes = w_bytes + T * H * bx + T * H * (4 if inp.dtype == "f32" else 2) + T * E * 4 + S * 8
-    flops = S * 6 * H * I
+    layer_bytes = w_bytes + T * H * bx + T * H * (4 if inp.dtype == "f32" else 2) + T * Eg * 4 + S * 8
+    flops = S_loc * 6 * H * I
     fc1_bytes = A * 2 * I * H * bw + (A * 2 * I * 4 if inp.dtype == "fp8" else 0) \
-        + T * H * bx + S * I * (2 if inp.dtype == "bf16" else 4)
+        + T * H * bx + S_loc * I * (2 if inp.dtype == "bf16" else 4)
     fc1_gbs = fc1_bytes / (fc1_ms * 1e-3) / 1e9
     step_s = ms_per_step * 1e-3
-    wl = cfg["name"]
+    wl = cfg["name"] + (f"_ep{args.ep}_rank0" if args.ep > 1 else "") \
+        + (f"_tp{args.tp}_rank0" if args.tp > 1 else "")
     if M >= 128:  # grouped-GEMM tiles (prefill-sized blocks): FC1 is bound by MFMA
-        fc1_flops = S * 2 * I * H * 2
+        fc1_flops = S_loc * 2 * I * H * 2
         fc1_tfs = fc1_flops / (fc1_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(fc1_tfs, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(fc1_tfs / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -240,7 +264,7 @@ def main():
         "roofline": roofline,
         "source_digest": source_digest(),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.ep == 1 and args.tp == 1:
         cb, _ = cpu_baseline(inp, args.cpu_seconds)
         rec["cpu_baseline"] = cb
     else:

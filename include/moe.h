@@ -110,7 +110,10 @@ moe_status moe_route_topk(const float* logits, int T, int E, int k, int renormal
  * hold: round_up(S + min(E, S) * (block_m - 1), block_m), S = T * k. The
  * number of blocks is capacity / block_m (the length of `block_expert`).
  *
- *  topk_ids      [T, k] int32, device: expert of flat slot s = t*k + j.
+ *  topk_ids      [T, k] int32, device: expert of flat slot s = t*k + j. An
+ *                id outside [0, E) marks a slot whose expert another shard
+ *                serves (expert parallelism, local expert numbering): the slot
+ *                is left out of the lists.
  *  sorted_ids    [capacity] int32, device, written: for e = 0..E-1 the slots
  *                routed to e in ascending s, each expert's run padded to a
  *                multiple of block_m with the sentinel S. Entries at and past
@@ -176,7 +179,9 @@ size_t moe_ffn_workspace_bytes(int T, int E, int H, int I, int k, int block_m, i
  *  sorted_ids, block_expert, num_padded   from moe_align_block with the same
  *                T, k, E and block_m.
  *  out           [T, H] bf16, written: out[t] = sum_j w[t,j] * y[t*k+j],
- *                accumulated in fp32 in j order, rounded once (RNE).
+ *                accumulated in fp32 in j order, rounded once (RNE). Slots
+ *                whose id lies outside [0, E) (served by another shard) add
+ *                nothing, so out is this shard's partial sum.
  *  Intermediate h is rounded to bf16 before FC2.
  *  Limits: 0 <= T, 1 <= E <= 1024, 1 <= k <= E, T * k < 2^24, H and I
  *  multiples of 128, block_m a power of two in [1, 256]; x, w1, w2, out and

@@ -14,7 +14,8 @@
 // slots at a time: lanes holding the same expert are found with one ballot per
 // expert-id bit, a lane's rank is the number of such lanes below it, and the
 // group's leader advances the wave's running base. Every placement follows from
-// slot order alone, so the output is identical on every run.
+// slot order alone, so the output is identical on every run. Ids outside
+// [0, E) mark slots of experts served by another shard and are left out.
 #include "moe_common.h"
 #include "moe_launch.h"
 #include "moe_route_dev.h"
@@ -56,7 +57,7 @@ __device__ __forceinline__ void align_body(const int32_t* ids, int S, int E, int
     }
 #pragma unroll
     for (int u = 0; u < kAlignUnroll; ++u)
-      if (e[u] >= 0) atomicAdd(&cnt[w][e[u]], 1);
+      if ((unsigned)e[u] < (unsigned)E) atomicAdd(&cnt[w][e[u]], 1);  // else: remote or past s1
   }
   __syncthreads();
 
@@ -117,7 +118,7 @@ __device__ __forceinline__ void align_body(const int32_t* ids, int S, int E, int
 #pragma unroll
     for (int u = 0; u < kAlignUnroll; ++u) {
       const int s = sb + u * kWave + lane;
-      const bool valid = ev[u] >= 0;
+      const bool valid = (unsigned)ev[u] < (unsigned)E;
       const int e = valid ? ev[u] : 0;
       uint64_t same = __ballot(valid);
       for (int bit = 0; bit < nbits; ++bit) {

@@ -1103,16 +1103,21 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const InT* __restrict__
 __device__ __forceinline__ void load8y(const float* p, float (&v)[8]) { load8(p, v); }
 __device__ __forceinline__ void load8y(const uint16_t* p, float (&v)[8]) { load8(p, v); }
 
+// Slots whose expert id lies outside [0, E) belong to another shard: their y
+// rows were never written and they add nothing.
 template <typename YT, typename OutT>
 __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
-                                                      const float* __restrict__ w, int T, int H,
-                                                      int k, OutT* __restrict__ out) {
+                                                      const float* __restrict__ w,
+                                                      const int32_t* __restrict__ ids, int E,
+                                                      int T, int H, int k,
+                                                      OutT* __restrict__ out) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   const int per_row = H >> 3;
   if (i >= (long)T * per_row) return;
   const int t = (int)(i / per_row), n = (int)(i % per_row) * 8;
   float acc[8] = {};
   for (int j = 0; j < k; ++j) {
+    if ((unsigned)ids[(size_t)t * k + j] >= (unsigned)E) continue;
     const float wj = w[(size_t)t * k + j];
     float v[8];
     load8y(y + ((size_t)t * k + j) * H + n, v);
@@ -1134,13 +1139,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
 // A combine for H not a multiple of 8 (fp32 path): one thread per element.
 __global__ __launch_bounds__(256) void combine_f32_scalar_kernel(const float* __restrict__ y,
                                                                  const float* __restrict__ w,
-                                                                 int T, int H, int k,
+                                                                 const int32_t* __restrict__ ids,
+                                                                 int E, int T, int H, int k,
                                                                  float* __restrict__ out) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= (long)T * H) return;
   const int t = (int)(i / H), n = (int)(i % H);
   float acc = 0.f;
-  for (int j = 0; j < k; ++j) acc += w[(size_t)t * k + j] * y[((size_t)t * k + j) * H + n];
+  for (int j = 0; j < k; ++j)
+    if ((unsigned)ids[(size_t)t * k + j] < (unsigned)E)
+      acc += w[(size_t)t * k + j] * y[((size_t)t * k + j) * H + n];
   out[i] = acc;
 }
 
@@ -1278,17 +1286,17 @@ static hipError_t launch_combine(const FfnProblem& p, const FfnWorkspace& L, int
     const dim3 grid((unsigned)((n + 255) / 256));
     if (dtype == MOE_DTYPE_BF16)
       combine_kernel<uint16_t, uint16_t><<<grid, 256, 0, stream>>>(
-          (const uint16_t*)y, p.topk_weights, p.T, p.H, p.k, (uint16_t*)p.out);
+          (const uint16_t*)y, p.topk_weights, p.topk_ids, p.E, p.T, p.H, p.k, (uint16_t*)p.out);
     else if (dtype == MOE_DTYPE_FP8)
       combine_kernel<float, uint16_t><<<grid, 256, 0, stream>>>(
-          (const float*)y, p.topk_weights, p.T, p.H, p.k, (uint16_t*)p.out);
+          (const float*)y, p.topk_weights, p.topk_ids, p.E, p.T, p.H, p.k, (uint16_t*)p.out);
     else
-      combine_kernel<float, float><<<grid, 256, 0, stream>>>((const float*)y, p.topk_weights, p.T,
-                                                             p.H, p.k, (float*)p.out);
+      combine_kernel<float, float><<<grid, 256, 0, stream>>>(
+          (const float*)y, p.topk_weights, p.topk_ids, p.E, p.T, p.H, p.k, (float*)p.out);
   } else {
     const long n = (long)p.T * p.H;
     combine_f32_scalar_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(
-        (const float*)y, p.topk_weights, p.T, p.H, p.k, (float*)p.out);
+        (const float*)y, p.topk_weights, p.topk_ids, p.E, p.T, p.H, p.k, (float*)p.out);
   }
   return hipGetLastError();
 }
