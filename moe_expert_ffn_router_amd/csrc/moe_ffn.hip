@@ -169,17 +169,25 @@ template <bool FP8>
 struct Cold {
   static constexpr int kChunk = FP8 ? 256 : 128;
   static constexpr int kStep = 128;
-  static constexpr int U = FP8 ? 1 : 2;  // k-chunks per pipeline group
 };
+
+// k-chunks per pipeline group: more bytes in flight per wave, paid in
+// registers. In the cold-only launch 4 (bf16) means 3 waves per SIMD instead
+// of 4 but twice the bytes in flight per wave (FC2 of 16-token decode: +4%,
+// FC1 unchanged); a launch that also holds the LDS-staged hot path keeps 2,
+// which holds its occupancy at 3.
+template <bool FP8, bool HOT>
+constexpr int cold_u() {
+  return FP8 ? 1 : (HOT ? 2 : 4);
+}
 
 __device__ __forceinline__ int half_split_off() {
   const int lane = threadIdx.x & 63;
   return ((lane & 15) >> 3) * 64 + (lane >> 4) * 16;
 }
 
-template <bool FP8>
+template <bool FP8, int U>
 struct ColdGroup {
-  static constexpr int U = Cold<FP8>::U;
   Frag<FP8> p[U], q[U], b[U];
   __device__ __forceinline__ void issue(const uint8_t* __restrict__ ap,
                                         const uint8_t* __restrict__ aq,
@@ -209,15 +217,15 @@ struct ColdGroup {
 // loaded only if ok) over kbytes bytes of every row. Two register groups
 // alternate: the next group's loads are issued before the current group's
 // MFMAs, so with in-order load counters they stay in flight meanwhile.
-template <bool FP8>
+template <bool FP8, int U>
 __device__ __forceinline__ void cold_kloop(const uint8_t* __restrict__ ap,
                                            const uint8_t* __restrict__ aq,
                                            const uint8_t* __restrict__ bp, bool ok, int kbytes,
                                            f32x4& accp, f32x4& accq) {
-  constexpr int CH = Cold<FP8>::kChunk, ST = Cold<FP8>::kStep, U = Cold<FP8>::U;
+  constexpr int CH = Cold<FP8>::kChunk, ST = Cold<FP8>::kStep;
   const int nch = kbytes / CH;
   const int ngrp = nch / U;
-  ColdGroup<FP8> g0, g1;
+  ColdGroup<FP8, U> g0, g1;
   if (ngrp > 0) g0.issue(ap, aq, bp, ok, 0);
   int g = 0;
   for (; g + 1 < ngrp; g += 2) {
@@ -403,7 +411,7 @@ __device__ __forceinline__ void store_h(const Fc1Args& p, int slot, int col, con
 // Cold FC1 tile r (h columns [8r, 8r+8)): P = gate rows [8r, 8r+8), Q = the
 // matching up rows [I+8r, I+8r+8). After the diagonal sums a lane holds g and
 // u of the same (column, token).
-template <bool FP8>
+template <bool FP8, int U>
 __device__ __forceinline__ void fc1_cold(const Fc1Args& p, int e, int r, int slot) {
   const int lane = threadIdx.x & 63;
   const size_t rowb = (size_t)p.H * (FP8 ? 1 : 2);
@@ -424,7 +432,7 @@ __device__ __forceinline__ void fc1_cold(const Fc1Args& p, int e, int r, int slo
     su = *(const f32x4*)(p.w1s + (size_t)e * 2 * p.I + p.I + col);
   }
   f32x4 accp = {}, accq = {};
-  cold_kloop<FP8>(ap, aq, bp, ok, (int)rowb, accp, accq);
+  cold_kloop<FP8, U>(ap, aq, bp, ok, (int)rowb, accp, accq);
   f32x4 g = diag_sum(accp), u = diag_sum(accq);
   if (holder && ok) {
     if (FP8) {
@@ -508,7 +516,7 @@ __device__ __forceinline__ void store_y(const Fc2Args& p, int slot, int row, con
 }
 
 // Cold FC2 tile r: P = output rows [16r, 16r+8), Q = [16r+8, 16r+16).
-template <bool FP8>
+template <bool FP8, int U>
 __device__ __forceinline__ void fc2_cold(const Fc2Args& p, int e, int r, int slot) {
   const int lane = threadIdx.x & 63;
   const size_t rowb = (size_t)p.I * (FP8 ? 1 : 2);
@@ -529,7 +537,7 @@ __device__ __forceinline__ void fc2_cold(const Fc2Args& p, int e, int r, int slo
     sq = *(const f32x4*)(p.w2s + (size_t)e * p.H + row + 8);
   }
   f32x4 accp = {}, accq = {};
-  cold_kloop<FP8>(ap, aq, bp, ok, (int)rowb, accp, accq);
+  cold_kloop<FP8, U>(ap, aq, bp, ok, (int)rowb, accp, accq);
   f32x4 vp = diag_sum(accp), vq = diag_sum(accq);
   if (holder && ok) {
     if (FP8) {
@@ -662,14 +670,16 @@ __device__ __forceinline__ void run_quads(const Args& p, int n_rt, uint8_t* lds)
 template <bool FP8, bool HOT>
 __global__ __launch_bounds__(256) void fc1_kernel(Fc1Args p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[HOT ? 2 * kHotTok * kLdsRow + 16 : 16];
-  run_quads<FP8, HOT, false, Fc1Args, fc1_cold<FP8>, fc1_hot_pass<FP8, 1>, fc1_hot_pass<FP8, 2>,
+  run_quads<FP8, HOT, false, Fc1Args, fc1_cold<FP8, cold_u<FP8, HOT>()>, fc1_hot_pass<FP8, 1>,
+            fc1_hot_pass<FP8, 2>,
             fc1_hot_pass<FP8, 3>, fc1_hot_pass<FP8, 4>>(p, p.I >> 3, lds);
 }
 
 template <bool FP8, bool HOT>
 __global__ __launch_bounds__(256) void fc2_kernel(Fc2Args p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[HOT ? 2 * kHotTok * kLdsRow + 16 : 16];
-  run_quads<FP8, HOT, HOT, Fc2Args, fc2_cold<FP8>, fc2_hot_pass<FP8, 1>, fc2_hot_pass<FP8, 2>,
+  run_quads<FP8, HOT, HOT, Fc2Args, fc2_cold<FP8, cold_u<FP8, HOT>()>, fc2_hot_pass<FP8, 1>,
+            fc2_hot_pass<FP8, 2>,
             fc2_hot_pass<FP8, 3>, fc2_hot_pass<FP8, 4>>(p, p.H >> 4, lds);
 }
 
