@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--tp", type=int, default=1,
                     help="time one tensor-parallel rank's share: rank 0 of G holds the "
                          "first I/G columns of every expert (FC2 gives a partial sum)")
+    ap.add_argument("--weight-only", action="store_true",
+                    help="FP8 workloads: run the weight-only (W8A16) FFN on the same codes "
+                         "and scales, activations kept in bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
@@ -74,7 +77,7 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, target_s: float):
+def cpu_baseline(inp, target_s: float, weight_only: bool = False):
     """The CPU oracle as it stands, on the first n tokens of the same workload;
     n grows until about target_s seconds of oracle work have been timed."""
     import numpy as np
@@ -102,7 +105,11 @@ def cpu_baseline(inp, target_s: float):
         toks = list(range(n_next))
         t0 = time.perf_counter()
         ids, w = oracle.route(logits[:n_next], inp.k)
-        if inp.dtype == "fp8":
+        if inp.dtype == "fp8" and weight_only:
+            sample_out = oracle.ffn_w8a16(x_bits[:n_next], w1h.__getitem__,
+                                          inp.host_w1_scale(), w2h.__getitem__,
+                                          inp.host_w2_scale(), ids, w, toks)
+        elif inp.dtype == "fp8":
             sample_out = oracle.ffn_fp8(x_bits[:n_next], w1h.__getitem__, inp.host_w1_scale(),
                                         w2h.__getitem__, inp.host_w2_scale(), ids, w, toks)
         elif inp.dtype == "bf16":
@@ -161,7 +168,12 @@ def main():
     M = args.block_m or moe.default_block_m(T, E, k)
     S = T * k
     dev = inp.x.device
+    if args.weight_only and inp.dtype != "fp8":
+        sys.exit("bench.py: --weight-only needs an FP8 workload (config 3)")
+    wo = args.weight_only
     dt_code = {"f32": moe.MOE_DTYPE_F32, "bf16": moe.MOE_DTYPE_BF16, "fp8": moe.MOE_DTYPE_FP8}[inp.dtype]
+    if wo:
+        dt_code = moe.MOE_DTYPE_W8A16
 
     # everything the step writes, allocated once
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)
@@ -176,7 +188,9 @@ def main():
 
     def ffn(flags):
         f = flags | args.flags
-        if inp.dtype == "fp8":
+        if wo:
+            moe.ffn_w8a16(inp.x, w1, s1, w2, s2, ids, wts, sid, be, npad, M, f, ws, out)
+        elif inp.dtype == "fp8":
             moe.ffn_fp8(inp.x, w1, s1, w2, s2, ids, wts, sid, be, npad, M, f, ws, out)
         elif inp.dtype == "bf16":
             moe.ffn_bf16(inp.x, w1, w2, ids, wts, sid, be, npad, M, f, ws, out)
@@ -230,10 +244,10 @@ def main():
     layer_bytes = w_bytes + T * H * bx + T * H * (4 if inp.dtype == "f32" else 2) + T * Eg * 4 + S * 8
     flops = S_loc * 6 * H * I
     fc1_bytes = A * 2 * I * H * bw + (A * 2 * I * 4 if inp.dtype == "fp8" else 0) \
-        + T * H * bx + S_loc * I * (2 if inp.dtype == "bf16" else 4)
+        + T * H * bx + S_loc * I * (2 if inp.dtype == "bf16" or wo else 4)
     fc1_gbs = fc1_bytes / (fc1_ms * 1e-3) / 1e9
     step_s = ms_per_step * 1e-3
-    wl = cfg["name"] + (f"_ep{args.ep}_rank0" if args.ep > 1 else "") \
+    wl = cfg["name"] + ("_w8a16" if wo else "") + (f"_ep{args.ep}_rank0" if args.ep > 1 else "") \
         + (f"_tp{args.tp}_rank0" if args.tp > 1 else "")
     if M >= 128:  # grouped-GEMM tiles (prefill-sized blocks): FC1 is bound by MFMA
         fc1_flops = S_loc * 2 * I * H * 2
@@ -252,7 +266,8 @@ def main():
     rec = {
         "metric": METRIC, "value": round(T / step_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": inp.dtype,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "w8a16" if wo else inp.dtype,
         "data": "synthetic",
         "config": {"workload": wl, "T": T, "E": E, "H": H, "I": I, "k": k, "block_m": M,
                    "routing": cfg["routing"], "active_experts": A, "seed": 0},
@@ -265,7 +280,7 @@ def main():
         "source_digest": source_digest(),
     }
     if not args.no_cpu_baseline and args.ep == 1 and args.tp == 1:
-        cb, _ = cpu_baseline(inp, args.cpu_seconds)
+        cb, _ = cpu_baseline(inp, args.cpu_seconds, wo)
         rec["cpu_baseline"] = cb
     else:
         rec["cpu_baseline"] = None

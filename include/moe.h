@@ -59,7 +59,7 @@ typedef enum moe_status {
 } moe_status;
 
 /* Element types of the FFN (argument `dtype` of moe_ffn_workspace_bytes). */
-enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1, MOE_DTYPE_FP8 = 2 };
+enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1, MOE_DTYPE_FP8 = 2, MOE_DTYPE_W8A16 = 3 };
 
 /* `flags` bits of the moe_ffn_* calls.
  * Stage bits select which stages run; 0 (no stage bit) runs the whole FFN.
@@ -161,6 +161,7 @@ int moe_default_block_m(int T, int E, int k);
  *   fp8 : h f32 [S, I] | hq e4m3 [S, I] | hs f32 [S] | xq e4m3 [T, H] |
  *         xs f32 [T] | y f32 [S, H]
  *   f32 : h f32 [S, I] | y f32 [S, H]
+ *   w8a16: as bf16
  * h = SiLU(gate) * up and y = FC2 output, both indexed by flat slot
  * s = t*k + j; hq/hs and xq/xs are the quantised h and x with their scales.
  */
@@ -213,6 +214,33 @@ moe_status moe_ffn_fp8(const uint16_t* x, const uint8_t* w1, const float* w1_sca
                        const int32_t* block_expert, const int32_t* num_padded, int T, int E,
                        int H, int I, int k, int block_m, unsigned flags, void* workspace,
                        size_t workspace_bytes, uint16_t* out, moe_stream_t stream);
+
+/*
+ * FFN, weight-only fp8 (W8A16): e4m3fn weight codes with fp32 per-output-row
+ * scales, bf16 activations, fp32 accumulation. The codes are widened on the
+ * fly to bf16 (exact: every e4m3fn value is a bf16 value) and multiplied on
+ * the bf16 matrix cores; no activation is quantised. Passage: "vLLM SM
+ * architecture adaptation", sections 4.2 (weight-only fallback MoE backend)
+ * and 5.2 (one FP8 weight format served either by FP8 matrix units or by
+ * dequantising weights for 16-bit matrix units).
+ *
+ *  x             [T, H] bf16.
+ *  w1            [E, 2I, H] e4m3fn codes, w1_scale [E, 2I] fp32 per output row.
+ *  w2            [E, H, I] e4m3fn codes, w2_scale [E, H] fp32 per output row.
+ *  g = w1_scale[e, n] * sum_c dec(w1[e, n, c]) * x[t, c] (likewise u);
+ *  h = SiLU(g) * u rounded to bf16; y = w2_scale[e, n] * (dec(w2[e, n]) . h)
+ *  rounded to bf16; combine and everything else as moe_ffn_bf16 (same limits,
+ *  scale pointers non-null and 16-byte aligned when T > 0). Workspace:
+ *  moe_ffn_workspace_bytes(..., MOE_DTYPE_W8A16). Every block runs the
+ *  decode-regime streaming kernels (weights are re-read once per 8 tokens of a
+ *  block), so the path is meant for small T.
+ */
+moe_status moe_ffn_w8a16(const uint16_t* x, const uint8_t* w1, const float* w1_scale,
+                         const uint8_t* w2, const float* w2_scale, const int32_t* topk_ids,
+                         const float* topk_weights, const int32_t* sorted_ids,
+                         const int32_t* block_expert, const int32_t* num_padded, int T, int E,
+                         int H, int I, int k, int block_m, unsigned flags, void* workspace,
+                         size_t workspace_bytes, uint16_t* out, moe_stream_t stream);
 
 /*
  * FFN, fp32 throughout (small problems; plain wave-per-output kernels, not a

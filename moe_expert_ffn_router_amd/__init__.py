@@ -11,6 +11,7 @@ The names mirror the C ABI in include/moe.h:
     align_block(topk_ids, E, block_m)                   -> (sorted_ids, block_expert, num_padded)
     ffn_bf16(x, w1, w2, ids, wts, sorted_ids, block_expert, num_padded, block_m, ...) -> out
     ffn_fp8(x, w1, w1_scale, w2, w2_scale, ids, wts, ..., block_m, ...)              -> out
+    ffn_w8a16(x, w1, w1_scale, w2, w2_scale, ids, wts, ..., block_m, ...)            -> out
     ffn_f32(x, w1, w2, ids, wts, ..., block_m, ...)                                 -> out
     forward(x, logits, w1, w2, k, ...)   convenience chaining of the three calls
 """
@@ -26,14 +27,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK = 0
-MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_FP8 = 0, 1, 2
+MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_FP8, MOE_DTYPE_W8A16 = 0, 1, 2, 3
 STAGE_FC1, STAGE_FC2, STAGE_COMBINE = 1 << 0, 1 << 1, 1 << 2
 NO_XCD_REMAP = 1 << 8
 ABI_VERSION = 1
 
 EXPORTS = ("moe_status_str", "moe_abi_version", "moe_route_topk", "moe_align_capacity",
            "moe_align_block", "moe_route_align", "moe_default_block_m",
-           "moe_ffn_workspace_bytes", "moe_ffn_bf16", "moe_ffn_fp8", "moe_ffn_f32")
+           "moe_ffn_workspace_bytes", "moe_ffn_bf16", "moe_ffn_fp8", "moe_ffn_w8a16",
+           "moe_ffn_f32")
 
 
 class MoEError(RuntimeError):
@@ -73,6 +75,8 @@ def _load() -> ctypes.CDLL:
     lib.moe_ffn_f32.argtypes = [P, P, P] + ffn_tail
     lib.moe_ffn_fp8.restype = I
     lib.moe_ffn_fp8.argtypes = [P, P, P, P, P] + ffn_tail
+    lib.moe_ffn_w8a16.restype = I
+    lib.moe_ffn_w8a16.argtypes = [P, P, P, P, P] + ffn_tail
     if lib.moe_abi_version() != ABI_VERSION:
         raise ImportError(f"libmoe ABI {lib.moe_abi_version()} != binding ABI {ABI_VERSION}")
     return lib
@@ -219,10 +223,8 @@ def ffn_bf16(x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert, num_pa
     return out
 
 
-def ffn_fp8(x, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids, block_expert,
-            num_padded, block_m: int, flags: int = 0, workspace=None, out=None, stream=None):
-    """moe_ffn_fp8: x [T,H] bfloat16; w1 [E,2I,H], w2 [E,H,I] e4m3fn codes (uint8 or
-    float8_e4m3fn) with float32 per-output-row scales -> out [T,H] bfloat16."""
+def _ffn_scaled(fn, dtype, x, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids,
+                block_expert, num_padded, block_m, flags, workspace, out, stream):
     fp8 = (torch.uint8, torch.float8_e4m3fn)
     _need(x, "x", (torch.bfloat16,))
     _need(w1, "w1", fp8, x.device)
@@ -234,15 +236,32 @@ def ffn_fp8(x, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids, b
     E, I2, _ = w1.shape
     k = topk_ids.shape[1]
     if workspace is None:
-        workspace = alloc_workspace(T, E, H, I2 // 2, k, block_m, MOE_DTYPE_FP8, x.device)
+        workspace = alloc_workspace(T, E, H, I2 // 2, k, block_m, dtype, x.device)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
-    _check(lib.moe_ffn_fp8(_ptr(x), _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale),
-                           _ptr(topk_ids), _ptr(topk_weights), _ptr(sorted_ids),
-                           _ptr(block_expert), _ptr(num_padded), T, E, H, I2 // 2, k, block_m,
-                           flags, _ptr(workspace), workspace.numel(), _ptr(out),
-                           _stream(stream)))
+    _check(fn(_ptr(x), _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale), _ptr(topk_ids),
+              _ptr(topk_weights), _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded), T, E,
+              H, I2 // 2, k, block_m, flags, _ptr(workspace), workspace.numel(), _ptr(out),
+              _stream(stream)))
     return out
+
+
+def ffn_fp8(x, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids, block_expert,
+            num_padded, block_m: int, flags: int = 0, workspace=None, out=None, stream=None):
+    """moe_ffn_fp8: x [T,H] bfloat16; w1 [E,2I,H], w2 [E,H,I] e4m3fn codes (uint8 or
+    float8_e4m3fn) with float32 per-output-row scales -> out [T,H] bfloat16."""
+    return _ffn_scaled(lib.moe_ffn_fp8, MOE_DTYPE_FP8, x, w1, w1_scale, w2, w2_scale, topk_ids,
+                       topk_weights, sorted_ids, block_expert, num_padded, block_m, flags,
+                       workspace, out, stream)
+
+
+def ffn_w8a16(x, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids, block_expert,
+              num_padded, block_m: int, flags: int = 0, workspace=None, out=None, stream=None):
+    """moe_ffn_w8a16: weight-only fp8. Arguments as ffn_fp8; activations stay
+    bfloat16 -> out [T,H] bfloat16."""
+    return _ffn_scaled(lib.moe_ffn_w8a16, MOE_DTYPE_W8A16, x, w1, w1_scale, w2, w2_scale,
+                       topk_ids, topk_weights, sorted_ids, block_expert, num_padded, block_m,
+                       flags, workspace, out, stream)
 
 
 def ffn_f32(x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert, num_padded,
@@ -267,16 +286,18 @@ def ffn_f32(x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert, num_pad
 
 
 def forward(x, logits, w1, w2, k: int, block_m: Optional[int] = None, renormalize: bool = False,
-            w1_scale=None, w2_scale=None, flags: int = 0, stream=None):
-    """route_align -> ffn_{f32,bf16,fp8}, dtype taken from w1; block_m defaults
-    to moe_default_block_m."""
+            w1_scale=None, w2_scale=None, flags: int = 0, weight_only: bool = False,
+            stream=None):
+    """route_align -> ffn_{f32,bf16,fp8,w8a16}, dtype taken from w1 (fp8 codes run
+    ffn_w8a16 with ``weight_only``, else ffn_fp8); block_m defaults to
+    moe_default_block_m."""
     E = w1.shape[0]
     if block_m is None:
         block_m = default_block_m(x.shape[0], E, k)
     ids, wts, sorted_ids, block_expert, num_padded = route_align(logits, k, block_m, renormalize,
                                                                  stream=stream)
     if w1.dtype in (torch.uint8, torch.float8_e4m3fn):
-        return ffn_fp8(x, w1, w1_scale, w2, w2_scale, ids, wts, sorted_ids, block_expert,
+        return (ffn_w8a16 if weight_only else ffn_fp8)(x, w1, w1_scale, w2, w2_scale, ids, wts, sorted_ids, block_expert,
                        num_padded, block_m, flags, stream=stream)
     if w1.dtype == torch.bfloat16:
         return ffn_bf16(x, w1, w2, ids, wts, sorted_ids, block_expert, num_padded, block_m,

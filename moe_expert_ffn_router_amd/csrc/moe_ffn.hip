@@ -587,6 +587,161 @@ __device__ __forceinline__ void fc2_hot_pass(const Fc2Args& p, int e, int r, int
   }
 }
 
+// ----------------------------------------- W8A16: e4m3 weights, bf16 x ---
+// Weight-only FP8 ("vLLM SM architecture adaptation", sections 4.2 and 5.2:
+// FP8 weights dequantised on the fly for 16-bit matrix cores). A tile's
+// codes stream as in the cold path (half-split rows, whole 128-byte lines,
+// non-temporal): a lane's 16 codes of one line are converted to two bf16x8
+// MFMA fragments by v_cvt_pk_f32_fp8 (exact: every e4m3 value is a bf16
+// value) and paired with the 16 bf16 activations of the same k. The
+// per-output-channel scale multiplies the fp32 sum once.
+
+// 16 e4m3 codes (byte order = k order) -> two bf16x8 fragments.
+__device__ __forceinline__ void e4m3x16_to_bf16(const u32x4& q, bf16x8& f0, bf16x8& f1) {
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[i], false);  // codes 4i, 4i+1
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[i], true);   // codes 4i+2, 4i+3
+    // exact values: the bf16 pattern is the float's upper half
+    w[2 * i] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xffff0000u);
+    w[2 * i + 1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xffff0000u);
+  }
+  f0 = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+  f1 = __builtin_bit_cast(bf16x8, u32x4{w[4], w[5], w[6], w[7]});
+}
+
+template <int U>
+struct W8Group {
+  u32x4 p[U], q[U];     // 16 codes of tiles P and Q per chunk
+  u32x4 b0[U], b1[U];   // the 16 matching bf16 activations
+  __device__ __forceinline__ void issue(const uint8_t* __restrict__ ap,
+                                        const uint8_t* __restrict__ aq,
+                                        const uint8_t* __restrict__ bp, bool ok, int c) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      p[u] = __builtin_nontemporal_load((const u32x4*)(ap + (size_t)(c + u) * 128));
+      q[u] = __builtin_nontemporal_load((const u32x4*)(aq + (size_t)(c + u) * 128));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      b0[u] = b1[u] = u32x4{0, 0, 0, 0};
+      if (ok) {
+        b0[u] = *(const u32x4*)(bp + (size_t)(c + u) * 256);
+        b1[u] = *(const u32x4*)(bp + (size_t)(c + u) * 256 + 16);
+      }
+    }
+  }
+  __device__ __forceinline__ void compute(f32x4& accp, f32x4& accq) const {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bf16x8 x0 = __builtin_bit_cast(bf16x8, b0[u]), x1 = __builtin_bit_cast(bf16x8, b1[u]);
+      bf16x8 f0, f1;
+      e4m3x16_to_bf16(p[u], f0, f1);
+      accp = mfma_bf16(f0, x0, accp);
+      accp = mfma_bf16(f1, x1, accp);
+      e4m3x16_to_bf16(q[u], f0, f1);
+      accq = mfma_bf16(f0, x0, accq);
+      accq = mfma_bf16(f1, x1, accq);
+    }
+  }
+};
+
+// accp/accq += codes of tiles P/Q (ap, aq: this lane's 16-byte piece of each
+// 128-byte line) . bf16 token tile (bp: the matching 32 bytes of each
+// 256-byte activation chunk) over kbytes = K bytes of codes per row.
+template <int U>
+__device__ __forceinline__ void w8_kloop(const uint8_t* __restrict__ ap,
+                                         const uint8_t* __restrict__ aq,
+                                         const uint8_t* __restrict__ bp, bool ok, int kbytes,
+                                         f32x4& accp, f32x4& accq) {
+  const int nch = kbytes / 128;
+  const int ngrp = nch / U;
+  W8Group<U> g0, g1;
+  if (ngrp > 0) g0.issue(ap, aq, bp, ok, 0);
+  int g = 0;
+  for (; g + 1 < ngrp; g += 2) {
+    g1.issue(ap, aq, bp, ok, (g + 1) * U);
+    g0.compute(accp, accq);
+    if (g + 2 < ngrp) g0.issue(ap, aq, bp, ok, (g + 2) * U);
+    g1.compute(accp, accq);
+  }
+  if (g < ngrp) g0.compute(accp, accq);
+  for (int c = ngrp * U; c < nch; ++c) {
+    W8Group<1> one;
+    one.issue(ap + (size_t)c * 128, aq + (size_t)c * 128, bp + (size_t)c * 256, ok, 0);
+    one.compute(accp, accq);
+  }
+}
+
+// Byte offsets of this lane's piece in the half-split layout: codes at
+// half*64 + kgroup*16 of each 128-byte line, activations at twice that.
+__device__ __forceinline__ int w8_code_off() { return half_split_off(); }
+__device__ __forceinline__ int w8_act_off() { return 2 * half_split_off(); }
+
+constexpr int kW8U = 2;  // code chunks per pipeline group
+
+// Cold FC1 tile r of the W8A16 path (layout as fc1_cold).
+__device__ __forceinline__ void fc1_cold_w8(const Fc1Args& p, int e, int r, int slot) {
+  const int lane = threadIdx.x & 63;
+  const size_t rowq = (size_t)p.H;      // code bytes per weight row
+  const size_t rowx = (size_t)p.H * 2;  // bytes per activation row
+  const uint8_t* w = (const uint8_t*)p.w1 + (size_t)e * 2 * p.I * rowq;
+  const uint8_t* ap = w + (size_t)(r * 8 + (lane & 7)) * rowq + w8_code_off();
+  const uint8_t* aq = w + (size_t)(p.I + r * 8 + (lane & 7)) * rowq + w8_code_off();
+  const bool ok = slot < p.S;
+  const uint8_t* bp = (const uint8_t*)p.x + (size_t)(ok ? slot / p.k : 0) * rowx + w8_act_off();
+  const bool holder = (lane & 8) == 0 && lane < 32;
+  const int col = r * 8 + 4 * (lane >> 4);
+  f32x4 sg = {1.f, 1.f, 1.f, 1.f}, su = sg;
+  if (holder) {
+    sg = *(const f32x4*)(p.w1s + (size_t)e * 2 * p.I + col);
+    su = *(const f32x4*)(p.w1s + (size_t)e * 2 * p.I + p.I + col);
+  }
+  f32x4 accp = {}, accq = {};
+  w8_kloop<kW8U>(ap, aq, bp, ok, (int)rowq, accp, accq);
+  f32x4 g = diag_sum(accp), u = diag_sum(accq);
+  if (holder && ok) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      g[i] *= sg[i];
+      u[i] *= su[i];
+    }
+    store_h<false>(p, slot, col, g, u);
+  }
+}
+
+// Cold FC2 tile r of the W8A16 path (layout as fc2_cold).
+__device__ __forceinline__ void fc2_cold_w8(const Fc2Args& p, int e, int r, int slot) {
+  const int lane = threadIdx.x & 63;
+  const size_t rowq = (size_t)p.I;
+  const size_t rowh = (size_t)p.I * 2;
+  const uint8_t* w = (const uint8_t*)p.w2 + (size_t)e * p.H * rowq;
+  const uint8_t* ap = w + (size_t)(r * 16 + (lane & 7)) * rowq + w8_code_off();
+  const uint8_t* aq = w + (size_t)(r * 16 + 8 + (lane & 7)) * rowq + w8_code_off();
+  const bool ok = slot < p.S;
+  const uint8_t* bp = (const uint8_t*)p.h + (size_t)(ok ? slot : 0) * rowh + w8_act_off();
+  const bool holder = (lane & 8) == 0 && lane < 32;
+  const int row = r * 16 + 4 * (lane >> 4);
+  f32x4 sp = {1.f, 1.f, 1.f, 1.f}, sq = sp;
+  if (holder) {
+    sp = *(const f32x4*)(p.w2s + (size_t)e * p.H + row);
+    sq = *(const f32x4*)(p.w2s + (size_t)e * p.H + row + 8);
+  }
+  f32x4 accp = {}, accq = {};
+  w8_kloop<kW8U>(ap, aq, bp, ok, (int)rowq, accp, accq);
+  f32x4 vp = diag_sum(accp), vq = diag_sum(accq);
+  if (holder && ok) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      vp[i] *= sp[i];
+      vq[i] *= sq[i];
+    }
+    store_y(p, slot, row, vp);
+    store_y(p, slot, row + 8, vq);
+  }
+}
+
 // ------------------------------------------------- persistent kernels ---
 
 // Work list: (block, quad of 4 consecutive tiles), one quad per workgroup
@@ -681,6 +836,22 @@ __global__ __launch_bounds__(256) void fc2_kernel(Fc2Args p) {
   run_quads<FP8, HOT, HOT, Fc2Args, fc2_cold<FP8, cold_u<FP8, HOT>()>, fc2_hot_pass<FP8, 1>,
             fc2_hot_pass<FP8, 2>,
             fc2_hot_pass<FP8, 3>, fc2_hot_pass<FP8, 4>>(p, p.H >> 4, lds);
+}
+
+// W8A16 runs every block by cold passes of 8 tokens (the weights stream once
+// per 8 tokens of a block): a decode path.
+__global__ __launch_bounds__(256) void fc1_w8a16_kernel(Fc1Args p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[16];
+  run_quads<false, false, false, Fc1Args, fc1_cold_w8, fc1_hot_pass<false, 1>,
+            fc1_hot_pass<false, 2>, fc1_hot_pass<false, 3>, fc1_hot_pass<false, 4>>(p, p.I >> 3,
+                                                                                     lds);
+}
+
+__global__ __launch_bounds__(256) void fc2_w8a16_kernel(Fc2Args p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[16];
+  run_quads<false, false, false, Fc2Args, fc2_cold_w8, fc2_hot_pass<false, 1>,
+            fc2_hot_pass<false, 2>, fc2_hot_pass<false, 3>, fc2_hot_pass<false, 4>>(p, p.H >> 4,
+                                                                                     lds);
 }
 
 // ------------------------------------------- dense tiles (big blocks) ---
@@ -1395,6 +1566,30 @@ hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_COMBINE) return launch_combine(p, L, MOE_DTYPE_FP8, stream);
+  return hipSuccess;
+}
+
+hipError_t launch_ffn_w8a16(const FfnProblem& p, hipStream_t stream) {
+  const FfnWorkspace L = ffn_workspace_layout(p.T, p.H, p.I, p.k, MOE_DTYPE_BF16);
+  const unsigned st = stages(p.flags);
+  const int remap = (p.flags & MOE_FFN_NO_XCD_REMAP) ? 0 : 1;
+  const int S = p.T * p.k, log2m = ilog2(p.block_m);
+  void* h = (char*)p.workspace + L.h_off;
+  void* y = (char*)p.workspace + L.y_off;
+  hipError_t err;
+  if (st & MOE_FFN_STAGE_FC1) {
+    Fc1Args a{p.x, nullptr, p.w1, p.w1_scale, p.sorted_ids, p.block_expert, p.num_padded,
+              p.H, p.I, p.k, S, log2m, remap, h, nullptr};
+    fc1_w8a16_kernel<<<persistent_grid(fc1_w8a16_kernel, 10), 256, 0, stream>>>(a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (st & MOE_FFN_STAGE_FC2) {
+    Fc2Args a{h, nullptr, p.w2, p.w2_scale, p.sorted_ids, p.block_expert, p.num_padded,
+              p.H, p.I, S, log2m, remap, y, 1, nullptr};
+    fc2_w8a16_kernel<<<persistent_grid(fc2_w8a16_kernel, 11), 256, 0, stream>>>(a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (st & MOE_FFN_STAGE_COMBINE) return launch_combine(p, L, MOE_DTYPE_BF16, stream);
   return hipSuccess;
 }
 

@@ -55,6 +55,7 @@ struct FfnProblem {
 
 hipError_t launch_ffn_bf16(const FfnProblem& p, hipStream_t stream);
 hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream);
+hipError_t launch_ffn_w8a16(const FfnProblem& p, hipStream_t stream);
 hipError_t launch_ffn_f32(const FfnProblem& p, hipStream_t stream);
 
 }  // namespace moe

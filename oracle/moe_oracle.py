@@ -44,7 +44,7 @@ import numpy as np
 __all__ = [
     "bf16_bits_to_f64", "e4m3fn_decode", "e4m3fn_encode", "E4M3FN_VALUES",
     "route", "align", "align_capacity", "swiglu_expert", "ffn", "quant_rows_e4m3",
-    "ffn_fp8", "normwise_rel_err",
+    "ffn_fp8", "dequant_rows", "ffn_w8a16", "normwise_rel_err",
 ]
 
 # ---------------------------------------------------------------- formats ---
@@ -274,6 +274,29 @@ def ffn_fp8(x_bits: np.ndarray, get_w1q: Callable[[int], np.ndarray], w1_scale: 
     for j in range(k):
         out += w[:, j:j + 1] * Y[:, j]
     return out
+
+
+# ------------------------------------------------------- weight-only FP8 ---
+
+def dequant_rows(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """W^[n, c] = dec(codes[n, c]) * scale[n], float64: one FP8 weight format
+    with a per-output-channel scale, widened for 16-bit matrix units
+    ("vLLM SM architecture adaptation", section 5.2)."""
+    return e4m3fn_decode(codes) * np.asarray(scale, dtype=np.float64)[:, None]
+
+
+def ffn_w8a16(x_bits: np.ndarray, get_w1q: Callable[[int], np.ndarray], w1_scale: np.ndarray,
+              get_w2q: Callable[[int], np.ndarray], w2_scale: np.ndarray, ids: np.ndarray,
+              weights: np.ndarray, tokens: Optional[Iterable[int]] = None,
+              num_experts: Optional[int] = None) -> np.ndarray:
+    """Weight-only FP8 (W8A16) variant: the weight-only fallback MoE backend of
+    "vLLM SM architecture adaptation" (sections 4.2 and 5.2). The FFN of ``ffn``
+    on the bfloat16 activations (``x_bits``) with each expert's weights
+    dequantised by ``dequant_rows``; no activation is quantised."""
+    x = bf16_bits_to_f64(x_bits)
+    return ffn(x, lambda e: dequant_rows(get_w1q(e), w1_scale[e]),
+               lambda e: dequant_rows(get_w2q(e), w2_scale[e]), ids, weights, tokens,
+               num_experts)
 
 
 # ------------------------------------------------------------- comparison ---

@@ -229,3 +229,53 @@ def test_ffn_fp8_quantises_h_per_slot_on_grid():
         b = np.float32(np.max(np.abs(row)).astype(np.float32) / np.float32(448.0))
         r = np.abs(row) / np.float64(b)
         assert np.all(np.min(np.abs(r[:, None] - grid[None, :]), axis=1) <= 1e-5 * np.maximum(r, 1))
+
+
+def _w8a16_case(rng, T, E, H, I):
+    w1q = rng.integers(0, 256, size=(E, 2 * I, H)).astype(np.uint8)
+    w2q = rng.integers(0, 256, size=(E, H, I)).astype(np.uint8)
+    w1q[(w1q & 0x7F) == 0x7F] = 0x3A                      # no NaN codes
+    w2q[(w2q & 0x7F) == 0x7F] = 0xB9
+    w1q = np.where(np.abs(oracle.e4m3fn_decode(w1q)) > 8, 0x34, w1q).astype(np.uint8)
+    w2q = np.where(np.abs(oracle.e4m3fn_decode(w2q)) > 8, 0xB4, w2q).astype(np.uint8)
+    s1 = rng.uniform(0.05, 0.4, size=(E, 2 * I)).astype(np.float32)
+    s2 = rng.uniform(0.05, 0.4, size=(E, H)).astype(np.float32)
+    x_bits = (torch.randn(T, H, generator=torch.Generator().manual_seed(int(rng.integers(99))))
+              .to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    return x_bits, w1q, s1, w2q, s2
+
+
+@pytest.mark.parametrize("T,E,H,I,k", [(2, 3, 5, 3, 2), (3, 2, 4, 6, 1)])
+def test_ffn_w8a16_matches_brute_force_with_library_decode(T, E, H, I, k):
+    # weights decoded by torch's float8_e4m3fn cast and scaled per output row by
+    # hand (H != 2I, so a per-column scale cannot pass), x taken from its bf16
+    # bits by torch, then the pure-Python MoE of the plain FFN
+    rng = np.random.default_rng(T * 13 + H)
+    x_bits, w1q, s1, w2q, s2 = _w8a16_case(rng, T, E, H, I)
+    ids, w = oracle.route(rng.standard_normal((T, E)).astype(np.float32), k)
+    got = oracle.ffn_w8a16(x_bits, lambda e: w1q[e], s1, lambda e: w2q[e], s2, ids, w)
+    dec = lambda q: torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    W1 = [[[float(dec(w1q[e])[n][c]) * float(s1[e][n]) for c in range(H)] for n in range(2 * I)]
+          for e in range(E)]
+    W2 = [[[float(dec(w2q[e])[n][c]) * float(s2[e][n]) for c in range(I)] for n in range(H)]
+          for e in range(E)]
+    X = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).tolist()
+    ref = brute_moe(X, W1, W2, ids.tolist(), w.tolist())
+    assert np.allclose(got, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_ffn_w8a16_scale_roles():
+    # doubling the FC2 row scales or the up-row scales doubles the output (y and
+    # h are linear in them); doubling the gate-row scales does not (SiLU)
+    rng = np.random.default_rng(21)
+    T, E, H, I, k = 3, 2, 8, 4, 2
+    x_bits, w1q, s1, w2q, s2 = _w8a16_case(rng, T, E, H, I)
+    ids, w = oracle.route(rng.standard_normal((T, E)).astype(np.float32), k)
+    f = lambda a, b: oracle.ffn_w8a16(x_bits, lambda e: w1q[e], a, lambda e: w2q[e], b, ids, w)
+    base = f(s1, s2)
+    up2 = s1.copy(); up2[:, I:] *= 2
+    gate2 = s1.copy(); gate2[:, :I] *= 2
+    assert np.allclose(f(s1, s2 * 2), 2 * base, rtol=1e-12, atol=0)
+    assert np.allclose(f(up2, s2), 2 * base, rtol=1e-12, atol=0)
+    assert not np.allclose(f(gate2, s2), 2 * base, rtol=1e-3)
+    assert not np.allclose(f(gate2, s2), base, rtol=1e-3)

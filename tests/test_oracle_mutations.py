@@ -125,11 +125,30 @@ def _ffn_fp8_no_x_quant(x_bits, g1, s1, g2, s2, ids, w, tokens=None):
         om.e4m3fn_decode = dec
 
 
+def _dequant_unscaled(codes, scale):
+    return om.e4m3fn_decode(codes)
+
+
+def _dequant_column_scale(codes, scale):
+    c = om.e4m3fn_decode(codes)
+    s = np.resize(np.asarray(scale, np.float64), c.shape[1])
+    return c * s[None, :]
+
+
+def _ffn_w8a16_quantises_x(x_bits, g1, s1, g2, s2, ids, w, tokens=None, num_experts=None):
+    x = om.bf16_bits_to_f64(x_bits).astype(np.float32)
+    q, a = om.quant_rows_e4m3(x)
+    xq = (om.e4m3fn_decode(q) * a[:, None]).astype(np.float32)
+    return MUT_ORIG_FFN_W8A16((xq.view(np.uint32) >> 16).astype(np.uint16), g1, s1, g2, s2, ids,
+                              w, tokens, num_experts)
+
+
 MUT_ORIG_ROUTE = om.route
 MUT_ORIG_SWIGLU = om.swiglu_expert
 MUT_ORIG_ALIGN = om.align
 MUT_ORIG_ENC = om.e4m3fn_encode
 MUT_ORIG_FFN_FP8 = om.ffn_fp8
+MUT_ORIG_FFN_W8A16 = om.ffn_w8a16
 
 MUTATIONS = [
     ("route", _route_ascending, [lambda: R.test_topk_ids_match_brute_force(7, 64, 8)]),
@@ -143,6 +162,12 @@ MUTATIONS = [
     ("e4m3fn_encode", _encode_ties_away, [FM.test_e4m3fn_encode_midpoints_go_to_even_code]),
     ("ffn_fp8", _ffn_fp8_no_h_quant, [F.test_ffn_fp8_quantises_h_per_slot_on_grid]),
     ("ffn_fp8", _ffn_fp8_no_x_quant, [F.test_ffn_fp8_quantises_x_per_token]),
+    ("dequant_rows", _dequant_unscaled,
+     [lambda: F.test_ffn_w8a16_matches_brute_force_with_library_decode(2, 3, 5, 3, 2)]),
+    ("dequant_rows", _dequant_column_scale,
+     [lambda: F.test_ffn_w8a16_matches_brute_force_with_library_decode(3, 2, 4, 6, 1)]),
+    ("ffn_w8a16", _ffn_w8a16_quantises_x,
+     [lambda: F.test_ffn_w8a16_matches_brute_force_with_library_decode(2, 3, 5, 3, 2)]),
 ]
 
 
