@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--weight-only", action="store_true",
                     help="FP8 workloads: run the weight-only (W8A16) FFN on the same codes "
                          "and scales, activations kept in bf16")
+    ap.add_argument("--block-fp8", action="store_true",
+                    help="FP8 workloads: weights quantised per 128x128 block (same master "
+                         "weights), activations per 128-element group")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
@@ -78,6 +81,7 @@ def measured_traffic(kernel: str, workload: str):
 
 
 def cpu_baseline(inp, target_s: float, weight_only: bool = False):
+    # inp.dtype "fp8_block" selects the block-scaled oracle
     """The CPU oracle as it stands, on the first n tokens of the same workload;
     n grows until about target_s seconds of oracle work have been timed."""
     import numpy as np
@@ -105,7 +109,11 @@ def cpu_baseline(inp, target_s: float, weight_only: bool = False):
         toks = list(range(n_next))
         t0 = time.perf_counter()
         ids, w = oracle.route(logits[:n_next], inp.k)
-        if inp.dtype == "fp8" and weight_only:
+        if inp.dtype == "fp8_block":
+            sample_out = oracle.ffn_fp8_block(x_bits[:n_next], w1h.__getitem__,
+                                              inp.host_w1_scale(), w2h.__getitem__,
+                                              inp.host_w2_scale(), ids, w, toks)
+        elif inp.dtype == "fp8" and weight_only:
             sample_out = oracle.ffn_w8a16(x_bits[:n_next], w1h.__getitem__,
                                           inp.host_w1_scale(), w2h.__getitem__,
                                           inp.host_w2_scale(), ids, w, toks)
@@ -150,7 +158,11 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     cfg = CONFIGS[args.config]
-    inp = config_inputs(args.config, device="cuda")
+    if (args.weight_only or args.block_fp8) and CONFIGS[args.config]["dtype"] != "fp8":
+        sys.exit("bench.py: --weight-only / --block-fp8 need an FP8 workload (config 3)")
+    if args.weight_only and args.block_fp8:
+        sys.exit("bench.py: --weight-only and --block-fp8 are separate measurements")
+    inp = config_inputs(args.config, device="cuda", dtype="fp8_block" if args.block_fp8 else None)
     T, E, H, I, k = inp.T, inp.E, inp.H, inp.I, inp.k
     Eg = E                                   # experts of the whole layer (routing)
     w1, w2, s1, s2 = inp.w1, inp.w2, inp.w1_scale, inp.w2_scale
@@ -168,10 +180,10 @@ def main():
     M = args.block_m or moe.default_block_m(T, E, k)
     S = T * k
     dev = inp.x.device
-    if args.weight_only and inp.dtype != "fp8":
-        sys.exit("bench.py: --weight-only needs an FP8 workload (config 3)")
     wo = args.weight_only
-    dt_code = {"f32": moe.MOE_DTYPE_F32, "bf16": moe.MOE_DTYPE_BF16, "fp8": moe.MOE_DTYPE_FP8}[inp.dtype]
+    blk = args.block_fp8
+    dt_code = {"f32": moe.MOE_DTYPE_F32, "bf16": moe.MOE_DTYPE_BF16, "fp8": moe.MOE_DTYPE_FP8,
+               "fp8_block": moe.MOE_DTYPE_FP8_BLOCK}[inp.dtype]
     if wo:
         dt_code = moe.MOE_DTYPE_W8A16
 
@@ -188,7 +200,9 @@ def main():
 
     def ffn(flags):
         f = flags | args.flags
-        if wo:
+        if blk:
+            moe.ffn_fp8_block(inp.x, w1, s1, w2, s2, ids, wts, sid, be, npad, M, f, ws, out)
+        elif wo:
             moe.ffn_w8a16(inp.x, w1, s1, w2, s2, ids, wts, sid, be, npad, M, f, ws, out)
         elif inp.dtype == "fp8":
             moe.ffn_fp8(inp.x, w1, s1, w2, s2, ids, wts, sid, be, npad, M, f, ws, out)
@@ -237,17 +251,20 @@ def main():
     # algorithmic work (active experts from this run's routing)
     ids_h = ids.cpu().numpy()
     A = int(np.unique(ids_h[ids_h < E]).size)       # active local experts
-    bw = {"f32": 4, "bf16": 2, "fp8": 1}[inp.dtype]
-    bx = {"f32": 4, "bf16": 2, "fp8": 2}[inp.dtype]
+    bw = {"f32": 4, "bf16": 2, "fp8": 1, "fp8_block": 1}[inp.dtype]
+    bx = {"f32": 4, "bf16": 2, "fp8": 2, "fp8_block": 2}[inp.dtype]
     S_loc = int((ids_h < E).sum())                   # slots this GPU computes
-    w_bytes = A * 3 * I * H * bw + (A * (2 * I + H) * 4 if inp.dtype == "fp8" else 0)
+    # weight scales per expert: per row (fp8) or per 128x128 block (fp8_block)
+    sc1 = {"fp8": 2 * I, "fp8_block": (2 * I // 128) * (H // 128)}.get(inp.dtype, 0) * 4
+    sc2 = {"fp8": H, "fp8_block": (H // 128) * (I // 128)}.get(inp.dtype, 0) * 4
+    w_bytes = A * 3 * I * H * bw + A * (sc1 + sc2)
     layer_bytes = w_bytes + T * H * bx + T * H * (4 if inp.dtype == "f32" else 2) + T * Eg * 4 + S * 8
     flops = S_loc * 6 * H * I
-    fc1_bytes = A * 2 * I * H * bw + (A * 2 * I * 4 if inp.dtype == "fp8" else 0) \
+    fc1_bytes = A * 2 * I * H * bw + A * sc1 \
         + T * H * bx + S_loc * I * (2 if inp.dtype == "bf16" or wo else 4)
     fc1_gbs = fc1_bytes / (fc1_ms * 1e-3) / 1e9
     step_s = ms_per_step * 1e-3
-    wl = cfg["name"] + ("_w8a16" if wo else "") + (f"_ep{args.ep}_rank0" if args.ep > 1 else "") \
+    wl = cfg["name"] + ("_w8a16" if wo else "") + ("_block128" if blk else "") + (f"_ep{args.ep}_rank0" if args.ep > 1 else "") \
         + (f"_tp{args.tp}_rank0" if args.tp > 1 else "")
     if M >= 128:  # grouped-GEMM tiles (prefill-sized blocks): FC1 is bound by MFMA
         fc1_flops = S_loc * 2 * I * H * 2

@@ -59,7 +59,13 @@ typedef enum moe_status {
 } moe_status;
 
 /* Element types of the FFN (argument `dtype` of moe_ffn_workspace_bytes). */
-enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1, MOE_DTYPE_FP8 = 2, MOE_DTYPE_W8A16 = 3 };
+enum {
+  MOE_DTYPE_F32 = 0,
+  MOE_DTYPE_BF16 = 1,
+  MOE_DTYPE_FP8 = 2,
+  MOE_DTYPE_W8A16 = 3,
+  MOE_DTYPE_FP8_BLOCK = 4
+};
 
 /* `flags` bits of the moe_ffn_* calls.
  * Stage bits select which stages run; 0 (no stage bit) runs the whole FFN.
@@ -162,6 +168,7 @@ int moe_default_block_m(int T, int E, int k);
  *         xs f32 [T] | y f32 [S, H]
  *   f32 : h f32 [S, I] | y f32 [S, H]
  *   w8a16: as bf16
+ *   fp8_block: as fp8, with hs f32 [S, I/128] and xs f32 [T, H/128]
  * h = SiLU(gate) * up and y = FC2 output, both indexed by flat slot
  * s = t*k + j; hq/hs and xq/xs are the quantised h and x with their scales.
  */
@@ -214,6 +221,37 @@ moe_status moe_ffn_fp8(const uint16_t* x, const uint8_t* w1, const float* w1_sca
                        const int32_t* block_expert, const int32_t* num_padded, int T, int E,
                        int H, int I, int k, int block_m, unsigned flags, void* workspace,
                        size_t workspace_bytes, uint16_t* out, moe_stream_t stream);
+
+/*
+ * FFN, block-scaled OCP fp8 e4m3fn: 128 x 128 weight blocks and 1 x 128
+ * activation groups, each with an fp32 scale, fp32 accumulation. Passage:
+ * "vLLM SM architecture adaptation", sections 4.1 (block FP8 MoE backends),
+ * 4.2 (block-wise FP8 grouped GEMM) and the runtime selection-flow figure of
+ * section 9 (block-wise FP8 dequantisation inside the GEMM loop); the
+ * 128-element block edge follows the 128-wide tiles named in that figure.
+ *
+ *  x             [T, H] bf16; quantised inside per (token, group of 128
+ *                columns): a = absmax/448 (fp32; 1 for an all-zero group),
+ *                code = e4m3fn_rne_sat(x / a).
+ *  w1            [E, 2I, H] e4m3fn codes; w1_scale [E, 2I/128, H/128] fp32,
+ *                one per 128 x 128 block (row block, column block).
+ *  w2            [E, H, I] e4m3fn codes; w2_scale [E, H/128, I/128] fp32.
+ *  For output row n and K-block c the partial sum over the block's 128 codes
+ *  is multiplied by w_scale[e, n/128, c] * a[row, c] and added in fp32:
+ *  g, u -> h = SiLU(g) * u in fp32, quantised per (slot, group of 128) the
+ *  same way, -> y; combine as moe_ffn_fp8. Other arguments and limits as
+ *  moe_ffn_bf16 (H and I multiples of 128); scale pointers non-null and
+ *  4-byte aligned when T > 0. Workspace: moe_ffn_workspace_bytes(...,
+ *  MOE_DTYPE_FP8_BLOCK). Every block runs the decode-regime streaming
+ *  kernels (weights re-read once per 8 tokens of a block): meant for small T.
+ */
+moe_status moe_ffn_fp8_block(const uint16_t* x, const uint8_t* w1, const float* w1_scale,
+                             const uint8_t* w2, const float* w2_scale, const int32_t* topk_ids,
+                             const float* topk_weights, const int32_t* sorted_ids,
+                             const int32_t* block_expert, const int32_t* num_padded, int T,
+                             int E, int H, int I, int k, int block_m, unsigned flags,
+                             void* workspace, size_t workspace_bytes, uint16_t* out,
+                             moe_stream_t stream);
 
 /*
  * FFN, weight-only fp8 (W8A16): e4m3fn weight codes with fp32 per-output-row

@@ -12,6 +12,7 @@ The names mirror the C ABI in include/moe.h:
     ffn_bf16(x, w1, w2, ids, wts, sorted_ids, block_expert, num_padded, block_m, ...) -> out
     ffn_fp8(x, w1, w1_scale, w2, w2_scale, ids, wts, ..., block_m, ...)              -> out
     ffn_w8a16(x, w1, w1_scale, w2, w2_scale, ids, wts, ..., block_m, ...)            -> out
+    ffn_fp8_block(x, w1, w1_scale, w2, w2_scale, ids, wts, ..., block_m, ...)        -> out
     ffn_f32(x, w1, w2, ids, wts, ..., block_m, ...)                                 -> out
     forward(x, logits, w1, w2, k, ...)   convenience chaining of the three calls
 """
@@ -27,7 +28,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK = 0
-MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_FP8, MOE_DTYPE_W8A16 = 0, 1, 2, 3
+MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_FP8, MOE_DTYPE_W8A16, MOE_DTYPE_FP8_BLOCK = 0, 1, 2, 3, 4
 STAGE_FC1, STAGE_FC2, STAGE_COMBINE = 1 << 0, 1 << 1, 1 << 2
 NO_XCD_REMAP = 1 << 8
 ABI_VERSION = 1
@@ -35,7 +36,7 @@ ABI_VERSION = 1
 EXPORTS = ("moe_status_str", "moe_abi_version", "moe_route_topk", "moe_align_capacity",
            "moe_align_block", "moe_route_align", "moe_default_block_m",
            "moe_ffn_workspace_bytes", "moe_ffn_bf16", "moe_ffn_fp8", "moe_ffn_w8a16",
-           "moe_ffn_f32")
+           "moe_ffn_fp8_block", "moe_ffn_f32")
 
 
 class MoEError(RuntimeError):
@@ -77,6 +78,8 @@ def _load() -> ctypes.CDLL:
     lib.moe_ffn_fp8.argtypes = [P, P, P, P, P] + ffn_tail
     lib.moe_ffn_w8a16.restype = I
     lib.moe_ffn_w8a16.argtypes = [P, P, P, P, P] + ffn_tail
+    lib.moe_ffn_fp8_block.restype = I
+    lib.moe_ffn_fp8_block.argtypes = [P, P, P, P, P] + ffn_tail
     if lib.moe_abi_version() != ABI_VERSION:
         raise ImportError(f"libmoe ABI {lib.moe_abi_version()} != binding ABI {ABI_VERSION}")
     return lib
@@ -264,6 +267,17 @@ def ffn_w8a16(x, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids,
                        flags, workspace, out, stream)
 
 
+def ffn_fp8_block(x, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids,
+                  block_expert, num_padded, block_m: int, flags: int = 0, workspace=None,
+                  out=None, stream=None):
+    """moe_ffn_fp8_block: x [T,H] bfloat16; w1 [E,2I,H], w2 [E,H,I] e4m3fn codes with
+    float32 scales per 128x128 block (w1_scale [E,2I/128,H/128], w2_scale [E,H/128,I/128])
+    -> out [T,H] bfloat16."""
+    return _ffn_scaled(lib.moe_ffn_fp8_block, MOE_DTYPE_FP8_BLOCK, x, w1, w1_scale, w2,
+                       w2_scale, topk_ids, topk_weights, sorted_ids, block_expert, num_padded,
+                       block_m, flags, workspace, out, stream)
+
+
 def ffn_f32(x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert, num_padded,
             block_m: int, flags: int = 0, workspace=None, out=None, stream=None):
     """moe_ffn_f32: float32 throughout."""
@@ -288,15 +302,18 @@ def ffn_f32(x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert, num_pad
 def forward(x, logits, w1, w2, k: int, block_m: Optional[int] = None, renormalize: bool = False,
             w1_scale=None, w2_scale=None, flags: int = 0, weight_only: bool = False,
             stream=None):
-    """route_align -> ffn_{f32,bf16,fp8,w8a16}, dtype taken from w1 (fp8 codes run
-    ffn_w8a16 with ``weight_only``, else ffn_fp8); block_m defaults to
-    moe_default_block_m."""
+    """route_align -> ffn_{f32,bf16,fp8,w8a16,fp8_block}, dtype taken from w1 (fp8
+    codes with 3-d block scales run ffn_fp8_block; with per-row scales ffn_w8a16
+    if ``weight_only``, else ffn_fp8); block_m defaults to moe_default_block_m."""
     E = w1.shape[0]
     if block_m is None:
         block_m = default_block_m(x.shape[0], E, k)
     ids, wts, sorted_ids, block_expert, num_padded = route_align(logits, k, block_m, renormalize,
                                                                  stream=stream)
     if w1.dtype in (torch.uint8, torch.float8_e4m3fn):
+        if w1_scale is not None and w1_scale.dim() == 3:
+            return ffn_fp8_block(x, w1, w1_scale, w2, w2_scale, ids, wts, sorted_ids,
+                                 block_expert, num_padded, block_m, flags, stream=stream)
         return (ffn_w8a16 if weight_only else ffn_fp8)(x, w1, w1_scale, w2, w2_scale, ids, wts, sorted_ids, block_expert,
                        num_padded, block_m, flags, stream=stream)
     if w1.dtype == torch.bfloat16:

@@ -159,7 +159,7 @@ MOE_EXPORT size_t moe_ffn_workspace_bytes(int T, int E, int H, int I, int k, int
   (void)E;
   (void)block_m;
   if (dtype != MOE_DTYPE_F32 && dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8 &&
-      dtype != MOE_DTYPE_W8A16)
+      dtype != MOE_DTYPE_W8A16 && dtype != MOE_DTYPE_FP8_BLOCK)
     return 0;
   if (T < 0 || H < 1 || I < 1 || k < 1) return 0;
   // W8A16 keeps the bf16 path's intermediates
@@ -217,6 +217,26 @@ MOE_EXPORT moe_status moe_ffn_w8a16(const uint16_t* x, const uint8_t* w1, const 
   if (!w1_scale || !w2_scale) return MOE_ERR_NULL;
   if (!aligned(w1_scale, 16) || !aligned(w2_scale, 16)) return MOE_ERR_ALIGN;
   return hip_status(moe::launch_ffn_w8a16(
+      problem(x, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids, block_expert,
+              num_padded, T, E, H, I, k, block_m, flags, workspace, out),
+      (hipStream_t)stream));
+}
+
+MOE_EXPORT moe_status moe_ffn_fp8_block(const uint16_t* x, const uint8_t* w1,
+                                        const float* w1_scale, const uint8_t* w2,
+                                        const float* w2_scale, const int32_t* topk_ids,
+                                        const float* topk_weights, const int32_t* sorted_ids,
+                                        const int32_t* block_expert, const int32_t* num_padded,
+                                        int T, int E, int H, int I, int k, int block_m,
+                                        unsigned flags, void* workspace, size_t workspace_bytes,
+                                        uint16_t* out, moe_stream_t stream) {
+  moe_status s = check_ffn(x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert,
+                           num_padded, T, E, H, I, k, block_m, flags, workspace, workspace_bytes,
+                           out, MOE_DTYPE_FP8_BLOCK);
+  if (s != MOE_OK || T == 0) return s;
+  if (!w1_scale || !w2_scale) return MOE_ERR_NULL;
+  if (!aligned(w1_scale, 4) || !aligned(w2_scale, 4)) return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_ffn_fp8_block(
       problem(x, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids, block_expert,
               num_padded, T, E, H, I, k, block_m, flags, workspace, out),
       (hipStream_t)stream));

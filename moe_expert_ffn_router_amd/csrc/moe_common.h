@@ -120,4 +120,10 @@ __device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b, const 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// 16x16x32 with both operands OCP fp8 e4m3: 8 codes per lane (one k-group).
+__device__ __forceinline__ f32x4 mfma_fp8_k32(const u32x2& a, const u32x2& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(__builtin_bit_cast(long, a),
+                                                    __builtin_bit_cast(long, b), c, 0, 0, 0);
+}
+
 }  // namespace moe

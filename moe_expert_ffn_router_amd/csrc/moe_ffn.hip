@@ -742,6 +742,145 @@ __device__ __forceinline__ void fc2_cold_w8(const Fc2Args& p, int e, int r, int 
   }
 }
 
+// ------------------------------- block-scaled FP8: 128x128 weight blocks ---
+// Block-wise FP8 ("vLLM SM architecture adaptation": section 4.1's block FP8
+// MoE backends, section 4.2's block-wise DeepGEMM MoE, section 9's figure:
+// dequantisation inside the GEMM loop). Weights carry one fp32 scale per
+// 128 x 128 block, activations one per 128 consecutive elements of a row
+// (x per token, h per slot), so every 128-byte line of a weight row and of
+// an activation row is exactly one K-block. A line's partial dot product is
+// formed apart from the others and scaled by (weight block scale) x
+// (activation group scale) into the fp32 sum. The half-split tiles of the
+// cold path carry both halves of the SAME line in D's two diagonal blocks,
+// so the 16x16x32 fp8 MFMA (8 codes per lane) keeps each MFMA inside one
+// line: a lane's 16 codes of a line are two MFMAs into a fresh partial,
+// which is scaled per lane (its column is its token) and added.
+
+template <int U>
+struct BlkGroup {
+  u32x4 p[U], q[U], b[U];  // 16 codes of tiles P, Q and of the token per line
+  float sa[U];             // activation group scale of this lane's token per line
+  float sp[U], sq[U];      // weight block scales of tiles P and Q per line
+  __device__ __forceinline__ void issue(const uint8_t* __restrict__ ap,
+                                        const uint8_t* __restrict__ aq,
+                                        const uint8_t* __restrict__ bp,
+                                        const float* __restrict__ as,
+                                        const float* __restrict__ wsp,
+                                        const float* __restrict__ wsq, bool ok, int c) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      p[u] = __builtin_nontemporal_load((const u32x4*)(ap + (size_t)(c + u) * 128));
+      q[u] = __builtin_nontemporal_load((const u32x4*)(aq + (size_t)(c + u) * 128));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      b[u] = u32x4{0, 0, 0, 0};
+      sa[u] = 0.f;
+      if (ok) {
+        b[u] = *(const u32x4*)(bp + (size_t)(c + u) * 128);
+        sa[u] = as[c + u];
+      }
+      sp[u] = wsp[c + u];
+      sq[u] = wsq[c + u];
+    }
+  }
+  __device__ __forceinline__ void compute(f32x4& accp, f32x4& accq) const {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const u32x2 b0{b[u].x, b[u].y}, b1{b[u].z, b[u].w};
+      f32x4 tp = mfma_fp8_k32(u32x2{p[u].x, p[u].y}, b0, f32x4{0.f, 0.f, 0.f, 0.f});
+      tp = mfma_fp8_k32(u32x2{p[u].z, p[u].w}, b1, tp);
+      f32x4 tq = mfma_fp8_k32(u32x2{q[u].x, q[u].y}, b0, f32x4{0.f, 0.f, 0.f, 0.f});
+      tq = mfma_fp8_k32(u32x2{q[u].z, q[u].w}, b1, tq);
+      const float fp = sp[u] * sa[u], fq = sq[u] * sa[u];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        accp[i] = fmaf(tp[i], fp, accp[i]);
+        accq[i] = fmaf(tq[i], fq, accq[i]);
+      }
+    }
+  }
+};
+
+// accp/accq = sum over the kbytes/128 lines of a row of the scaled line
+// partials of tiles P and Q. as: the lane's token's group scales; wsp/wsq:
+// the block-scale rows of P's and Q's row block.
+template <int U>
+__device__ __forceinline__ void blk_kloop(const uint8_t* __restrict__ ap,
+                                          const uint8_t* __restrict__ aq,
+                                          const uint8_t* __restrict__ bp,
+                                          const float* __restrict__ as,
+                                          const float* __restrict__ wsp,
+                                          const float* __restrict__ wsq, bool ok, int kbytes,
+                                          f32x4& accp, f32x4& accq) {
+  const int nch = kbytes / 128;
+  const int ngrp = nch / U;
+  BlkGroup<U> g0, g1;
+  if (ngrp > 0) g0.issue(ap, aq, bp, as, wsp, wsq, ok, 0);
+  int g = 0;
+  for (; g + 1 < ngrp; g += 2) {
+    g1.issue(ap, aq, bp, as, wsp, wsq, ok, (g + 1) * U);
+    g0.compute(accp, accq);
+    if (g + 2 < ngrp) g0.issue(ap, aq, bp, as, wsp, wsq, ok, (g + 2) * U);
+    g1.compute(accp, accq);
+  }
+  if (g < ngrp) g0.compute(accp, accq);
+  for (int c = ngrp * U; c < nch; ++c) {
+    BlkGroup<1> one;
+    one.issue(ap, aq, bp, as, wsp, wsq, ok, c);
+    one.compute(accp, accq);
+  }
+}
+
+constexpr int kBlk = 128;   // block edge (weights) and group length (activations)
+constexpr int kBlkU = 2;    // lines per pipeline group
+
+// Cold FC1 tile r of the block-scaled path (layout as fc1_cold). x: codes
+// [T, H]; xs: group scales [T, H/128]; w1s: block scales [E, 2I/128, H/128].
+__device__ __forceinline__ void fc1_cold_blk(const Fc1Args& p, int e, int r, int slot) {
+  const int lane = threadIdx.x & 63;
+  const int kb = p.H / kBlk, nb = 2 * p.I / kBlk;
+  const int off = half_split_off();
+  const uint8_t* w = (const uint8_t*)p.w1 + (size_t)e * 2 * p.I * p.H;
+  const uint8_t* ap = w + (size_t)(r * 8 + (lane & 7)) * p.H + off;
+  const uint8_t* aq = w + (size_t)(p.I + r * 8 + (lane & 7)) * p.H + off;
+  const bool ok = slot < p.S;
+  const int t = ok ? slot / p.k : 0;
+  const uint8_t* bp = (const uint8_t*)p.x + (size_t)t * p.H + off;
+  const float* as = p.xs + (size_t)t * kb;
+  const float* wsp = p.w1s + ((size_t)e * nb + (r * 8) / kBlk) * kb;
+  const float* wsq = p.w1s + ((size_t)e * nb + (p.I + r * 8) / kBlk) * kb;
+  f32x4 accp = {}, accq = {};
+  blk_kloop<kBlkU>(ap, aq, bp, as, wsp, wsq, ok, p.H, accp, accq);
+  const f32x4 g = diag_sum(accp), u = diag_sum(accq);
+  if ((lane & 8) == 0 && lane < 32 && ok) store_h<true>(p, slot, r * 8 + 4 * (lane >> 4), g, u);
+}
+
+// Cold FC2 tile r of the block-scaled path (layout as fc2_cold). h: codes
+// [S, I]; hs: group scales [S, I/128]; w2s: block scales [E, H/128, I/128].
+// Both 8-row halves of the tile lie in one 128-row block.
+__device__ __forceinline__ void fc2_cold_blk(const Fc2Args& p, int e, int r, int slot) {
+  const int lane = threadIdx.x & 63;
+  const int kb = p.I / kBlk, nb = p.H / kBlk;
+  const int off = half_split_off();
+  const uint8_t* w = (const uint8_t*)p.w2 + (size_t)e * p.H * p.I;
+  const uint8_t* ap = w + (size_t)(r * 16 + (lane & 7)) * p.I + off;
+  const uint8_t* aq = w + (size_t)(r * 16 + 8 + (lane & 7)) * p.I + off;
+  const bool ok = slot < p.S;
+  const int s = ok ? slot : 0;
+  const uint8_t* bp = (const uint8_t*)p.h + (size_t)s * p.I + off;
+  const float* as = p.hs + (size_t)s * kb;
+  const float* ws = p.w2s + ((size_t)e * nb + (r * 16) / kBlk) * kb;
+  f32x4 accp = {}, accq = {};
+  blk_kloop<kBlkU>(ap, aq, bp, as, ws, ws, ok, p.I, accp, accq);
+  const f32x4 vp = diag_sum(accp), vq = diag_sum(accq);
+  if ((lane & 8) == 0 && lane < 32 && ok) {
+    const int row = r * 16 + 4 * (lane >> 4);
+    store_y(p, slot, row, vp);
+    store_y(p, slot, row + 8, vq);
+  }
+}
+
 // ------------------------------------------------- persistent kernels ---
 
 // Work list: (block, quad of 4 consecutive tiles), one quad per workgroup
@@ -852,6 +991,21 @@ __global__ __launch_bounds__(256) void fc2_w8a16_kernel(Fc2Args p) {
   run_quads<false, false, false, Fc2Args, fc2_cold_w8, fc2_hot_pass<false, 1>,
             fc2_hot_pass<false, 2>, fc2_hot_pass<false, 3>, fc2_hot_pass<false, 4>>(p, p.H >> 4,
                                                                                      lds);
+}
+
+// Block-scaled FP8 runs every block by cold passes of 8 tokens, like W8A16.
+__global__ __launch_bounds__(256) void fc1_blk_kernel(Fc1Args p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[16];
+  run_quads<true, false, false, Fc1Args, fc1_cold_blk, fc1_hot_pass<true, 1>,
+            fc1_hot_pass<true, 2>, fc1_hot_pass<true, 3>, fc1_hot_pass<true, 4>>(p, p.I >> 3,
+                                                                                  lds);
+}
+
+__global__ __launch_bounds__(256) void fc2_blk_kernel(Fc2Args p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[16];
+  run_quads<true, false, false, Fc2Args, fc2_cold_blk, fc2_hot_pass<true, 1>,
+            fc2_hot_pass<true, 2>, fc2_hot_pass<true, 3>, fc2_hot_pass<true, 4>>(p, p.H >> 4,
+                                                                                  lds);
 }
 
 // ------------------------------------------- dense tiles (big blocks) ---
@@ -1279,6 +1433,42 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const InT* __restrict__
   if (lane == 0) scales[r] = scale;
 }
 
+// Per-group FP8 quantiser: groups of 128 consecutive elements of a row, 16
+// lanes per group (8 elements each), four groups per wave; the decisions of
+// quant_rows_kernel within each group. scales: [R, C/128].
+template <typename InT>
+__global__ __launch_bounds__(256) void quant_groups_kernel(const InT* __restrict__ in, int R,
+                                                           int C, uint8_t* __restrict__ codes,
+                                                           float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int G = C / kBlk;
+  const long n = (long)R * G;
+  const long gi = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+  const bool live = gi < n;  // a 16-lane row is live or not as a whole
+  const size_t at = live ? (size_t)(gi / G) * C + (size_t)(gi % G) * kBlk + (lane & 15) * 8 : 0;
+  float v[8] = {};
+  if (live) load8(in + at, v);
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  // max over the 16 lanes of the group (DPP inside one row)
+  amax = fmaxf(amax, wave_partner<0>(amax));
+  amax = fmaxf(amax, wave_partner<1>(amax));
+  amax = fmaxf(amax, wave_partner<2>(amax));
+  amax = fmaxf(amax, wave_partner<3>(amax));
+  const float scale = amax == 0.f ? 1.0f : amax / 448.0f;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo |= f32_to_e4m3fn(v[i] / scale) << (8 * i);
+    hi |= f32_to_e4m3fn(v[4 + i] / scale) << (8 * i);
+  }
+  if (live) {
+    *(u32x2*)(codes + at) = u32x2{lo, hi};
+    if ((lane & 15) == 0) scales[gi] = scale;
+  }
+}
+
 // ----------------------------------------------------------- combine ---
 // out[t, n] = sum_j w[t, j] * y[t*k + j, n], fp32 in j order, one rounding.
 __device__ __forceinline__ void load8y(const float* p, float (&v)[8]) { load8(p, v); }
@@ -1413,11 +1603,14 @@ FfnWorkspace ffn_workspace_layout(int T, int H, int I, int k, int dtype) {
   };
   const size_t hbytes = dtype == MOE_DTYPE_BF16 ? 2 : 4;
   put(L.h_off, L.h_bytes, S * I * hbytes);
-  if (dtype == MOE_DTYPE_FP8) {
+  if (dtype == MOE_DTYPE_FP8 || dtype == MOE_DTYPE_FP8_BLOCK) {
+    // one scale per row (FP8) or per 128-element group of a row (block FP8)
+    const size_t hg = dtype == MOE_DTYPE_FP8 ? 1 : (size_t)I / kBlk;
+    const size_t xg = dtype == MOE_DTYPE_FP8 ? 1 : (size_t)H / kBlk;
     put(L.hq_off, L.hq_bytes, S * I);
-    put(L.hs_off, L.hs_bytes, S * 4);
+    put(L.hs_off, L.hs_bytes, S * hg * 4);
     put(L.xq_off, L.xq_bytes, (size_t)T * H);
-    put(L.xs_off, L.xs_bytes, (size_t)T * 4);
+    put(L.xs_off, L.xs_bytes, (size_t)T * xg * 4);
   }
   put(L.y_off, L.y_bytes, S * H * (dtype == MOE_DTYPE_BF16 ? 2 : 4));
   put(L.q_off, L.q_bytes, S ? 2 * kQueues * sizeof(int) : 0);
@@ -1590,6 +1783,42 @@ hipError_t launch_ffn_w8a16(const FfnProblem& p, hipStream_t stream) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_COMBINE) return launch_combine(p, L, MOE_DTYPE_BF16, stream);
+  return hipSuccess;
+}
+
+hipError_t launch_ffn_fp8_block(const FfnProblem& p, hipStream_t stream) {
+  const FfnWorkspace L = ffn_workspace_layout(p.T, p.H, p.I, p.k, MOE_DTYPE_FP8_BLOCK);
+  const unsigned st = stages(p.flags);
+  const int remap = (p.flags & MOE_FFN_NO_XCD_REMAP) ? 0 : 1;
+  const int S = p.T * p.k, log2m = ilog2(p.block_m);
+  char* ws = (char*)p.workspace;
+  float* h = (float*)(ws + L.h_off);
+  uint8_t* hq = (uint8_t*)(ws + L.hq_off);
+  float* hs = (float*)(ws + L.hs_off);
+  uint8_t* xq = (uint8_t*)(ws + L.xq_off);
+  float* xs = (float*)(ws + L.xs_off);
+  float* y = (float*)(ws + L.y_off);
+  hipError_t err;
+  if (st & MOE_FFN_STAGE_FC1) {
+    const long ng = (long)p.T * (p.H / kBlk);
+    quant_groups_kernel<uint16_t><<<(unsigned)((ng + 15) / 16), 256, 0, stream>>>(
+        (const uint16_t*)p.x, p.T, p.H, xq, xs);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    Fc1Args a{xq, xs, p.w1, p.w1_scale, p.sorted_ids, p.block_expert, p.num_padded,
+              p.H, p.I, p.k, S, log2m, remap, h, nullptr};
+    fc1_blk_kernel<<<persistent_grid(fc1_blk_kernel, 12), 256, 0, stream>>>(a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (st & MOE_FFN_STAGE_FC2) {
+    const long ng = (long)S * (p.I / kBlk);
+    quant_groups_kernel<float><<<(unsigned)((ng + 15) / 16), 256, 0, stream>>>(h, S, p.I, hq, hs);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    Fc2Args a{hq, hs, p.w2, p.w2_scale, p.sorted_ids, p.block_expert, p.num_padded,
+              p.H, p.I, S, log2m, remap, y, 0, nullptr};
+    fc2_blk_kernel<<<persistent_grid(fc2_blk_kernel, 13), 256, 0, stream>>>(a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (st & MOE_FFN_STAGE_COMBINE) return launch_combine(p, L, MOE_DTYPE_FP8, stream);
   return hipSuccess;
 }
 

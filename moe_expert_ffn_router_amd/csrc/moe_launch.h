@@ -27,9 +27,9 @@ hipError_t launch_route_align(const float* logits, int T, int E, int k, int reno
 struct FfnWorkspace {
   size_t h_off, h_bytes;    // h per slot: bf16 [S, I] (bf16), f32 [S, I] (fp8, f32)
   size_t hq_off, hq_bytes;  // fp8: e4m3 codes of h [S, I]
-  size_t hs_off, hs_bytes;  // fp8: per-slot scale of h [S]
+  size_t hs_off, hs_bytes;  // fp8: scales of h, per slot [S] (block FP8: [S, I/128])
   size_t xq_off, xq_bytes;  // fp8: e4m3 codes of x [T, H]
-  size_t xs_off, xs_bytes;  // fp8: per-token scale of x [T]
+  size_t xs_off, xs_bytes;  // fp8: scales of x, per token [T] (block FP8: [T, H/128])
   size_t y_off, y_bytes;    // per-slot FC2 output [S, H]: bf16 (bf16), f32 (fp8, f32)
   size_t q_off, q_bytes;    // work counters of the dense kernels, int32 [16]
   size_t total;
@@ -56,6 +56,7 @@ struct FfnProblem {
 hipError_t launch_ffn_bf16(const FfnProblem& p, hipStream_t stream);
 hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream);
 hipError_t launch_ffn_w8a16(const FfnProblem& p, hipStream_t stream);
+hipError_t launch_ffn_fp8_block(const FfnProblem& p, hipStream_t stream);
 hipError_t launch_ffn_f32(const FfnProblem& p, hipStream_t stream);
 
 }  // namespace moe

@@ -44,7 +44,8 @@ import numpy as np
 __all__ = [
     "bf16_bits_to_f64", "e4m3fn_decode", "e4m3fn_encode", "E4M3FN_VALUES",
     "route", "align", "align_capacity", "swiglu_expert", "ffn", "quant_rows_e4m3",
-    "ffn_fp8", "dequant_rows", "ffn_w8a16", "normwise_rel_err",
+    "ffn_fp8", "dequant_rows", "ffn_w8a16", "quant_groups_e4m3", "dequant_blocks",
+    "ffn_fp8_block", "normwise_rel_err",
 ]
 
 # ---------------------------------------------------------------- formats ---
@@ -297,6 +298,75 @@ def ffn_w8a16(x_bits: np.ndarray, get_w1q: Callable[[int], np.ndarray], w1_scale
     return ffn(x, lambda e: dequant_rows(get_w1q(e), w1_scale[e]),
                lambda e: dequant_rows(get_w2q(e), w2_scale[e]), ids, weights, tokens,
                num_experts)
+
+
+# ------------------------------------------------------ block-wise FP8 ---
+# Block-wise FP8 MoE ("vLLM SM architecture adaptation": section 4.1's
+# block_fp8 backends, section 4.2's block-wise FP8 grouped GEMM, the section-9
+# figure's block-wise FP8 dequantisation inside the GEMM loop). The pages fix
+# no block size; the oracle takes 128 (the 128-wide tiles of that figure):
+# weight scales per 128 x 128 block, activation scales per 128 consecutive
+# elements of a row.
+
+BLOCK = 128
+
+
+def quant_groups_e4m3(v: np.ndarray, group: int = BLOCK) -> Tuple[np.ndarray, np.ndarray]:
+    """``quant_rows_e4m3`` applied to every run of ``group`` consecutive
+    elements of each row (the row length is a multiple of ``group``).
+    Returns (codes uint8 [R, C], scales float32 [R, C/group])."""
+    v = np.asarray(v, dtype=np.float32)
+    R, C = v.shape
+    q, s = quant_rows_e4m3(v.reshape(R * (C // group), group))
+    return q.reshape(R, C), s.reshape(R, C // group)
+
+
+def dequant_blocks(codes: np.ndarray, scale: np.ndarray, block: int = BLOCK) -> np.ndarray:
+    """W^[n, c] = dec(codes[n, c]) * scale[n // block, c // block], float64."""
+    s = np.asarray(scale, dtype=np.float64)
+    return e4m3fn_decode(codes) * np.repeat(np.repeat(s, block, axis=0), block, axis=1)
+
+
+def ffn_fp8_block(x_bits: np.ndarray, get_w1q: Callable[[int], np.ndarray],
+                  w1_scale: np.ndarray, get_w2q: Callable[[int], np.ndarray],
+                  w2_scale: np.ndarray, ids: np.ndarray, weights: np.ndarray,
+                  tokens: Optional[Iterable[int]] = None,
+                  num_experts: Optional[int] = None) -> np.ndarray:
+    """Block-scaled FP8 variant, format-exact. ``w1_scale`` [E, 2I/128, H/128],
+    ``w2_scale`` [E, H/128, I/128]. x^ = group-dequantised x (groups of 128
+    per token); h is computed in float64 from x^ and W1^, rounded to float32,
+    and group-quantised per slot row before FC2; combine as in ``ffn``. Since
+    sum_c W^[n,c] x^[c] = sum_b w_s[n/128, b] a[b] sum_{c in b} dec(Wq) dec(xq),
+    dequantise-then-multiply is the same number as scaling each block's
+    partial sum."""
+    x32 = bf16_bits_to_f64(x_bits).astype(np.float32)
+    tok = np.arange(x32.shape[0]) if tokens is None else np.asarray(list(tokens))
+    xq, xs = quant_groups_e4m3(x32[tok])
+    xhat = e4m3fn_decode(xq) * np.repeat(xs.astype(np.float64), BLOCK, axis=1)
+    k = ids.shape[1]
+    H = x32.shape[1]
+    Y = np.zeros((tok.size, k, H), dtype=np.float64)
+    sub = ids[tok]
+    for e in np.unique(sub):
+        e = int(e)
+        if num_experts is not None and not 0 <= e < num_experts:
+            continue
+        w1 = dequant_blocks(get_w1q(e), w1_scale[e])
+        w2 = dequant_blocks(get_w2q(e), w2_scale[e])
+        I = w2.shape[1]
+        rows, js = np.nonzero(sub == e)
+        xr = xhat[rows]
+        g = xr @ w1[:I].T
+        u = xr @ w1[I:].T
+        h = (g / (1.0 + np.exp(-g)) * u).astype(np.float32)
+        hq, hs = quant_groups_e4m3(h)
+        hhat = e4m3fn_decode(hq) * np.repeat(hs.astype(np.float64), BLOCK, axis=1)
+        Y[rows, js] = hhat @ w2.T
+    w = np.asarray(weights, dtype=np.float64)[tok]
+    out = np.zeros((tok.size, H), dtype=np.float64)
+    for j in range(k):
+        out += w[:, j:j + 1] * Y[:, j]
+    return out
 
 
 # ------------------------------------------------------------- comparison ---

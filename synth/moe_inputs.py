@@ -66,15 +66,15 @@ class MoEInputs:
     H: int
     I: int
     k: int
-    dtype: str                      # "f32" | "bf16" | "fp8"
+    dtype: str                      # "f32" | "bf16" | "fp8" | "fp8_block"
     routing: str
     seed: int
     x: torch.Tensor                 # [T, H] float32 (f32) or bfloat16 (bf16, fp8)
     logits: torch.Tensor            # [T, E] float32
     w1: torch.Tensor                # [E, 2I, H] float32 | bfloat16 | uint8 (e4m3fn codes)
     w2: torch.Tensor                # [E, H, I]
-    w1_scale: Optional[torch.Tensor] = None  # [E, 2I] float32 (fp8 only)
-    w2_scale: Optional[torch.Tensor] = None  # [E, H] float32 (fp8 only)
+    w1_scale: Optional[torch.Tensor] = None  # [E, 2I] (fp8) | [E, 2I/128, H/128] (fp8_block)
+    w2_scale: Optional[torch.Tensor] = None  # [E, H] (fp8) | [E, H/128, I/128] (fp8_block)
 
     @property
     def S(self) -> int:
@@ -167,6 +167,17 @@ def _quant_rows_e4m3(m: torch.Tensor):
     return q.view(torch.uint8), scale
 
 
+def _quant_blocks_e4m3(m: torch.Tensor, b: int = 128):
+    """Block-wise weight preparation: fp32 scale = absmax/448 per b x b block,
+    codes by torch's float8_e4m3fn cast of the clamped ratio."""
+    R, C = m.shape
+    blk = m.view(R // b, b, C // b, b)
+    amax = blk.abs().amax(dim=(1, 3))
+    scale = torch.where(amax == 0, torch.ones_like(amax), amax / 448.0)
+    q = (blk / scale[:, None, :, None]).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return q.view(R, C).view(torch.uint8), scale
+
+
 def make_inputs(T: int, E: int, H: int, I: int, k: int, dtype: str = "bf16",
                 routing: str = "normal", seed: int = 0, device="cpu",
                 wstd: Optional[float] = None, zipf_s: float = 1.2,
@@ -181,18 +192,24 @@ def make_inputs(T: int, E: int, H: int, I: int, k: int, dtype: str = "bf16",
         lg = np.ascontiguousarray(logits, dtype=np.float32)
         assert lg.shape == (T, E)
     xt = torch.from_numpy(x32)
-    if dtype in ("bf16", "fp8"):
+    if dtype in ("bf16", "fp8", "fp8_block"):
         xt = xt.to(torch.bfloat16)
     elif dtype != "f32":
         raise ValueError(dtype)
     x_dev = xt.to(device)
     lg_dev = torch.from_numpy(lg).to(device)
 
-    wdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[dtype]
+    wdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8,
+           "fp8_block": torch.uint8}[dtype]
     w1 = torch.empty((E, 2 * I, H), dtype=wdt, device=device)
     w2 = torch.empty((E, H, I), dtype=wdt, device=device)
-    s1 = torch.empty((E, 2 * I), dtype=torch.float32, device=device) if dtype == "fp8" else None
-    s2 = torch.empty((E, H), dtype=torch.float32, device=device) if dtype == "fp8" else None
+    s1 = s2 = None
+    if dtype == "fp8":
+        s1 = torch.empty((E, 2 * I), dtype=torch.float32, device=device)
+        s2 = torch.empty((E, H), dtype=torch.float32, device=device)
+    elif dtype == "fp8_block":
+        s1 = torch.empty((E, 2 * I // 128, H // 128), dtype=torch.float32, device=device)
+        s2 = torch.empty((E, H // 128, I // 128), dtype=torch.float32, device=device)
     std1 = wstd if wstd is not None else 1.0 / np.sqrt(H)
     std2 = wstd if wstd is not None else 1.0 / np.sqrt(I)
     for e in range(E):
@@ -201,6 +218,9 @@ def make_inputs(T: int, E: int, H: int, I: int, k: int, dtype: str = "bf16",
         if dtype == "fp8":
             w1[e], s1[e] = _quant_rows_e4m3(m1)
             w2[e], s2[e] = _quant_rows_e4m3(m2)
+        elif dtype == "fp8_block":
+            w1[e], s1[e] = _quant_blocks_e4m3(m1)
+            w2[e], s2[e] = _quant_blocks_e4m3(m2)
         else:
             w1[e] = m1.to(wdt)
             w2[e] = m2.to(wdt)
@@ -209,9 +229,10 @@ def make_inputs(T: int, E: int, H: int, I: int, k: int, dtype: str = "bf16",
                      x=x_dev, logits=lg_dev, w1=w1, w2=w2, w1_scale=s1, w2_scale=s2)
 
 
-def config_inputs(n: int, device="cpu", seed: int = 0) -> MoEInputs:
+def config_inputs(n: int, device="cpu", seed: int = 0, dtype: Optional[str] = None) -> MoEInputs:
+    """Workload n; ``dtype`` overrides its weight format (same master weights)."""
     c = CONFIGS[n]
-    return make_inputs(c["T"], c["E"], c["H"], c["I"], c["k"], dtype=c["dtype"],
+    return make_inputs(c["T"], c["E"], c["H"], c["I"], c["k"], dtype=dtype or c["dtype"],
                        routing=c["routing"], seed=seed, device=device,
                        wstd=c.get("wstd"), zipf_s=c.get("zipf_s", 1.2),
                        zipf_sigma=c.get("zipf_sigma", 0.5))

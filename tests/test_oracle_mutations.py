@@ -5,6 +5,7 @@ import pytest
 
 import oracle
 import oracle.moe_oracle as om
+from tests import test_oracle_block as B
 from tests import test_oracle_ffn as F
 from tests import test_oracle_formats as FM
 from tests import test_oracle_route_align as R
@@ -143,12 +144,43 @@ def _ffn_w8a16_quantises_x(x_bits, g1, s1, g2, s2, ids, w, tokens=None, num_expe
                               w, tokens, num_experts)
 
 
+def _dequant_blocks_transposed(codes, scale, block=128):
+    s = np.asarray(scale, np.float64).T
+    return om.e4m3fn_decode(codes) * np.repeat(np.repeat(s, block, 0), block, 1)
+
+
+def _quant_groups_whole_row(v, group=128):
+    q, s = om.quant_rows_e4m3(v)
+    return q, np.repeat(s[:, None], np.asarray(v).shape[1] // group, axis=1)
+
+
+def _ffn_fp8_block_no_h_quant(x_bits, g1, s1, g2, s2, ids, w, tokens=None, num_experts=None):
+    orig = om.quant_groups_e4m3
+    calls = {"n": 0}
+
+    def q(v, group=128):
+        calls["n"] += 1
+        if calls["n"] == 1:
+            return orig(v, group)
+        v = np.asarray(v, np.float32)
+        return v, np.ones((v.shape[0], v.shape[1] // group), np.float32)
+    dec = om.e4m3fn_decode
+    om.quant_groups_e4m3 = q
+    om.e4m3fn_decode = lambda c: np.asarray(c, np.float64) if np.asarray(c).dtype != np.uint8 else dec(c)
+    try:
+        return MUT_ORIG_FFN_FP8_BLOCK(x_bits, g1, s1, g2, s2, ids, w, tokens, num_experts)
+    finally:
+        om.quant_groups_e4m3 = orig
+        om.e4m3fn_decode = dec
+
+
 MUT_ORIG_ROUTE = om.route
 MUT_ORIG_SWIGLU = om.swiglu_expert
 MUT_ORIG_ALIGN = om.align
 MUT_ORIG_ENC = om.e4m3fn_encode
 MUT_ORIG_FFN_FP8 = om.ffn_fp8
 MUT_ORIG_FFN_W8A16 = om.ffn_w8a16
+MUT_ORIG_FFN_FP8_BLOCK = om.ffn_fp8_block
 
 MUTATIONS = [
     ("route", _route_ascending, [lambda: R.test_topk_ids_match_brute_force(7, 64, 8)]),
@@ -166,6 +198,12 @@ MUTATIONS = [
      [lambda: F.test_ffn_w8a16_matches_brute_force_with_library_decode(2, 3, 5, 3, 2)]),
     ("dequant_rows", _dequant_column_scale,
      [lambda: F.test_ffn_w8a16_matches_brute_force_with_library_decode(3, 2, 4, 6, 1)]),
+    ("dequant_blocks", _dequant_blocks_transposed,
+     [lambda: B.test_ffn_fp8_block_matches_blockwise_loops(2, 2)]),
+    ("quant_groups_e4m3", _quant_groups_whole_row,
+     [B.test_quant_groups_closed_forms, lambda: B.test_ffn_fp8_block_matches_blockwise_loops(1, 1)]),
+    ("ffn_fp8_block", _ffn_fp8_block_no_h_quant,
+     [lambda: B.test_ffn_fp8_block_matches_blockwise_loops(1, 1)]),
     ("ffn_w8a16", _ffn_w8a16_quantises_x,
      [lambda: F.test_ffn_w8a16_matches_brute_force_with_library_decode(2, 3, 5, 3, 2)]),
 ]
