@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--block-fp8", action="store_true",
                     help="FP8 workloads: weights quantised per 128x128 block (same master "
                          "weights), activations per 128-element group")
+    ap.add_argument("--single-launch", action="store_true",
+                    help="T <= 16: the whole layer as one cooperative launch (moe_forward_small)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
@@ -216,7 +218,24 @@ def main():
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
 
+    if args.single_launch:
+        if wo or blk or args.ep > 1 or args.tp > 1 or T > moe.small_max_tokens():
+            sys.exit("bench.py: --single-launch takes an unsharded bf16/fp8 workload of at "
+                     f"most {moe.small_max_tokens()} tokens")
+        ws_small = torch.empty(moe.forward_small_workspace_bytes(T, E, H, I, k, dt_code),
+                               dtype=torch.uint8, device=dev)
+
+    def step_small(i=None):
+        if i is not None:
+            ev_a[i].record(stream)
+        moe.forward_small(inp.logits, inp.x, w1, w2, k, False, s1, s2, args.flags, out, ids,
+                          wts, ws_small, stream)
+        if i is not None:
+            ev_b[i].record(stream)
+
     def step(i=None):
+        if args.single_launch:
+            return step_small(i)
         if E == Eg:
             moe.route_align(inp.logits, k, M, out=(ids, wts, sid, be, npad), stream=stream)
         else:  # the rank routes over all experts and aligns its local ones
@@ -264,9 +283,17 @@ def main():
         + T * H * bx + S_loc * I * (2 if inp.dtype == "bf16" or wo else 4)
     fc1_gbs = fc1_bytes / (fc1_ms * 1e-3) / 1e9
     step_s = ms_per_step * 1e-3
-    wl = cfg["name"] + ("_w8a16" if wo else "") + ("_block128" if blk else "") + (f"_ep{args.ep}_rank0" if args.ep > 1 else "") \
+    wl = cfg["name"] + ("_w8a16" if wo else "") + ("_block128" if blk else "") \
+        + ("_single_launch" if args.single_launch else "") + (f"_ep{args.ep}_rank0" if args.ep > 1 else "") \
         + (f"_tp{args.tp}_rank0" if args.tp > 1 else "")
-    if M >= 128:  # grouped-GEMM tiles (prefill-sized blocks): FC1 is bound by MFMA
+    if args.single_launch:  # one kernel for the whole layer: its bytes over its duration
+        gbs = layer_bytes / (fc1_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic("small_forward", wl),
+                    "kernel": "small_forward (whole layer, one launch)",
+                    "kernel_ms": round(fc1_ms, 4), "alg_bytes_per_launch": layer_bytes}
+    elif M >= 128:  # grouped-GEMM tiles (prefill-sized blocks): FC1 is bound by MFMA
         fc1_flops = S_loc * 2 * I * H * 2
         fc1_tfs = fc1_flops / (fc1_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(fc1_tfs, 1), "peak": MFMA_BF16_PEAK_TFLOPS,

@@ -292,6 +292,44 @@ moe_status moe_ffn_f32(const float* x, const float* w1, const float* w2,
                        int block_m, unsigned flags, void* workspace, size_t workspace_bytes,
                        float* out, moe_stream_t stream);
 
+/*
+ * Single-launch forward of a small batch: router softmax + top-k, alignment,
+ * FC1 + SiLU*up, FC2 and the combine in one cooperative persistent kernel
+ * (plus a 256-thread kernel that clears its barrier words). Passage: "vLLM SM
+ * architecture adaptation", section 4.3: for a batch of at most 8 tokens the
+ * grouped-GEMM path's launch overhead is what a single-kernel path avoids.
+ * Results equal, bit for bit, moe_route_topk -> moe_align_block ->
+ * moe_ffn_bf16 / moe_ffn_fp8 at the same T (any block_m): every expert's
+ * slots are served by the same 8-token streaming passes.
+ *
+ *  logits        [T, E] fp32; renormalize as in moe_route_topk.
+ *  x             [T, H] bf16.
+ *  w1, w2        dtype MOE_DTYPE_BF16: bf16 [E, 2I, H] and [E, H, I];
+ *                MOE_DTYPE_FP8: e4m3fn codes with w1_scale [E, 2I] and
+ *                w2_scale [E, H] fp32 (16-byte aligned), as moe_ffn_fp8.
+ *  topk_ids, topk_weights   [T, k], written (as moe_route_topk).
+ *  out           [T, H] bf16, written.
+ *  workspace     moe_forward_small_workspace_bytes(T, E, H, I, k, dtype)
+ *                bytes, 256-byte aligned, no initialisation needed. Its last
+ *                4 bytes are a status word: 0 after the call has run, nonzero
+ *                if a device-side barrier wait gave up (out is then
+ *                undefined; not expected, the launch guarantees residency).
+ *  flags         0 or MOE_FFN_NO_XCD_REMAP.
+ *  Limits: 0 <= T <= moe_small_max_tokens() (16), 1 <= E <= 1024,
+ *  1 <= k <= E, T * k <= 256, H and I multiples of 128. Returns
+ *  MOE_ERR_SHAPE beyond them, MOE_ERR_UNSUPPORTED for another dtype or flag,
+ *  MOE_ERR_HIP if the cooperative launch is refused. Calls that share a
+ *  workspace must not overlap in time.
+ */
+int moe_small_max_tokens(void);
+size_t moe_forward_small_workspace_bytes(int T, int E, int H, int I, int k, int dtype);
+moe_status moe_forward_small(const float* logits, const uint16_t* x, const void* w1,
+                             const float* w1_scale, const void* w2, const float* w2_scale, int T,
+                             int E, int H, int I, int k, int renormalize, int dtype,
+                             unsigned flags, int32_t* topk_ids, float* topk_weights,
+                             void* workspace, size_t workspace_bytes, uint16_t* out,
+                             moe_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,6 +15,7 @@ The names mirror the C ABI in include/moe.h:
     ffn_fp8_block(x, w1, w1_scale, w2, w2_scale, ids, wts, ..., block_m, ...)        -> out
     ffn_f32(x, w1, w2, ids, wts, ..., block_m, ...)                                 -> out
     forward(x, logits, w1, w2, k, ...)   convenience chaining of the three calls
+    forward_small(logits, x, w1, w2, k, ...) -> (out, topk_ids, topk_weights)   one launch, T <= 16
 """
 from __future__ import annotations
 
@@ -36,7 +37,8 @@ ABI_VERSION = 1
 EXPORTS = ("moe_status_str", "moe_abi_version", "moe_route_topk", "moe_align_capacity",
            "moe_align_block", "moe_route_align", "moe_default_block_m",
            "moe_ffn_workspace_bytes", "moe_ffn_bf16", "moe_ffn_fp8", "moe_ffn_w8a16",
-           "moe_ffn_fp8_block", "moe_ffn_f32")
+           "moe_ffn_fp8_block", "moe_ffn_f32", "moe_small_max_tokens",
+           "moe_forward_small_workspace_bytes", "moe_forward_small")
 
 
 class MoEError(RuntimeError):
@@ -80,6 +82,12 @@ def _load() -> ctypes.CDLL:
     lib.moe_ffn_w8a16.argtypes = [P, P, P, P, P] + ffn_tail
     lib.moe_ffn_fp8_block.restype = I
     lib.moe_ffn_fp8_block.argtypes = [P, P, P, P, P] + ffn_tail
+    lib.moe_small_max_tokens.restype = I
+    lib.moe_small_max_tokens.argtypes = []
+    lib.moe_forward_small_workspace_bytes.restype = Z
+    lib.moe_forward_small_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.moe_forward_small.restype = I
+    lib.moe_forward_small.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, U, P, P, P, Z, P, P]
     if lib.moe_abi_version() != ABI_VERSION:
         raise ImportError(f"libmoe ABI {lib.moe_abi_version()} != binding ABI {ABI_VERSION}")
     return lib
@@ -321,3 +329,46 @@ def forward(x, logits, w1, w2, k: int, block_m: Optional[int] = None, renormaliz
                         flags, stream=stream)
     return ffn_f32(x, w1, w2, ids, wts, sorted_ids, block_expert, num_padded, block_m, flags,
                    stream=stream)
+
+
+def small_max_tokens() -> int:
+    return int(lib.moe_small_max_tokens())
+
+
+def forward_small_workspace_bytes(T, E, H, I, k, dtype) -> int:
+    return int(lib.moe_forward_small_workspace_bytes(T, E, H, I, k, dtype))
+
+
+def forward_small(logits, x, w1, w2, k: int, renormalize: bool = False, w1_scale=None,
+                  w2_scale=None, flags: int = 0, out=None, topk_ids=None, topk_weights=None,
+                  workspace=None, stream=None):
+    """moe_forward_small: the whole layer for T <= small_max_tokens() in one launch.
+    bf16 weights, or e4m3fn codes with per-row float32 scales (W8A8). Returns
+    (out [T,H] bfloat16, topk_ids [T,k] int32, topk_weights [T,k] float32)."""
+    fp8 = w1.dtype in (torch.uint8, torch.float8_e4m3fn)
+    wdt = (torch.uint8, torch.float8_e4m3fn) if fp8 else (torch.bfloat16,)
+    _need(x, "x", (torch.bfloat16,))
+    _need(logits, "logits", (torch.float32,), x.device)
+    _need(w1, "w1", wdt, x.device)
+    _need(w2, "w2", wdt, x.device)
+    if fp8:
+        _need(w1_scale, "w1_scale", (torch.float32,), x.device)
+        _need(w2_scale, "w2_scale", (torch.float32,), x.device)
+    T, H = x.shape
+    E, I2, _ = w1.shape
+    dtype = MOE_DTYPE_FP8 if fp8 else MOE_DTYPE_BF16
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    if topk_weights is None:
+        topk_weights = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        n = forward_small_workspace_bytes(T, E, H, I2 // 2, k, dtype)
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
+    _check(lib.moe_forward_small(_ptr(logits), _ptr(x), _ptr(w1), _ptr(w1_scale) if fp8 else None,
+                                 _ptr(w2), _ptr(w2_scale) if fp8 else None, T, E, H, I2 // 2, k,
+                                 1 if renormalize else 0, dtype, flags, _ptr(topk_ids),
+                                 _ptr(topk_weights), _ptr(workspace), workspace.numel(),
+                                 _ptr(out), _stream(stream)))
+    return out, topk_ids, topk_weights

@@ -149,6 +149,49 @@ MOE_EXPORT moe_status moe_route_align(const float* logits, int T, int E, int k, 
                                       block_expert, num_padded, st));
 }
 
+MOE_EXPORT int moe_small_max_tokens(void) { return moe::kSmallTokens; }
+
+static moe_status check_small(int T, int E, int H, int I, int k, int dtype, unsigned flags) {
+  moe_status s = check_common(T, E, k);
+  if (s != MOE_OK) return s;
+  if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8) return MOE_ERR_UNSUPPORTED;
+  if (T > moe::kSmallTokens || E > moe::kSmallExperts || (long)T * k > moe::kSmallSlots)
+    return MOE_ERR_SHAPE;
+  if (H < 128 || I < 128 || H % 128 != 0 || I % 128 != 0) return MOE_ERR_SHAPE;
+  if (flags & ~(unsigned)MOE_FFN_NO_XCD_REMAP) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+MOE_EXPORT size_t moe_forward_small_workspace_bytes(int T, int E, int H, int I, int k,
+                                                    int dtype) {
+  if (check_small(T, E, H, I, k, dtype, 0) != MOE_OK) return 0;
+  return moe::small_workspace_bytes(T, H, I, k, dtype);
+}
+
+MOE_EXPORT moe_status moe_forward_small(const float* logits, const uint16_t* x, const void* w1,
+                                        const float* w1_scale, const void* w2,
+                                        const float* w2_scale, int T, int E, int H, int I,
+                                        int k, int renormalize, int dtype, unsigned flags,
+                                        int32_t* topk_ids, float* topk_weights, void* workspace,
+                                        size_t workspace_bytes, uint16_t* out,
+                                        moe_stream_t stream) {
+  moe_status s = check_small(T, E, H, I, k, dtype, flags);
+  if (s != MOE_OK || T == 0) return s;
+  const bool fp8 = dtype == MOE_DTYPE_FP8;
+  if (!logits || !x || !w1 || !w2 || !topk_ids || !topk_weights || !workspace || !out)
+    return MOE_ERR_NULL;
+  if (fp8 && (!w1_scale || !w2_scale)) return MOE_ERR_NULL;
+  if (!aligned(logits, 4) || !aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) ||
+      !aligned(out, 16) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4) ||
+      !aligned(workspace, 256) || (fp8 && (!aligned(w1_scale, 16) || !aligned(w2_scale, 16))))
+    return MOE_ERR_ALIGN;
+  if (workspace_bytes < moe::small_workspace_bytes(T, H, I, k, dtype)) return MOE_ERR_WORKSPACE;
+  moe::SmallProblem p{logits, x, w1, fp8 ? w1_scale : nullptr, w2, fp8 ? w2_scale : nullptr,
+                      T, E, H, I, k, renormalize ? 1 : 0, flags, dtype, topk_ids, topk_weights,
+                      workspace, out};
+  return hip_status(moe::launch_forward_small(p, (hipStream_t)stream));
+}
+
 MOE_EXPORT int moe_default_block_m(int T, int E, int k) {
   if (check_common(T, E, k) != MOE_OK) return 0;
   return (long)T * k >= 128L * E ? 256 : 64;

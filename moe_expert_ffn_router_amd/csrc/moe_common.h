@@ -120,6 +120,16 @@ __device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b, const 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// A device-scope store: written through to the point where every XCD sees
+// it (the L2 of one XCD is not coherent with the others' within a kernel).
+__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  st_dev((uint32_t*)p, __float_as_uint(v));
+}
+__device__ __forceinline__ void st_dev(int32_t* p, int32_t v) { st_dev((uint32_t*)p, (uint32_t)v); }
+
 // 16x16x32 with both operands OCP fp8 e4m3: 8 codes per lane (one k-group).
 __device__ __forceinline__ f32x4 mfma_fp8_k32(const u32x2& a, const u32x2& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(__builtin_bit_cast(long, a),

@@ -29,6 +29,7 @@
 // SiLU(gate) * up is formed in registers.
 #include "moe_common.h"
 #include "moe_launch.h"
+#include "moe_route_dev.h"
 
 #include <mutex>
 
@@ -390,28 +391,41 @@ struct Fc1Args {
   int* queue;          // work counters, zero at launch (dense and hot launches)
 };
 
-// Store SiLU(g)*u for 4 consecutive h columns of one slot.
-template <bool FP8>
+// Store SiLU(g)*u for 4 consecutive h columns of one slot (WT: device-scope
+// stores, for a reader in the same kernel on another XCD).
+template <bool FP8, bool WT = false>
 __device__ __forceinline__ void store_h(const Fc1Args& p, int slot, int col, const f32x4& g,
                                         const f32x4& u) {
   if (FP8) {
     f32x4 hv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) hv[i] = silu_mul(g[i], u[i]);
-    *(f32x4*)((float*)p.h + (size_t)slot * p.I + col) = hv;
+    float* dst = (float*)p.h + (size_t)slot * p.I + col;
+    if (WT) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st_dev(dst + i, hv[i]);
+    } else {
+      *(f32x4*)dst = hv;
+    }
   } else {
     uint32_t hb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16_rne(silu_mul(g[i], u[i]));
-    *(u32x2*)((uint16_t*)p.h + (size_t)slot * p.I + col) =
-        u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+    const u32x2 v{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+    uint32_t* dst = (uint32_t*)((uint16_t*)p.h + (size_t)slot * p.I + col);
+    if (WT) {
+      st_dev(dst, v.x);
+      st_dev(dst + 1, v.y);
+    } else {
+      *(u32x2*)dst = v;
+    }
   }
 }
 
 // Cold FC1 tile r (h columns [8r, 8r+8)): P = gate rows [8r, 8r+8), Q = the
 // matching up rows [I+8r, I+8r+8). After the diagonal sums a lane holds g and
 // u of the same (column, token).
-template <bool FP8, int U>
+template <bool FP8, int U, bool WT = false>
 __device__ __forceinline__ void fc1_cold(const Fc1Args& p, int e, int r, int slot) {
   const int lane = threadIdx.x & 63;
   const size_t rowb = (size_t)p.H * (FP8 ? 1 : 2);
@@ -442,7 +456,7 @@ __device__ __forceinline__ void fc1_cold(const Fc1Args& p, int e, int r, int slo
         u[i] *= su[i] * xs;
       }
     }
-    store_h<FP8>(p, slot, col, g, u);
+    store_h<FP8, WT>(p, slot, col, g, u);
   }
 }
 
@@ -504,19 +518,32 @@ struct Fc2Args {
   int* queue;          // work counters, zero at launch (dense and hot launches)
 };
 
-// Store 4 consecutive FC2 outputs of one slot.
+// Store 4 consecutive FC2 outputs of one slot (WT as store_h).
+template <bool WT = false>
 __device__ __forceinline__ void store_y(const Fc2Args& p, int slot, int row, const f32x4& v) {
   if (p.y_bf16) {
-    *(u32x2*)((uint16_t*)p.y + (size_t)slot * p.H + row) =
-        u32x2{f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-              f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
+    const u32x2 b{f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                  f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
+    uint32_t* dst = (uint32_t*)((uint16_t*)p.y + (size_t)slot * p.H + row);
+    if (WT) {
+      st_dev(dst, b.x);
+      st_dev(dst + 1, b.y);
+    } else {
+      *(u32x2*)dst = b;
+    }
   } else {
-    *(f32x4*)((float*)p.y + (size_t)slot * p.H + row) = v;
+    float* dst = (float*)p.y + (size_t)slot * p.H + row;
+    if (WT) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st_dev(dst + i, v[i]);
+    } else {
+      *(f32x4*)dst = v;
+    }
   }
 }
 
 // Cold FC2 tile r: P = output rows [16r, 16r+8), Q = [16r+8, 16r+16).
-template <bool FP8, int U>
+template <bool FP8, int U, bool WT = false>
 __device__ __forceinline__ void fc2_cold(const Fc2Args& p, int e, int r, int slot) {
   const int lane = threadIdx.x & 63;
   const size_t rowb = (size_t)p.I * (FP8 ? 1 : 2);
@@ -547,8 +574,8 @@ __device__ __forceinline__ void fc2_cold(const Fc2Args& p, int e, int r, int slo
         vq[i] *= sq[i] * hs;
       }
     }
-    store_y(p, slot, row, vp);
-    store_y(p, slot, row + 8, vq);
+    store_y<WT>(p, slot, row, vp);
+    store_y<WT>(p, slot, row + 8, vq);
   }
 }
 
@@ -1220,7 +1247,7 @@ struct DenseSched {
 };
 
 __global__ void zero_counters_kernel(int* __restrict__ c, int n) {
-  if ((int)threadIdx.x < n) c[threadIdx.x] = 0;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) c[i] = 0;
 }
 
 // First block and length of the run of blocks with expert e containing bn
@@ -1402,14 +1429,12 @@ __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
   }
 }
 
-template <typename InT>
-__global__ __launch_bounds__(256) void quant_rows_kernel(const InT* __restrict__ in, int R, int C,
-                                                         uint8_t* __restrict__ codes,
-                                                         float* __restrict__ scales) {
+// One row of C elements by the calling wave: codes and its scale (WT as
+// store_h).
+template <typename InT, bool WT = false>
+__device__ __forceinline__ void quant_row(const InT* __restrict__ row, int C,
+                                          uint8_t* __restrict__ codes, float* __restrict__ scale_out) {
   const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= R) return;
-  const InT* row = in + (size_t)r * C;
   float amax = 0.f;
   for (int c = lane * 8; c < C; c += kWave * 8) {
     float v[8];
@@ -1428,9 +1453,26 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const InT* __restrict__
       lo |= f32_to_e4m3fn(v[i] / scale) << (8 * i);
       hi |= f32_to_e4m3fn(v[4 + i] / scale) << (8 * i);
     }
-    *(u32x2*)(codes + (size_t)r * C + c) = u32x2{lo, hi};
+    if (WT) {
+      st_dev((uint32_t*)(codes + c), lo);
+      st_dev((uint32_t*)(codes + c) + 1, hi);
+    } else {
+      *(u32x2*)(codes + c) = u32x2{lo, hi};
+    }
   }
-  if (lane == 0) scales[r] = scale;
+  if (lane == 0) {
+    if (WT) st_dev(scale_out, scale);
+    else *scale_out = scale;
+  }
+}
+
+template <typename InT>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const InT* __restrict__ in, int R, int C,
+                                                         uint8_t* __restrict__ codes,
+                                                         float* __restrict__ scales) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  quant_row<InT>(in + (size_t)r * C, C, codes + (size_t)r * C, scales + r);
 }
 
 // Per-group FP8 quantiser: groups of 128 consecutive elements of a row, 16
@@ -1476,15 +1518,12 @@ __device__ __forceinline__ void load8y(const uint16_t* p, float (&v)[8]) { load8
 
 // Slots whose expert id lies outside [0, E) belong to another shard: their y
 // rows were never written and they add nothing.
+// Outputs [8i, 8i+8) of the flattened [T, H] result (H a multiple of 8).
 template <typename YT, typename OutT>
-__global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
-                                                      const float* __restrict__ w,
-                                                      const int32_t* __restrict__ ids, int E,
-                                                      int T, int H, int k,
-                                                      OutT* __restrict__ out) {
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void combine8(const YT* __restrict__ y, const float* __restrict__ w,
+                                         const int32_t* __restrict__ ids, int E, int H, int k,
+                                         OutT* __restrict__ out, long i) {
   const int per_row = H >> 3;
-  if (i >= (long)T * per_row) return;
   const int t = (int)(i / per_row), n = (int)(i % per_row) * 8;
   float acc[8] = {};
   for (int j = 0; j < k; ++j) {
@@ -1505,6 +1544,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
     *(f32x4*)(out + (size_t)t * H + n) = f32x4{acc[0], acc[1], acc[2], acc[3]};
     *(f32x4*)(out + (size_t)t * H + n + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
   }
+}
+
+template <typename YT, typename OutT>
+__global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
+                                                      const float* __restrict__ w,
+                                                      const int32_t* __restrict__ ids, int E,
+                                                      int T, int H, int k,
+                                                      OutT* __restrict__ out) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long)T * (H >> 3)) return;
+  combine8<YT, OutT>(y, w, ids, E, H, k, out, i);
 }
 
 // A combine for H not a multiple of 8 (fp32 path): one thread per element.
@@ -1588,6 +1638,193 @@ __global__ __launch_bounds__(256) void fc2_f32_kernel(const float* __restrict__ 
   }
 }
 
+// --------------------------------------------- single-launch small path ---
+// For batches of at most kSmallMaxT tokens the whole layer runs as one
+// cooperative persistent kernel ("vLLM SM architecture adaptation", section
+// 4.3: for a batch of at most 8 tokens the grouped-GEMM path's launch
+// overhead is what a single-kernel path avoids). Phases, separated by grid
+// barriers: routing (one wave per token; FP8: other waves quantise x rows) |
+// alignment, rebuilt by every workgroup in LDS from the routed ids, then FC1 |
+// (FP8: quantise h rows) | FC2 | combine. Every block of such a batch is cold,
+// so FC1 and FC2 are exactly the cold passes of the separate launches, over
+// units of (expert, up to 8 of its slots) instead of aligned blocks; results
+// equal theirs bit for bit.
+
+constexpr int kSmallMaxT = 16;
+constexpr int kSmallMaxS = 256;     // slots (one per thread of a workgroup)
+constexpr int kSmallMaxE = 1024;
+constexpr int kBarInts = 512;       // barrier words, zero at launch
+constexpr int kBarTop = 256, kBarGen = 288, kBarErr = 511;
+
+struct SmallArgs {
+  const float* logits;
+  const uint16_t* x;
+  const void* w1;
+  const float* w1s;
+  const void* w2;
+  const float* w2s;
+  int T, E, H, I, k, renorm, remap;
+  int32_t* ids;
+  float* wts;
+  uint8_t* xq;     // FP8: codes and scales of x
+  float* xs;
+  void* h;         // bf16 [S, I] or f32 [S, I] (FP8)
+  uint8_t* hq;     // FP8: codes and scales of h
+  float* hs;
+  void* y;         // bf16 [S, H] or f32 [S, H] (FP8)
+  uint16_t* out;
+  int* bar;        // kBarInts words: group counters at 32*g (g < 8), top, gen, error
+};
+
+// Grid barrier over all workgroups of a cooperative launch (all resident).
+// Two levels: workgroup g arrives on the counter of group g & 7, the last of
+// a group on the top counter, the last group raises the generation word the
+// others poll. Counters only grow within a launch, so barrier j waits for
+// the generation to reach j. Everything a phase hands to the next one is
+// written with device-scope stores (through to where every XCD reads; the
+// L2s of the XCDs are not coherent with each other), so a release needs
+// only those stores to have completed, not a write-back of the whole L2
+// (one per workgroup and barrier cost ~0.1 ms in all on MI355X); one
+// acquire per workgroup then drops stale cached lines before the next
+// phase reads. A wait gives up after 2^18 polls (each a
+// device-scope load and a short sleep: well under a second) and raises the
+// error word, so the kernel always ends.
+struct GridSync {
+  int* bar;
+  int j = 0;
+  __device__ __forceinline__ void sync() {
+    ++j;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's device-scope stores are done
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int per_group = (int)gridDim.x >> 3;
+      if (atomicAdd(bar + 32 * (blockIdx.x & 7), 1) == j * per_group - 1 &&
+          atomicAdd(bar + kBarTop, 1) == j * 8 - 1)
+        atomicMax(bar + kBarGen, j);
+      int spins = 0;
+      while (__hip_atomic_load(bar + kBarGen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < j) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins > (1 << 18)) {
+          atomicMax(bar + kBarErr, j);
+          break;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // drop stale cached lines
+    }
+    __syncthreads();
+  }
+};
+
+// The work units of a batch: (expert, up to 8 of its slots), experts
+// ascending, slots ascending within an expert; built from the routed ids by
+// every workgroup (S <= 256: one slot per thread).
+struct SmallPlan {
+  int ids[kSmallMaxS];
+  int rank[kSmallMaxS];    // position of the slot among its expert's slots
+  int sorted[kSmallMaxS];  // slots by (expert, slot)
+  int ue[kSmallMaxS];      // unit -> expert
+  int upos[kSmallMaxS];    // unit -> its first position in sorted
+  int ulen[kSmallMaxS];    // unit -> slots (1..8)
+  int nunits;
+};
+
+__device__ __forceinline__ void small_plan(const int32_t* __restrict__ ids, int S, int E,
+                                           SmallPlan& P) {
+  const int s = threadIdx.x;
+  const int e = s < S ? ids[s] : -1;
+  if (s < S) P.ids[s] = e;
+  __syncthreads();
+  const bool valid = s < S && (unsigned)e < (unsigned)E;
+  int rank = 0, below = 0, cnt = 0;
+  if (valid) {
+    for (int q = 0; q < S; ++q) {
+      const int f = P.ids[q];
+      rank += (f == e) & (q < s);
+      cnt += f == e;
+      below += (unsigned)f < (unsigned)e;  // slots of lower experts (never an invalid id)
+    }
+  }
+  P.rank[s] = valid ? rank : -1;
+  __syncthreads();
+  const bool starts = valid && (rank & 7) == 0;
+  if (valid) {
+    int ubase = 0;  // units of lower experts
+    for (int q = 0; q < S; ++q) {
+      const int f = P.ids[q];
+      ubase += ((unsigned)f < (unsigned)e) & ((P.rank[q] & 7) == 0);
+    }
+    const int pos = below + rank;
+    P.sorted[pos] = s;
+    if (starts) {
+      const int u = ubase + (rank >> 3);
+      P.ue[u] = e;
+      P.upos[u] = pos;
+      P.ulen[u] = min(8, cnt - rank);
+    }
+  }
+  const int n = __syncthreads_count(starts);
+  if (s == 0) P.nunits = n;
+  __syncthreads();
+}
+
+template <bool FP8, int VPL>
+__global__ __launch_bounds__(256) void small_forward_kernel(SmallArgs a) {
+  __shared__ SmallPlan P;
+  GridSync gs{a.bar};
+  const int w = threadIdx.x >> 6, ti = threadIdx.x & 7;
+  const int gw = blockIdx.x * 4 + w;  // global wave
+  const int nw = gridDim.x * 4;
+  const int S = a.T * a.k;
+  // routing, and the x quantiser of the FP8 path
+  if (gw < a.T) {
+    float v[VPL];
+    load_logits<VPL>(a.logits, gw, a.E, v);
+    route_token<VPL, true>(v, gw, a.E, a.k, a.renorm, a.ids, a.wts, nullptr);
+  } else if (FP8 && gw < 2 * a.T) {
+    const int t = gw - a.T;
+    quant_row<uint16_t, true>(a.x + (size_t)t * a.H, a.H, a.xq + (size_t)t * a.H, a.xs + t);
+  }
+  gs.sync();
+  small_plan(a.ids, S, a.E, P);
+  {  // FC1: units x quads of 4 tiles of 8 h columns
+    const Fc1Args f{FP8 ? (const void*)a.xq : (const void*)a.x, a.xs, a.w1, a.w1s, nullptr,
+                    nullptr, nullptr, a.H, a.I, a.k, S, 0, a.remap, a.h, nullptr};
+    const int qpu = a.I >> 5;
+    const Share sh = wg_share((long)P.nunits * qpu, a.remap);
+    for (long qd = sh.q0; qd < sh.q1; ++qd) {
+      const int u = (int)(qd / qpu), r = (int)(qd % qpu) * 4 + w;
+      const int slot = ti < P.ulen[u] ? P.sorted[P.upos[u] + ti] : S;
+      fc1_cold<FP8, cold_u<FP8, false>(), true>(f, P.ue[u], r, slot);
+    }
+  }
+  gs.sync();
+  if constexpr (FP8) {
+    for (int r = gw; r < S; r += nw)
+      quant_row<float, true>((const float*)a.h + (size_t)r * a.I, a.I, a.hq + (size_t)r * a.I,
+                             a.hs + r);
+    gs.sync();
+  }
+  {  // FC2: units x quads of 4 tiles of 16 output rows
+    const Fc2Args f{FP8 ? (const void*)a.hq : (const void*)a.h, a.hs, a.w2, a.w2s, nullptr,
+                    nullptr, nullptr, a.H, a.I, S, 0, a.remap, a.y, FP8 ? 0 : 1, nullptr};
+    const int qpu = a.H >> 6;
+    const Share sh = wg_share((long)P.nunits * qpu, a.remap);
+    for (long qd = sh.q0; qd < sh.q1; ++qd) {
+      const int u = (int)(qd / qpu), r = (int)(qd % qpu) * 4 + w;
+      const int slot = ti < P.ulen[u] ? P.sorted[P.upos[u] + ti] : S;
+      fc2_cold<FP8, cold_u<FP8, false>(), true>(f, P.ue[u], r, slot);
+    }
+  }
+  gs.sync();
+  const long n8 = (long)a.T * (a.H >> 3);
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long)gridDim.x * 256) {
+    if (FP8)
+      combine8<float, uint16_t>((const float*)a.y, a.wts, a.ids, a.E, a.H, a.k, a.out, i);
+    else
+      combine8<uint16_t, uint16_t>((const uint16_t*)a.y, a.wts, a.ids, a.E, a.H, a.k, a.out, i);
+  }
+}
+
 // -------------------------------------------------------- host side ---
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -1623,7 +1860,7 @@ FfnWorkspace ffn_workspace_layout(int T, int H, int I, int k, int dtype) {
 template <typename K>
 static int persistent_grid(K kernel, int slot, int threads = 256) {
   static std::mutex mu;
-  static int cache[64][16];
+  static int cache[64][32];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   std::lock_guard<std::mutex> lock(mu);
@@ -1820,6 +2057,44 @@ hipError_t launch_ffn_fp8_block(const FfnProblem& p, hipStream_t stream) {
   }
   if (st & MOE_FFN_STAGE_COMBINE) return launch_combine(p, L, MOE_DTYPE_FP8, stream);
   return hipSuccess;
+}
+
+static_assert(kSmallTokens == kSmallMaxT && kSmallExperts == kSmallMaxE &&
+              kSmallSlots == kSmallMaxS, "small-path limits");
+
+size_t small_workspace_bytes(int T, int H, int I, int k, int dtype) {
+  return align_up(ffn_workspace_layout(T, H, I, k, dtype).total, 256) + kBarInts * sizeof(int);
+}
+
+template <bool FP8>
+static hipError_t launch_small(const SmallProblem& p, const SmallArgs& a, hipStream_t stream) {
+  void* args[] = {(void*)&a};
+  auto go = [&](auto kernel, int slot) {
+    const int grid = persistent_grid(kernel, slot);
+    return hipLaunchCooperativeKernel(kernel, dim3(grid), dim3(256), args, 0, stream);
+  };
+  const int base = FP8 ? 19 : 16;
+  if (p.E <= 64) return go(small_forward_kernel<FP8, 1>, base);
+  if (p.E <= 256) return go(small_forward_kernel<FP8, 4>, base + 1);
+  return go(small_forward_kernel<FP8, 16>, base + 2);
+}
+
+hipError_t launch_forward_small(const SmallProblem& p, hipStream_t stream) {
+  const bool fp8 = p.dtype == MOE_DTYPE_FP8;
+  const FfnWorkspace L = ffn_workspace_layout(p.T, p.H, p.I, p.k, p.dtype);
+  char* ws = (char*)p.workspace;
+  int* bar = (int*)(ws + align_up(L.total, 256));
+  SmallArgs a{p.logits, (const uint16_t*)p.x, p.w1, p.w1_scale, p.w2, p.w2_scale,
+              p.T, p.E, p.H, p.I, p.k, p.renorm, (p.flags & MOE_FFN_NO_XCD_REMAP) ? 0 : 1,
+              p.ids, p.wts,
+              fp8 ? (uint8_t*)(ws + L.xq_off) : nullptr, fp8 ? (float*)(ws + L.xs_off) : nullptr,
+              ws + L.h_off,
+              fp8 ? (uint8_t*)(ws + L.hq_off) : nullptr, fp8 ? (float*)(ws + L.hs_off) : nullptr,
+              ws + L.y_off, (uint16_t*)p.out, bar};
+  zero_counters_kernel<<<1, 256, 0, stream>>>(bar, kBarInts);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return fp8 ? launch_small<true>(p, a, stream) : launch_small<false>(p, a, stream);
 }
 
 hipError_t launch_ffn_f32(const FfnProblem& p, hipStream_t stream) {

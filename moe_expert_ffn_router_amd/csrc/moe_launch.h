@@ -57,6 +57,31 @@ hipError_t launch_ffn_bf16(const FfnProblem& p, hipStream_t stream);
 hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream);
 hipError_t launch_ffn_w8a16(const FfnProblem& p, hipStream_t stream);
 hipError_t launch_ffn_fp8_block(const FfnProblem& p, hipStream_t stream);
+
+// Single-launch forward of a small batch (T <= kSmallTokens): routing,
+// alignment, FC1, FC2 and combine in one cooperative kernel.
+constexpr int kSmallTokens = 16;
+constexpr int kSmallExperts = 1024;
+constexpr int kSmallSlots = 256;
+struct SmallProblem {
+  const float* logits;
+  const void* x;
+  const void* w1;
+  const float* w1_scale;
+  const void* w2;
+  const float* w2_scale;
+  int T, E, H, I, k, renorm;
+  unsigned flags;
+  int dtype;  // MOE_DTYPE_BF16 or MOE_DTYPE_FP8
+  int32_t* ids;
+  float* wts;
+  void* workspace;
+  void* out;
+};
+// ffn_workspace_layout of the dtype, then the barrier words (the last 4
+// bytes: the status word).
+size_t small_workspace_bytes(int T, int H, int I, int k, int dtype);
+hipError_t launch_forward_small(const SmallProblem& p, hipStream_t stream);
 hipError_t launch_ffn_f32(const FfnProblem& p, hipStream_t stream);
 
 }  // namespace moe

@@ -45,9 +45,10 @@ __device__ __forceinline__ void load_logits(const float* __restrict__ logits, in
 }
 
 // Routes token t, whose logits the calling wave holds in v (load_logits);
-// writes its k ids and weights, and the ids also to ids_copy (e.g. LDS) when
-// that is not null.
-template <int VPL>
+// writes its k ids and weights (WT: with device-scope stores, for readers in
+// the same kernel on other XCDs), and the ids also to ids_copy (e.g. LDS)
+// when that is not null.
+template <int VPL, bool WT = false>
 __device__ __forceinline__ void route_token(const float (&v)[VPL], int t, int E, int k,
                                             int renorm, int32_t* __restrict__ ids,
                                             float* __restrict__ wts, int32_t* ids_copy) {
@@ -107,8 +108,14 @@ __device__ __forceinline__ void route_token(const float (&v)[VPL], int t, int E,
   for (int i = 0; i < VPL; ++i) {
     const int j = i * kWave + lane;
     if (j < k) {
-      ids[(size_t)t * k + j] = my_id[i];
-      wts[(size_t)t * k + j] = renorm ? my_p[i] / psum : my_p[i];
+      const float wj = renorm ? my_p[i] / psum : my_p[i];
+      if (WT) {
+        st_dev(ids + (size_t)t * k + j, my_id[i]);
+        st_dev(wts + (size_t)t * k + j, wj);
+      } else {
+        ids[(size_t)t * k + j] = my_id[i];
+        wts[(size_t)t * k + j] = wj;
+      }
       if (ids_copy) ids_copy[(size_t)t * k + j] = my_id[i];
     }
   }

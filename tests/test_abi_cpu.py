@@ -108,6 +108,20 @@ def call_fp8(s1=P, s2=P, **kw):
                            a["flags"], a["ws"], a["wsb"], a["out"], None)
 
 
+def call_w8a16(s1=P, s2=P, **kw):
+    a = _ffn_args(**kw)
+    return lib.moe_ffn_w8a16(a["x"], a["w1"], s1, a["w2"], s2, a["ids"], a["wts"], a["sid"],
+                             a["be"], a["npad"], a["T"], a["E"], a["H"], a["I"], a["k"], a["M"],
+                             a["flags"], a["ws"], a["wsb"], a["out"], None)
+
+
+def call_fp8_block(s1=P, s2=P, **kw):
+    a = _ffn_args(**kw)
+    return lib.moe_ffn_fp8_block(a["x"], a["w1"], s1, a["w2"], s2, a["ids"], a["wts"],
+                                 a["sid"], a["be"], a["npad"], a["T"], a["E"], a["H"], a["I"],
+                                 a["k"], a["M"], a["flags"], a["ws"], a["wsb"], a["out"], None)
+
+
 def call_f32(**kw):
     a = _ffn_args(**kw)
     return lib.moe_ffn_f32(a["x"], a["w1"], a["w2"], a["ids"], a["wts"], a["sid"], a["be"],
@@ -115,7 +129,7 @@ def call_f32(**kw):
                            a["ws"], a["wsb"], a["out"], None)
 
 
-@pytest.mark.parametrize("call", [call_bf16, call_fp8, call_f32])
+@pytest.mark.parametrize("call", [call_bf16, call_fp8, call_w8a16, call_fp8_block, call_f32])
 def test_ffn_validation(call):
     assert call(H=200) == SHAPE if call is not call_f32 else call(H=202) == SHAPE
     assert call(I=0) == SHAPE
@@ -132,9 +146,42 @@ def test_ffn_validation(call):
     assert call(T=0, x=None, out=None, ws=None) == OK       # empty batch: nothing launched
 
 
-def test_fp8_scale_pointers_validated():
-    assert call_fp8(s1=None) == NULL
-    assert call_fp8(s2=P + 4) == ALIGN
+@pytest.mark.parametrize("call", [call_fp8, call_w8a16])
+def test_fp8_scale_pointers_validated(call):
+    assert call(s1=None) == NULL
+    assert call(s2=P + 4) == ALIGN
+    assert call(T=0, x=None, out=None, ws=None, s1=None, s2=None) == OK
+
+
+def test_block_scale_pointers_validated():
+    assert call_fp8_block(s1=None) == NULL
+    assert call_fp8_block(s2=P + 2) == ALIGN
+
+
+def call_small(logits=P, x=P, w1=P, s1=P, w2=P, s2=P, T=16, E=64, H=4096, I=1536, k=8,
+               renorm=0, dtype=1, flags=0, ids=P, wts=P, ws=P, wsb=1 << 40, out=P):
+    return lib.moe_forward_small(logits, x, w1, s1, w2, s2, T, E, H, I, k, renorm, dtype, flags,
+                                 ids, wts, ws, wsb, out, None)
+
+
+def test_small_path_validation():
+    assert lib.moe_small_max_tokens() == 16
+    assert call_small(T=17) == SHAPE
+    assert call_small(T=16, k=17, E=64) == SHAPE          # T * k > 256
+    assert call_small(E=1025, k=2) == SHAPE
+    assert call_small(H=200) == SHAPE
+    assert call_small(dtype=0) == UNSUP                   # f32
+    assert call_small(dtype=3) == UNSUP
+    assert call_small(flags=1) == UNSUP                   # stage flags are not taken
+    assert call_small(logits=None) == NULL
+    assert call_small(dtype=2, s1=None) == NULL
+    assert call_small(dtype=2, s2=P + 4) == ALIGN
+    assert call_small(ws=P + 64) == ALIGN
+    assert call_small(wsb=100) == WORKSPACE
+    assert call_small(T=0, logits=None, x=None, out=None, ws=None) == OK
+    wsb = lib.moe_forward_small_workspace_bytes
+    assert wsb(16, 64, 4096, 1536, 8, 1) > lib.moe_ffn_workspace_bytes(16, 64, 4096, 1536, 8, 64, 1)
+    assert wsb(17, 64, 4096, 1536, 8, 1) == 0 and wsb(16, 64, 4096, 1536, 8, 0) == 0
 
 
 def test_default_block_m():
@@ -153,5 +200,9 @@ def test_workspace_bytes():
     assert bf >= S * I * 2 + S * H * 2 and bf % 256 == 0      # h, y bf16
     f8 = ws(16, 64, H, I, 8, 64, 2)
     assert f8 >= S * I * 4 + S * I + S * 4 + 16 * H + 16 * 4 + S * H * 4
+    assert ws(16, 64, H, I, 8, 64, 3) == bf                  # W8A16 keeps bf16 intermediates
+    fb = ws(16, 64, H, I, 8, 64, 4)                          # block FP8: group scales
+    assert fb > f8
+    assert fb >= S * I * 4 + S * I + S * (I // 128) * 4 + 16 * H + 16 * (H // 128) * 4 + S * H * 4
     assert ws(16, 64, H, I, 8, 64, 7) == 0
     assert ws(0, 64, H, I, 8, 64, 1) == 0

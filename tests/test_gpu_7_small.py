@@ -1,0 +1,104 @@
+"""GPU checks of the single-launch small-batch forward: parity with the oracle,
+bit-for-bit equality with the separate launches (routing, alignment, FFN) at
+the same T, its status word, determinism, the XCD-remap switch and an empty
+batch."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import make_inputs
+from tests.gpu_util import TOL, cfg_inputs, moe, oracle_forward, out_f64, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _small(inp, renormalize=False, flags=0, workspace=None):
+    m = moe()
+    if workspace is None:
+        dt = m.MOE_DTYPE_FP8 if inp.dtype == "fp8" else m.MOE_DTYPE_BF16
+        n = m.forward_small_workspace_bytes(inp.T, inp.E, inp.H, inp.I, inp.k, dt)
+        workspace = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")  # not zero
+    out, ids, wts = m.forward_small(inp.logits, inp.x, inp.w1, inp.w2, inp.k, renormalize,
+                                    inp.w1_scale, inp.w2_scale, flags, workspace=workspace)
+    torch.cuda.synchronize()
+    status = int(workspace[-4:].view(torch.int32).item())
+    return out, ids, wts, status
+
+
+def _separate(inp, renormalize=False):
+    m = moe()
+    bm = m.default_block_m(inp.T, inp.E, inp.k)
+    ids, w, sid, be, npad = m.route_align(inp.logits, inp.k, bm, renormalize)
+    if inp.dtype == "fp8":
+        out = m.ffn_fp8(inp.x, inp.w1, inp.w1_scale, inp.w2, inp.w2_scale, ids, w, sid, be,
+                        npad, bm)
+    else:
+        out = m.ffn_bf16(inp.x, inp.w1, inp.w2, ids, w, sid, be, npad, bm)
+    torch.cuda.synchronize()
+    return out, ids, w
+
+
+def _check(inp, renormalize=False):
+    out, ids, wts, status = _small(inp, renormalize)
+    assert status == 0, f"device-side barrier wait gave up (status {status})"
+    ids_o, w_o, ref = oracle_forward(inp, renormalize=renormalize)
+    assert np.array_equal(ids.cpu().numpy(), ids_o), "topk_ids differ from the oracle"
+    assert np.max(np.abs(wts.cpu().numpy() - w_o), initial=0.0) <= 1e-5
+    err = oracle.normwise_rel_err(out_f64(out), ref)
+    say(f"  normwise rel err {err:.3e} (tol {TOL[inp.dtype]})")
+    assert err <= TOL[inp.dtype]
+    out_s, ids_s, w_s = _separate(inp, renormalize)
+    assert torch.equal(ids, ids_s) and torch.equal(wts, w_s)
+    assert torch.equal(out.view(torch.int16), out_s.view(torch.int16)), \
+        "single launch differs from the separate launches"
+
+
+@pytest.mark.parametrize("n", [2, 3])
+def test_decode_workloads(n):
+    inp = cfg_inputs(n)
+    say(f"small path config {n} ({inp.dtype}) T={inp.T} E={inp.E} H={inp.H} I={inp.I} k={inp.k}")
+    _check(inp)
+
+
+CASES = [  # T, E, H, I, k, routing
+    (1, 1, 128, 128, 1, "normal"),
+    (5, 4, 128, 256, 4, "normal"),
+    (16, 2, 256, 128, 2, "normal"),
+    (12, 3, 384, 256, 2, "zipf"),
+    (16, 256, 256, 128, 16, "normal"),    # 256 slots: one per thread of a workgroup
+    (7, 1000, 128, 128, 3, "normal"),     # wide router
+    (16, 64, 512, 384, 8, "zipf"),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "T{}_E{}_H{}_I{}_k{}_{}".format(*c))
+def test_small_shapes(case, dtype):
+    T, E, H, I, k, routing = case
+    say(f"small path {dtype} T={T} E={E} H={H} I={I} k={k} {routing}")
+    inp = make_inputs(T, E, H, I, k, dtype=dtype, routing=routing, seed=T + E, device="cuda")
+    _check(inp)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_renormalize_determinism_remap(dtype):
+    m = moe()
+    inp = make_inputs(16, 32, 256, 256, 4, dtype=dtype, routing="normal", seed=3, device="cuda")
+    say(f"small path renormalize/determinism/remap {dtype}")
+    _check(inp, renormalize=True)
+    a = _small(inp)
+    b = _small(inp)
+    c = _small(inp, flags=m.NO_XCD_REMAP)
+    for r in (a, b, c):
+        assert r[3] == 0
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[0].view(torch.int16), c[0].view(torch.int16))
+
+
+def test_empty_batch():
+    m = moe()
+    say("small path T=0")
+    inp = make_inputs(1, 4, 128, 128, 2, dtype="bf16", seed=0, device="cuda")
+    out, ids, wts = m.forward_small(inp.logits[:0], inp.x[:0], inp.w1, inp.w2, 2)
+    assert out.shape == (0, 128) and ids.shape == (0, 2)
