@@ -258,6 +258,8 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     fc1_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]))
+    # per-step durations from the same events: FC1 start of step i to FC1 start of step i+1
+    step_ev = np.array([ev_a[i].elapsed_time(ev_a[i + 1]) for i in range(n_ev - 1)] or [0.0])
 
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
@@ -310,6 +312,7 @@ def main():
     rec = {
         "metric": METRIC, "value": round(T / step_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "step_ms_p10_p50_p90": [round(float(np.percentile(step_ev, q)), 4) for q in (10, 50, 90)],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "w8a16" if wo else inp.dtype,
         "data": "synthetic",
