@@ -171,6 +171,9 @@ def align_block(topk_ids: torch.Tensor, E: int, block_m: int, out=None, stream=N
     return sorted_ids, block_expert, num_padded
 
 
+align = align_block  # the alignment step under its short name
+
+
 def route_align(logits: torch.Tensor, k: int, block_m: int, renormalize: bool = False,
                 out=None, stream=None):
     """Routing and alignment in one call (moe_route_align). logits [T, E] float32.
