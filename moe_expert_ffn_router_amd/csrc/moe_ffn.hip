@@ -706,7 +706,7 @@ __device__ __forceinline__ void w8_kloop(const uint8_t* __restrict__ ap,
 __device__ __forceinline__ int w8_code_off() { return half_split_off(); }
 __device__ __forceinline__ int w8_act_off() { return 2 * half_split_off(); }
 
-constexpr int kW8U = 2;  // code chunks per pipeline group
+constexpr int kW8U = 2;  // code chunks per pipeline group (FC1; FC2's shorter rows take 1)
 
 // Cold FC1 tile r of the W8A16 path (layout as fc1_cold).
 __device__ __forceinline__ void fc1_cold_w8(const Fc1Args& p, int e, int r, int slot) {
@@ -756,7 +756,7 @@ __device__ __forceinline__ void fc2_cold_w8(const Fc2Args& p, int e, int r, int 
     sq = *(const f32x4*)(p.w2s + (size_t)e * p.H + row + 8);
   }
   f32x4 accp = {}, accq = {};
-  w8_kloop<kW8U>(ap, aq, bp, ok, (int)rowq, accp, accq);
+  w8_kloop<1>(ap, aq, bp, ok, (int)rowq, accp, accq);  // short rows: occupancy over depth
   f32x4 vp = diag_sum(accp), vq = diag_sum(accq);
   if (holder && ok) {
 #pragma unroll
@@ -860,7 +860,7 @@ __device__ __forceinline__ void blk_kloop(const uint8_t* __restrict__ ap,
 }
 
 constexpr int kBlk = 128;   // block edge (weights) and group length (activations)
-constexpr int kBlkU = 2;    // lines per pipeline group
+constexpr int kBlkU = 2;    // lines per pipeline group (FC1; FC2's shorter rows take 1)
 
 // Cold FC1 tile r of the block-scaled path (layout as fc1_cold). x: codes
 // [T, H]; xs: group scales [T, H/128]; w1s: block scales [E, 2I/128, H/128].
@@ -899,7 +899,7 @@ __device__ __forceinline__ void fc2_cold_blk(const Fc2Args& p, int e, int r, int
   const float* as = p.hs + (size_t)s * kb;
   const float* ws = p.w2s + ((size_t)e * nb + (r * 16) / kBlk) * kb;
   f32x4 accp = {}, accq = {};
-  blk_kloop<kBlkU>(ap, aq, bp, as, ws, ws, ok, p.I, accp, accq);
+  blk_kloop<1>(ap, aq, bp, as, ws, ws, ok, p.I, accp, accq);  // short rows: occupancy over depth
   const f32x4 vp = diag_sum(accp), vq = diag_sum(accq);
   if ((lane & 8) == 0 && lane < 32 && ok) {
     const int row = r * 16 + 4 * (lane >> 4);
