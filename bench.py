@@ -61,11 +61,16 @@ def parse():
 
 
 def source_digest() -> str:
+    """Hash of the sources the FFN kernels are compiled from (moe_ffn.hip and the
+    headers), so that measured counters stay tied to the kernels they measured."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "moe_expert_ffn_router_amd", "csrc")
     for f in sorted(os.listdir(d)):
-        with open(os.path.join(d, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        if f == "moe_ffn.hip" or f.endswith(".h"):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    with open(os.path.join(ROOT, "include", "moe.h"), "rb") as fh:
+        h.update(b"moe.h" + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -145,7 +150,7 @@ def cpu_baseline(inp, target_s: float, weight_only: bool = False):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (no multi-GPU path); "
+        print("bench.py: one GPU only (the library has no multi-GPU path); "
               "run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 

@@ -54,7 +54,7 @@ typedef enum moe_status {
   MOE_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
   MOE_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
   MOE_ERR_WORKSPACE = 4,   /* workspace too small */
-  MOE_ERR_UNSUPPORTED = 5, /* a valid request this build does not serve */
+  MOE_ERR_UNSUPPORTED = 5, /* a valid request this library does not serve */
   MOE_ERR_HIP = 6          /* a HIP runtime call or launch failed */
 } moe_status;
 

@@ -76,7 +76,7 @@ MOE_EXPORT const char* moe_status_str(moe_status s) {
     case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: a size is out of range or inconsistent";
     case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: a pointer is not suitably aligned";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
-    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: request not served by this build";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: request not served by this library";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP runtime call or kernel launch failed";
   }
   return "MOE_ERR_UNKNOWN: not a moe_status value";
