@@ -28,14 +28,18 @@ constexpr int kAlignMaxE = 1024;
 constexpr int kAlignUnroll = 16;
 constexpr int kFuseMaxTokens = kAlignWaves;  // fused routing + alignment: one token per wave
 constexpr int kFuseMaxSlots = 4096;          // and ids that fit a 16 KB LDS table
+constexpr int kAlignWideWaves = 16;          // align_kernel's width for large batches
+constexpr int kAlignWideSlots = 16384;
 
-// The whole alignment, run by one workgroup of kAlignThreads threads. ids may
-// live in global memory or in LDS; cnt and off are the workgroup's LDS tables.
+// The whole alignment, run by one workgroup of NW waves. ids may live in
+// global memory or in LDS; cnt and off are the workgroup's LDS tables.
+template <int NW>
 __device__ __forceinline__ void align_body(const int32_t* ids, int S, int E, int log2m, int cap,
                                            int32_t* __restrict__ sorted_ids,
                                            int32_t* __restrict__ block_expert,
                                            int32_t* __restrict__ num_padded,
                                            int (*cnt)[kAlignMaxE], int* off) {
+  constexpr int kAlignWaves = NW, kAlignThreads = NW * kWave;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int M = 1 << log2m;
 
@@ -136,13 +140,14 @@ __device__ __forceinline__ void align_body(const int32_t* ids, int S, int E, int
   }
 }
 
-__global__ __launch_bounds__(kAlignThreads) void align_kernel(
+template <int NW>
+__global__ __launch_bounds__(NW * kWave) void align_kernel(
     const int32_t* __restrict__ ids, int S, int E, int log2m, int cap,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
     int32_t* __restrict__ num_padded) {
-  __shared__ int cnt[kAlignWaves][kAlignMaxE];  // per-wave histograms, then per-wave bases
-  __shared__ int off[kAlignMaxE + 1];           // padded exclusive offsets; off[E] = total
-  align_body(ids, S, E, log2m, cap, sorted_ids, block_expert, num_padded, cnt, off);
+  __shared__ int cnt[NW][kAlignMaxE];  // per-wave histograms, then per-wave bases
+  __shared__ int off[kAlignMaxE + 1];  // padded exclusive offsets; off[E] = total
+  align_body<NW>(ids, S, E, log2m, cap, sorted_ids, block_expert, num_padded, cnt, off);
 }
 
 // Routing and alignment of a small batch in one launch: wave w routes token w
@@ -167,7 +172,8 @@ __global__ __launch_bounds__(kAlignThreads) void route_align_kernel(
     route_token<VPL>(v, t, E, k, renorm, ids, wts, ids_lds);
   }
   __syncthreads();
-  align_body(ids_lds, T * k, E, log2m, cap, sorted_ids, block_expert, num_padded, cnt, off);
+  align_body<kAlignWaves>(ids_lds, T * k, E, log2m, cap, sorted_ids, block_expert, num_padded,
+                          cnt, off);
 }
 
 static int ilog2_align(int block_m) {
@@ -210,8 +216,12 @@ hipError_t launch_align(const int32_t* ids, int S, int E, int block_m, int cap,
                         hipStream_t stream) {
   int log2m = 0;
   while ((1 << log2m) < block_m) ++log2m;
-  align_kernel<<<1, kAlignThreads, 0, stream>>>(ids, S, E, log2m, cap, sorted_ids, block_expert,
-                                                num_padded);
+  if (S >= kAlignWideSlots)  // many slots: 16 waves share the two passes over them
+    align_kernel<kAlignWideWaves><<<1, kAlignWideWaves * kWave, 0, stream>>>(
+        ids, S, E, log2m, cap, sorted_ids, block_expert, num_padded);
+  else
+    align_kernel<kAlignWaves><<<1, kAlignThreads, 0, stream>>>(ids, S, E, log2m, cap, sorted_ids,
+                                                               block_expert, num_padded);
   return hipGetLastError();
 }
 
