@@ -266,6 +266,20 @@ def main():
     # per-step durations from the same events: FC1 start of step i to FC1 start of step i+1
     step_ev = np.array([ev_a[i].elapsed_time(ev_a[i + 1]) for i in range(n_ev - 1)] or [0.0])
 
+    # after the timed region: the FFN launches alone (FC1 + FC2 + combine, routing and
+    # alignment already in place), each bracketed by its own events
+    ffn_ev = None
+    if not args.single_launch:
+        n_f = min(50, args.steps)
+        fa = [torch.cuda.Event(enable_timing=True) for _ in range(n_f)]
+        fb = [torch.cuda.Event(enable_timing=True) for _ in range(n_f)]
+        for i in range(n_f):
+            fa[i].record(stream)
+            ffn(0)
+            fb[i].record(stream)
+        torch.cuda.synchronize()
+        ffn_ev = np.array([a.elapsed_time(b) for a, b in zip(fa, fb)])
+
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -318,6 +332,8 @@ def main():
         "metric": METRIC, "value": round(T / step_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "step_ms_p10_p50_p90": [round(float(np.percentile(step_ev, q)), 4) for q in (10, 50, 90)],
+        "ffn_only_ms_p10_p50_p90": None if ffn_ev is None else
+        [round(float(np.percentile(ffn_ev, q)), 4) for q in (10, 50, 90)],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "w8a16" if wo else inp.dtype,
         "data": "synthetic",
