@@ -50,7 +50,11 @@ def parse():
                     help="FP8 workloads: weights quantised per 128x128 block (same master "
                          "weights), activations per 128-element group")
     ap.add_argument("--single-launch", action="store_true",
-                    help="T <= 16: the whole layer as one cooperative launch (moe_forward_small)")
+                    help="T <= 16: the whole layer as one cooperative launch (moe_forward_small "
+                         "with FORWARD_ONE_KERNEL)")
+    ap.add_argument("--small-path", action="store_true",
+                    help="T <= 16: the whole layer through moe_forward_small's separate "
+                         "launches (no alignment step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
@@ -223,9 +227,11 @@ def main():
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
 
-    if args.single_launch:
+    small = args.single_launch or args.small_path
+    small_flags = args.flags | (moe.FORWARD_ONE_KERNEL if args.single_launch else 0)
+    if small:
         if wo or blk or args.ep > 1 or args.tp > 1 or T > moe.small_max_tokens():
-            sys.exit("bench.py: --single-launch takes an unsharded bf16/fp8 workload of at "
+            sys.exit("bench.py: --single-launch/--small-path take an unsharded bf16/fp8 workload of at "
                      f"most {moe.small_max_tokens()} tokens")
         ws_small = torch.empty(moe.forward_small_workspace_bytes(T, E, H, I, k, dt_code),
                                dtype=torch.uint8, device=dev)
@@ -233,13 +239,13 @@ def main():
     def step_small(i=None):
         if i is not None:
             ev_a[i].record(stream)
-        moe.forward_small(inp.logits, inp.x, w1, w2, k, False, s1, s2, args.flags, out, ids,
+        moe.forward_small(inp.logits, inp.x, w1, w2, k, False, s1, s2, small_flags, out, ids,
                           wts, ws_small, stream)
         if i is not None:
             ev_b[i].record(stream)
 
     def step(i=None):
-        if args.single_launch:
+        if small:
             return step_small(i)
         if E == Eg:
             moe.route_align(inp.logits, k, M, out=(ids, wts, sid, be, npad), stream=stream)
@@ -269,7 +275,7 @@ def main():
     # after the timed region: the FFN launches alone (FC1 + FC2 + combine, routing and
     # alignment already in place), each bracketed by its own events
     ffn_ev = None
-    if not args.single_launch:
+    if not small:
         n_f = min(50, args.steps)
         fa = [torch.cuda.Event(enable_timing=True) for _ in range(n_f)]
         fb = [torch.cuda.Event(enable_timing=True) for _ in range(n_f)]
@@ -305,7 +311,8 @@ def main():
     fc1_gbs = fc1_bytes / (fc1_ms * 1e-3) / 1e9
     step_s = ms_per_step * 1e-3
     wl = cfg["name"] + ("_w8a16" if wo else "") + ("_block128" if blk else "") \
-        + ("_single_launch" if args.single_launch else "") + (f"_ep{args.ep}_rank0" if args.ep > 1 else "") \
+        + ("_single_launch" if args.single_launch else "") \
+        + ("_small_path" if args.small_path else "") + (f"_ep{args.ep}_rank0" if args.ep > 1 else "") \
         + (f"_tp{args.tp}_rank0" if args.tp > 1 else "")
     if args.single_launch:  # one kernel for the whole layer: its bytes over its duration
         gbs = layer_bytes / (fc1_ms * 1e-3) / 1e9
@@ -313,6 +320,13 @@ def main():
                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                     "traffic": measured_traffic("small_forward", wl),
                     "kernel": "small_forward (whole layer, one launch)",
+                    "kernel_ms": round(fc1_ms, 4), "alg_bytes_per_launch": layer_bytes}
+    elif args.small_path:  # events bracket the whole call: its bytes over the call's time
+        gbs = layer_bytes / (fc1_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "traffic": None,
+                    "kernel": "moe_forward_small (whole layer: route, FC1, FC2, combine)",
                     "kernel_ms": round(fc1_ms, 4), "alg_bytes_per_launch": layer_bytes}
     elif M >= 128:  # grouped-GEMM tiles (prefill-sized blocks): FC1 is bound by MFMA
         fc1_flops = S_loc * 2 * I * H * 2

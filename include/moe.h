@@ -80,6 +80,8 @@ enum {
 #define MOE_FFN_STAGE_FC2 (1u << 1)
 #define MOE_FFN_STAGE_COMBINE (1u << 2)
 #define MOE_FFN_NO_XCD_REMAP (1u << 8)
+/* moe_forward_small only: run the whole layer as one cooperative kernel */
+#define MOE_FORWARD_ONE_KERNEL (1u << 9)
 
 /* Human-readable name of a status (static storage, never NULL). */
 const char* moe_status_str(moe_status s);
@@ -293,14 +295,18 @@ moe_status moe_ffn_f32(const float* x, const float* w1, const float* w2,
                        float* out, moe_stream_t stream);
 
 /*
- * Single-launch forward of a small batch: router softmax + top-k, alignment,
- * FC1 + SiLU*up, FC2 and the combine in one cooperative persistent kernel
- * (plus a 256-thread kernel that clears its barrier words). Passage: "vLLM SM
- * architecture adaptation", section 4.3: for a batch of at most 8 tokens the
- * grouped-GEMM path's launch overhead is what a single-kernel path avoids.
- * Results equal, bit for bit, moe_route_topk -> moe_align_block ->
- * moe_ffn_bf16 / moe_ffn_fp8 at the same T (any block_m): every expert's
- * slots are served by the same 8-token streaming passes.
+ * Forward of a small batch: router softmax + top-k, FC1 + SiLU*up, FC2 and
+ * the combine without an alignment step. By default as separate launches
+ * (routing; fp8: x quantiser; FC1; fp8: h quantiser; FC2; combine) in which
+ * FC1 and FC2 each group the slots by expert in LDS from the routed ids, so
+ * no alignment kernel runs. With MOE_FORWARD_ONE_KERNEL the whole layer is
+ * one cooperative persistent kernel (plus a 256-thread kernel that clears its
+ * barrier words). Passage: "vLLM SM architecture adaptation", section 4.3:
+ * for a batch of at most 8 tokens the grouped-GEMM path's launch overhead is
+ * what a single-kernel path avoids. Either way the results equal, bit for
+ * bit, moe_route_topk -> moe_align_block -> moe_ffn_bf16 / moe_ffn_fp8 at
+ * the same T (any block_m): every expert's slots are served by the same
+ * 8-token streaming passes.
  *
  *  logits        [T, E] fp32; renormalize as in moe_route_topk.
  *  x             [T, H] bf16.
@@ -310,15 +316,17 @@ moe_status moe_ffn_f32(const float* x, const float* w1, const float* w2,
  *  topk_ids, topk_weights   [T, k], written (as moe_route_topk).
  *  out           [T, H] bf16, written.
  *  workspace     moe_forward_small_workspace_bytes(T, E, H, I, k, dtype)
- *                bytes, 256-byte aligned, no initialisation needed. Its last
- *                4 bytes are a status word: 0 after the call has run, nonzero
- *                if a device-side barrier wait gave up (out is then
- *                undefined; not expected, the launch guarantees residency).
- *  flags         0 or MOE_FFN_NO_XCD_REMAP.
+ *                bytes (or more), 256-byte aligned, no initialisation needed.
+ *                With MOE_FORWARD_ONE_KERNEL the last 4 of those bytes are a
+ *                status word:
+ *                0 after the call has run, nonzero if a device-side barrier
+ *                wait gave up (out is then undefined; not expected, the launch
+ *                guarantees residency).
+ *  flags         0 or MOE_FFN_NO_XCD_REMAP, optionally | MOE_FORWARD_ONE_KERNEL.
  *  Limits: 0 <= T <= moe_small_max_tokens() (16), 1 <= E <= 1024,
  *  1 <= k <= E, T * k <= 256, H and I multiples of 128. Returns
  *  MOE_ERR_SHAPE beyond them, MOE_ERR_UNSUPPORTED for another dtype or flag,
- *  MOE_ERR_HIP if the cooperative launch is refused. Calls that share a
+ *  MOE_ERR_HIP if a launch (the cooperative one) is refused. Calls that share a
  *  workspace must not overlap in time.
  */
 int moe_small_max_tokens(void);

@@ -32,6 +32,7 @@ MOE_OK = 0
 MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_FP8, MOE_DTYPE_W8A16, MOE_DTYPE_FP8_BLOCK = 0, 1, 2, 3, 4
 STAGE_FC1, STAGE_FC2, STAGE_COMBINE = 1 << 0, 1 << 1, 1 << 2
 NO_XCD_REMAP = 1 << 8
+FORWARD_ONE_KERNEL = 1 << 9  # forward_small: the whole layer as one cooperative launch
 ABI_VERSION = 1
 
 EXPORTS = ("moe_status_str", "moe_abi_version", "moe_route_topk", "moe_align_capacity",
@@ -345,8 +346,10 @@ def forward_small_workspace_bytes(T, E, H, I, k, dtype) -> int:
 def forward_small(logits, x, w1, w2, k: int, renormalize: bool = False, w1_scale=None,
                   w2_scale=None, flags: int = 0, out=None, topk_ids=None, topk_weights=None,
                   workspace=None, stream=None):
-    """moe_forward_small: the whole layer for T <= small_max_tokens() in one launch.
-    bf16 weights, or e4m3fn codes with per-row float32 scales (W8A8). Returns
+    """moe_forward_small: the whole layer for T <= small_max_tokens() without an
+    alignment step (separate launches; one cooperative launch with
+    flags | FORWARD_ONE_KERNEL). bf16 weights, or e4m3fn codes with per-row
+    float32 scales (W8A8). Returns
     (out [T,H] bfloat16, topk_ids [T,k] int32, topk_weights [T,k] float32)."""
     fp8 = w1.dtype in (torch.uint8, torch.float8_e4m3fn)
     wdt = (torch.uint8, torch.float8_e4m3fn) if fp8 else (torch.bfloat16,)

@@ -158,7 +158,7 @@ static moe_status check_small(int T, int E, int H, int I, int k, int dtype, unsi
   if (T > moe::kSmallTokens || E > moe::kSmallExperts || (long)T * k > moe::kSmallSlots)
     return MOE_ERR_SHAPE;
   if (H < 128 || I < 128 || H % 128 != 0 || I % 128 != 0) return MOE_ERR_SHAPE;
-  if (flags & ~(unsigned)MOE_FFN_NO_XCD_REMAP) return MOE_ERR_UNSUPPORTED;
+  if (flags & ~(unsigned)(MOE_FFN_NO_XCD_REMAP | MOE_FORWARD_ONE_KERNEL)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

@@ -1767,11 +1767,60 @@ __device__ __forceinline__ void small_plan(const int32_t* __restrict__ ids, int 
   __syncthreads();
 }
 
+// FC1 over (unit, quad) shares: a quad is 4 tiles of 8 h columns, one per wave.
+// WT: device-scope stores (the reader is in the same kernel on another XCD).
+template <bool FP8, bool WT>
+__device__ __forceinline__ void small_fc1(const SmallArgs& a, const SmallPlan& P) {
+  const int w = threadIdx.x >> 6, ti = threadIdx.x & 7;
+  const int S = a.T * a.k;
+  const Fc1Args f{FP8 ? (const void*)a.xq : (const void*)a.x, a.xs, a.w1, a.w1s, nullptr,
+                  nullptr, nullptr, a.H, a.I, a.k, S, 0, a.remap, a.h, nullptr};
+  const int qpu = a.I >> 5;
+  const Share sh = wg_share((long)P.nunits * qpu, a.remap);
+  for (long qd = sh.q0; qd < sh.q1; ++qd) {
+    const int u = (int)(qd / qpu), r = (int)(qd % qpu) * 4 + w;
+    const int slot = ti < P.ulen[u] ? P.sorted[P.upos[u] + ti] : S;
+    fc1_cold<FP8, cold_u<FP8, false>(), WT>(f, P.ue[u], r, slot);
+  }
+}
+
+// FC2 over (unit, quad) shares: a quad is 4 tiles of 16 output rows.
+template <bool FP8, bool WT>
+__device__ __forceinline__ void small_fc2(const SmallArgs& a, const SmallPlan& P) {
+  const int w = threadIdx.x >> 6, ti = threadIdx.x & 7;
+  const int S = a.T * a.k;
+  const Fc2Args f{FP8 ? (const void*)a.hq : (const void*)a.h, a.hs, a.w2, a.w2s, nullptr,
+                  nullptr, nullptr, a.H, a.I, S, 0, a.remap, a.y, FP8 ? 0 : 1, nullptr};
+  const int qpu = a.H >> 6;
+  const Share sh = wg_share((long)P.nunits * qpu, a.remap);
+  for (long qd = sh.q0; qd < sh.q1; ++qd) {
+    const int u = (int)(qd / qpu), r = (int)(qd % qpu) * 4 + w;
+    const int slot = ti < P.ulen[u] ? P.sorted[P.upos[u] + ti] : S;
+    fc2_cold<FP8, cold_u<FP8, false>(), WT>(f, P.ue[u], r, slot);
+  }
+}
+
+// The split form of the small path: FC1 and FC2 as launches of their own that
+// each rebuild the plan from the routed ids (one launch per step and no
+// alignment kernel: the routed ids are all they need).
+template <bool FP8>
+__global__ __launch_bounds__(256) void small_fc1_kernel(SmallArgs a) {
+  __shared__ SmallPlan P;
+  small_plan(a.ids, a.T * a.k, a.E, P);
+  small_fc1<FP8, false>(a, P);
+}
+template <bool FP8>
+__global__ __launch_bounds__(256) void small_fc2_kernel(SmallArgs a) {
+  __shared__ SmallPlan P;
+  small_plan(a.ids, a.T * a.k, a.E, P);
+  small_fc2<FP8, false>(a, P);
+}
+
 template <bool FP8, int VPL>
 __global__ __launch_bounds__(256) void small_forward_kernel(SmallArgs a) {
   __shared__ SmallPlan P;
   GridSync gs{a.bar};
-  const int w = threadIdx.x >> 6, ti = threadIdx.x & 7;
+  const int w = threadIdx.x >> 6;
   const int gw = blockIdx.x * 4 + w;  // global wave
   const int nw = gridDim.x * 4;
   const int S = a.T * a.k;
@@ -1786,17 +1835,7 @@ __global__ __launch_bounds__(256) void small_forward_kernel(SmallArgs a) {
   }
   gs.sync();
   small_plan(a.ids, S, a.E, P);
-  {  // FC1: units x quads of 4 tiles of 8 h columns
-    const Fc1Args f{FP8 ? (const void*)a.xq : (const void*)a.x, a.xs, a.w1, a.w1s, nullptr,
-                    nullptr, nullptr, a.H, a.I, a.k, S, 0, a.remap, a.h, nullptr};
-    const int qpu = a.I >> 5;
-    const Share sh = wg_share((long)P.nunits * qpu, a.remap);
-    for (long qd = sh.q0; qd < sh.q1; ++qd) {
-      const int u = (int)(qd / qpu), r = (int)(qd % qpu) * 4 + w;
-      const int slot = ti < P.ulen[u] ? P.sorted[P.upos[u] + ti] : S;
-      fc1_cold<FP8, cold_u<FP8, false>(), true>(f, P.ue[u], r, slot);
-    }
-  }
+  small_fc1<FP8, true>(a, P);
   gs.sync();
   if constexpr (FP8) {
     for (int r = gw; r < S; r += nw)
@@ -1804,17 +1843,7 @@ __global__ __launch_bounds__(256) void small_forward_kernel(SmallArgs a) {
                              a.hs + r);
     gs.sync();
   }
-  {  // FC2: units x quads of 4 tiles of 16 output rows
-    const Fc2Args f{FP8 ? (const void*)a.hq : (const void*)a.h, a.hs, a.w2, a.w2s, nullptr,
-                    nullptr, nullptr, a.H, a.I, S, 0, a.remap, a.y, FP8 ? 0 : 1, nullptr};
-    const int qpu = a.H >> 6;
-    const Share sh = wg_share((long)P.nunits * qpu, a.remap);
-    for (long qd = sh.q0; qd < sh.q1; ++qd) {
-      const int u = (int)(qd / qpu), r = (int)(qd % qpu) * 4 + w;
-      const int slot = ti < P.ulen[u] ? P.sorted[P.upos[u] + ti] : S;
-      fc2_cold<FP8, cold_u<FP8, false>(), true>(f, P.ue[u], r, slot);
-    }
-  }
+  small_fc2<FP8, true>(a, P);
   gs.sync();
   const long n8 = (long)a.T * (a.H >> 3);
   for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long)gridDim.x * 256) {
@@ -2079,6 +2108,42 @@ static hipError_t launch_small(const SmallProblem& p, const SmallArgs& a, hipStr
   return go(small_forward_kernel<FP8, 16>, base + 2);
 }
 
+// The split small path: route, (fp8: quantise x), FC1, (fp8: quantise h), FC2,
+// combine, each its own launch; FC1 and FC2 plan from the routed ids.
+template <bool FP8>
+static hipError_t launch_small_split(const SmallProblem& p, const SmallArgs& a,
+                                     hipStream_t stream) {
+  hipError_t err;
+  if ((err = launch_route_topk(p.logits, p.T, p.E, p.k, p.renorm, p.ids, p.wts, stream)) !=
+      hipSuccess)
+    return err;
+  const int S = p.T * p.k;
+  if (FP8) {
+    quant_rows_kernel<uint16_t><<<(p.T + 3) / 4, 256, 0, stream>>>(a.x, p.T, p.H, a.xq, a.xs);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  small_fc1_kernel<FP8><<<persistent_grid(small_fc1_kernel<FP8>, FP8 ? 24 : 22), 256, 0,
+                          stream>>>(a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (FP8) {
+    quant_rows_kernel<float><<<(S + 3) / 4, 256, 0, stream>>>((const float*)a.h, S, p.I, a.hq,
+                                                              a.hs);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  small_fc2_kernel<FP8><<<persistent_grid(small_fc2_kernel<FP8>, FP8 ? 25 : 23), 256, 0,
+                          stream>>>(a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const long n8 = (long)p.T * (p.H / 8);
+  const dim3 grid((unsigned)((n8 + 255) / 256));
+  if (FP8)
+    combine_kernel<float, uint16_t><<<grid, 256, 0, stream>>>(
+        (const float*)a.y, p.wts, p.ids, p.E, p.T, p.H, p.k, (uint16_t*)p.out);
+  else
+    combine_kernel<uint16_t, uint16_t><<<grid, 256, 0, stream>>>(
+        (const uint16_t*)a.y, p.wts, p.ids, p.E, p.T, p.H, p.k, (uint16_t*)p.out);
+  return hipGetLastError();
+}
+
 hipError_t launch_forward_small(const SmallProblem& p, hipStream_t stream) {
   const bool fp8 = p.dtype == MOE_DTYPE_FP8;
   const FfnWorkspace L = ffn_workspace_layout(p.T, p.H, p.I, p.k, p.dtype);
@@ -2091,6 +2156,8 @@ hipError_t launch_forward_small(const SmallProblem& p, hipStream_t stream) {
               ws + L.h_off,
               fp8 ? (uint8_t*)(ws + L.hq_off) : nullptr, fp8 ? (float*)(ws + L.hs_off) : nullptr,
               ws + L.y_off, (uint16_t*)p.out, bar};
+  if (!(p.flags & MOE_FORWARD_ONE_KERNEL))
+    return fp8 ? launch_small_split<true>(p, a, stream) : launch_small_split<false>(p, a, stream);
   zero_counters_kernel<<<1, 256, 0, stream>>>(bar, kBarInts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

@@ -173,6 +173,7 @@ def test_small_path_validation():
     assert call_small(dtype=0) == UNSUP                   # f32
     assert call_small(dtype=3) == UNSUP
     assert call_small(flags=1) == UNSUP                   # stage flags are not taken
+    assert call_small(flags=1 << 10) == UNSUP
     assert call_small(logits=None) == NULL
     assert call_small(dtype=2, s1=None) == NULL
     assert call_small(dtype=2, s2=P + 4) == ALIGN

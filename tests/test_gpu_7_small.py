@@ -1,7 +1,7 @@
-"""GPU checks of the single-launch small-batch forward: parity with the oracle,
-bit-for-bit equality with the separate launches (routing, alignment, FFN) at
-the same T, its status word, determinism, the XCD-remap switch and an empty
-batch."""
+"""GPU checks of the small-batch forward, in both of its modes (separate
+launches without alignment, and one cooperative launch): parity with the
+oracle, bit-for-bit equality with routing + alignment + FFN at the same T, the
+one-kernel status word, determinism, the XCD-remap switch and an empty batch."""
 import numpy as np
 import pytest
 import torch
@@ -13,16 +13,21 @@ from tests.gpu_util import TOL, cfg_inputs, moe, oracle_forward, out_f64, say
 pytestmark = pytest.mark.gpu
 
 
+MODES = ["split", "one_kernel"]
+
+
 def _small(inp, renormalize=False, flags=0, workspace=None):
     m = moe()
+    dt = m.MOE_DTYPE_FP8 if inp.dtype == "fp8" else m.MOE_DTYPE_BF16
+    n = m.forward_small_workspace_bytes(inp.T, inp.E, inp.H, inp.I, inp.k, dt)
     if workspace is None:
-        dt = m.MOE_DTYPE_FP8 if inp.dtype == "fp8" else m.MOE_DTYPE_BF16
-        n = m.forward_small_workspace_bytes(inp.T, inp.E, inp.H, inp.I, inp.k, dt)
         workspace = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")  # not zero
     out, ids, wts = m.forward_small(inp.logits, inp.x, inp.w1, inp.w2, inp.k, renormalize,
                                     inp.w1_scale, inp.w2_scale, flags, workspace=workspace)
     torch.cuda.synchronize()
-    status = int(workspace[-4:].view(torch.int32).item())
+    # the status word is written by the one-kernel mode only
+    # (the last 4 of the n bytes this batch needs, also in a larger workspace)
+    status = int(workspace[n - 4:n].view(torch.int32).item()) if flags & m.FORWARD_ONE_KERNEL else 0
     return out, ids, wts, status
 
 
@@ -39,8 +44,12 @@ def _separate(inp, renormalize=False):
     return out, ids, w
 
 
-def _check(inp, renormalize=False):
-    out, ids, wts, status = _small(inp, renormalize)
+def _flags(mode):
+    return moe().FORWARD_ONE_KERNEL if mode == "one_kernel" else 0
+
+
+def _check(inp, mode, renormalize=False):
+    out, ids, wts, status = _small(inp, renormalize, flags=_flags(mode))
     assert status == 0, f"device-side barrier wait gave up (status {status})"
     ids_o, w_o, ref = oracle_forward(inp, renormalize=renormalize)
     assert np.array_equal(ids.cpu().numpy(), ids_o), "topk_ids differ from the oracle"
@@ -51,14 +60,16 @@ def _check(inp, renormalize=False):
     out_s, ids_s, w_s = _separate(inp, renormalize)
     assert torch.equal(ids, ids_s) and torch.equal(wts, w_s)
     assert torch.equal(out.view(torch.int16), out_s.view(torch.int16)), \
-        "single launch differs from the separate launches"
+        f"small path ({mode}) differs from routing + alignment + FFN"
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("n", [2, 3])
-def test_decode_workloads(n):
+def test_decode_workloads(n, mode):
     inp = cfg_inputs(n)
-    say(f"small path config {n} ({inp.dtype}) T={inp.T} E={inp.E} H={inp.H} I={inp.I} k={inp.k}")
-    _check(inp)
+    say(f"small path {mode} config {n} ({inp.dtype}) T={inp.T} E={inp.E} H={inp.H} I={inp.I} "
+        f"k={inp.k}")
+    _check(inp, mode)
 
 
 CASES = [  # T, E, H, I, k, routing
@@ -72,33 +83,56 @@ CASES = [  # T, E, H, I, k, routing
 ]
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "T{}_E{}_H{}_I{}_k{}_{}".format(*c))
-def test_small_shapes(case, dtype):
+def test_small_shapes(case, dtype, mode):
     T, E, H, I, k, routing = case
-    say(f"small path {dtype} T={T} E={E} H={H} I={I} k={k} {routing}")
+    say(f"small path {mode} {dtype} T={T} E={E} H={H} I={I} k={k} {routing}")
     inp = make_inputs(T, E, H, I, k, dtype=dtype, routing=routing, seed=T + E, device="cuda")
-    _check(inp)
+    _check(inp, mode)
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-def test_renormalize_determinism_remap(dtype):
+def test_renormalize_determinism_remap(dtype, mode):
     m = moe()
+    f = _flags(mode)
     inp = make_inputs(16, 32, 256, 256, 4, dtype=dtype, routing="normal", seed=3, device="cuda")
-    say(f"small path renormalize/determinism/remap {dtype}")
-    _check(inp, renormalize=True)
-    a = _small(inp)
-    b = _small(inp)
-    c = _small(inp, flags=m.NO_XCD_REMAP)
+    say(f"small path {mode} renormalize/determinism/remap {dtype}")
+    _check(inp, mode, renormalize=True)
+    a = _small(inp, flags=f)
+    b = _small(inp, flags=f)
+    c = _small(inp, flags=f | m.NO_XCD_REMAP)
     for r in (a, b, c):
         assert r[3] == 0
     assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
     assert torch.equal(a[0].view(torch.int16), c[0].view(torch.int16))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_modes_agree_on_a_reused_workspace(dtype):
+    """Both modes on one workspace, alternating, with a smaller batch second:
+    no state carries from one call to the next."""
+    m = moe()
+    say(f"small path modes on a shared workspace {dtype}")
+    big = make_inputs(16, 64, 256, 256, 8, dtype=dtype, routing="zipf", seed=11, device="cuda")
+    small = make_inputs(3, 64, 256, 256, 8, dtype=dtype, routing="normal", seed=12, device="cuda")
+    code = m.MOE_DTYPE_FP8 if dtype == "fp8" else m.MOE_DTYPE_BF16
+    n = m.forward_small_workspace_bytes(16, 64, 256, 256, 8, code)
+    ws = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")
+    ref = {id(big): _separate(big)[0], id(small): _separate(small)[0]}
+    for inp in (big, small, big, small):
+        for mode in ("one_kernel", "split"):
+            out, _, _, status = _small(inp, flags=_flags(mode), workspace=ws)
+            assert status == 0
+            assert torch.equal(out.view(torch.int16), ref[id(inp)].view(torch.int16)), mode
+
+
 def test_empty_batch():
     m = moe()
     say("small path T=0")
     inp = make_inputs(1, 4, 128, 128, 2, dtype="bf16", seed=0, device="cuda")
-    out, ids, wts = m.forward_small(inp.logits[:0], inp.x[:0], inp.w1, inp.w2, 2)
-    assert out.shape == (0, 128) and ids.shape == (0, 2)
+    for f in (0, m.FORWARD_ONE_KERNEL):
+        out, ids, wts = m.forward_small(inp.logits[:0], inp.x[:0], inp.w1, inp.w2, 2, flags=f)
+        assert out.shape == (0, 128) and ids.shape == (0, 2)
