@@ -31,6 +31,7 @@
 #include "moe_launch.h"
 #include "moe_route_dev.h"
 
+#include <map>
 #include <mutex>
 
 #include "../../include/moe.h"
@@ -52,9 +53,14 @@ struct Share {
   long q0, q1;
 };
 
+// Fewer units than workgroups: unit i goes to workgroup i, so consecutive
+// units land on different XCDs and, within an XCD, on different CUs (equal
+// contiguous shares would give the units to every other workgroup, which the
+// dispatcher packs onto every other CU).
 __device__ __forceinline__ Share wg_share(long total, int remap) {
   int wg = blockIdx.x;
   const int G = gridDim.x;
+  if (total < G) return wg < total ? Share{wg, wg + 1} : Share{0, 0};
   if (remap && (G & 7) == 0) wg = (wg & 7) * (G >> 3) + (wg >> 3);
   return {total * wg / G, total * (wg + 1) / G};
 }
@@ -457,6 +463,71 @@ __device__ __forceinline__ void fc1_cold(const Fc1Args& p, int e, int r, int slo
       }
     }
     store_h<FP8, WT>(p, slot, col, g, u);
+  }
+}
+
+// K slices of a cold tile shared by the 4 waves of a workgroup: wave w takes
+// chunks [kslice(n, w), kslice(n, w + 1)) of the n chunks of a row (the last
+// slice also takes a trailing half chunk).
+__device__ __forceinline__ int kslice(int n, int w) { return (w * n) >> 2; }
+
+// LDS of the sliced cold tiles: two buffers of [wave][P|Q][lane] partial
+// accumulators, alternating from one tile to the next.
+constexpr int kRedF4 = 4 * 2 * 64;
+
+// Cold FC1 tile r (as fc1_cold) computed by all 4 waves of the workgroup,
+// each over a quarter of K; the partial accumulators are summed in wave order
+// by wave (j & 3), which finishes the tile. j counts the workgroup's sliced
+// tiles (same on every wave); `slot` is this lane's token slot.
+template <bool FP8, int U, bool WT = false>
+__device__ __forceinline__ void fc1_cold_sliced(const Fc1Args& p, int e, int r, int slot,
+                                                f32x4* __restrict__ red, int j) {
+  constexpr int CH = Cold<FP8>::kChunk;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const size_t rowb = (size_t)p.H * (FP8 ? 1 : 2);
+  const int nch = (int)(rowb / CH);
+  const int c0 = kslice(nch, w), c1 = kslice(nch, w + 1);
+  const int kb = (c1 - c0) * CH + (w == 3 ? (int)(rowb % CH) : 0);
+  const int off = half_split_off() + c0 * CH;
+  const uint8_t* wb = (const uint8_t*)p.w1 + (size_t)e * 2 * p.I * rowb;
+  const uint8_t* ap = wb + (size_t)(r * 8 + (lane & 7)) * rowb + off;
+  const uint8_t* aq = wb + (size_t)(p.I + r * 8 + (lane & 7)) * rowb + off;
+  const bool ok = slot < p.S;
+  const uint8_t* bp = (const uint8_t*)p.x + (size_t)(ok ? slot / p.k : 0) * rowb + off;
+  const bool fin = w == (j & 3);
+  const bool holder = (lane & 8) == 0 && lane < 32;
+  const int col = r * 8 + 4 * (lane >> 4);
+  float xs = 1.f;
+  f32x4 sg = {1.f, 1.f, 1.f, 1.f}, su = sg;
+  if (FP8 && fin && holder && ok) {
+    xs = p.xs[slot / p.k];
+    sg = *(const f32x4*)(p.w1s + (size_t)e * 2 * p.I + col);
+    su = *(const f32x4*)(p.w1s + (size_t)e * 2 * p.I + p.I + col);
+  }
+  f32x4 accp = {}, accq = {};
+  cold_kloop<FP8, U>(ap, aq, bp, ok, kb, accp, accq);
+  f32x4* buf = red + (j & 1) * kRedF4;
+  buf[(2 * w) * 64 + lane] = accp;
+  buf[(2 * w + 1) * 64 + lane] = accq;
+  __syncthreads();
+  if (fin) {
+    f32x4 sp = buf[lane], sq = buf[64 + lane];
+#pragma unroll
+    for (int v = 1; v < 4; ++v) {
+      sp += buf[(2 * v) * 64 + lane];
+      sq += buf[(2 * v + 1) * 64 + lane];
+    }
+    f32x4 g = diag_sum(sp), u = diag_sum(sq);
+    if (holder && ok) {
+      if (FP8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          g[i] *= sg[i] * xs;
+          u[i] *= su[i] * xs;
+        }
+      }
+      store_h<FP8, WT>(p, slot, col, g, u);
+    }
   }
 }
 
@@ -994,6 +1065,32 @@ __global__ __launch_bounds__(256) void fc1_kernel(Fc1Args p) {
   run_quads<FP8, HOT, false, Fc1Args, fc1_cold<FP8, cold_u<FP8, HOT>()>, fc1_hot_pass<FP8, 1>,
             fc1_hot_pass<FP8, 2>,
             fc1_hot_pass<FP8, 3>, fc1_hot_pass<FP8, 4>>(p, p.I >> 3, lds);
+}
+
+// Cold-only FC1 launch (T <= 16 tokens): the work list is (block, tile) and
+// the 4 waves of a workgroup compute each tile together, one K quarter each,
+// so four times as many waves stream weights as with one tile per wave, each
+// along a dependent load chain a quarter as long. Blocks of more than 8 tokens
+// run one such tile per 8 tokens.
+template <bool FP8>
+__global__ __launch_bounds__(256) void fc1_sliced_kernel(Fc1Args p) {
+  __shared__ f32x4 red[2 * kRedF4];
+  const int M = 1 << p.log2m, nb = p.num_padded[0] >> p.log2m, tpb = p.I >> 3;
+  const int ti = threadIdx.x & 7;
+  const Share sh = wg_share((long)nb * tpb, p.remap);
+  int j = 0, cur_b = -1, e = 0, m = 0;
+  for (long u = sh.q0; u < sh.q1; ++u) {
+    const int b = (int)(u / tpb), r = (int)(u % tpb);
+    if (b != cur_b) {
+      cur_b = b;
+      e = p.block_expert[b];
+      m = block_valid(p.sorted_ids, b, M, p.S);
+    }
+    for (int t0 = 0; t0 < m; t0 += kColdMax, ++j) {
+      const int slot = t0 + ti < m ? p.sorted_ids[(size_t)b * M + t0 + ti] : p.S;
+      fc1_cold_sliced<FP8, cold_u<FP8, false>()>(p, e, r, slot, red, j);
+    }
+  }
 }
 
 template <bool FP8, bool HOT>
@@ -1767,20 +1864,23 @@ __device__ __forceinline__ void small_plan(const int32_t* __restrict__ ids, int 
   __syncthreads();
 }
 
-// FC1 over (unit, quad) shares: a quad is 4 tiles of 8 h columns, one per wave.
+// FC1 over (unit, tile) shares, each tile of 8 h columns K-sliced over the 4
+// waves (as in the cold-only FC1 launch, so the results are the same bits).
 // WT: device-scope stores (the reader is in the same kernel on another XCD).
 template <bool FP8, bool WT>
-__device__ __forceinline__ void small_fc1(const SmallArgs& a, const SmallPlan& P) {
-  const int w = threadIdx.x >> 6, ti = threadIdx.x & 7;
+__device__ __forceinline__ void small_fc1(const SmallArgs& a, const SmallPlan& P,
+                                          f32x4* __restrict__ red) {
+  const int ti = threadIdx.x & 7;
   const int S = a.T * a.k;
   const Fc1Args f{FP8 ? (const void*)a.xq : (const void*)a.x, a.xs, a.w1, a.w1s, nullptr,
                   nullptr, nullptr, a.H, a.I, a.k, S, 0, a.remap, a.h, nullptr};
-  const int qpu = a.I >> 5;
-  const Share sh = wg_share((long)P.nunits * qpu, a.remap);
-  for (long qd = sh.q0; qd < sh.q1; ++qd) {
-    const int u = (int)(qd / qpu), r = (int)(qd % qpu) * 4 + w;
+  const int tpu = a.I >> 3;
+  const Share sh = wg_share((long)P.nunits * tpu, a.remap);
+  int j = 0;
+  for (long t = sh.q0; t < sh.q1; ++t, ++j) {
+    const int u = (int)(t / tpu), r = (int)(t % tpu);
     const int slot = ti < P.ulen[u] ? P.sorted[P.upos[u] + ti] : S;
-    fc1_cold<FP8, cold_u<FP8, false>(), WT>(f, P.ue[u], r, slot);
+    fc1_cold_sliced<FP8, cold_u<FP8, false>(), WT>(f, P.ue[u], r, slot, red, j);
   }
 }
 
@@ -1806,8 +1906,9 @@ __device__ __forceinline__ void small_fc2(const SmallArgs& a, const SmallPlan& P
 template <bool FP8>
 __global__ __launch_bounds__(256) void small_fc1_kernel(SmallArgs a) {
   __shared__ SmallPlan P;
+  __shared__ f32x4 red[2 * kRedF4];
   small_plan(a.ids, a.T * a.k, a.E, P);
-  small_fc1<FP8, false>(a, P);
+  small_fc1<FP8, false>(a, P, red);
 }
 template <bool FP8>
 __global__ __launch_bounds__(256) void small_fc2_kernel(SmallArgs a) {
@@ -1819,6 +1920,7 @@ __global__ __launch_bounds__(256) void small_fc2_kernel(SmallArgs a) {
 template <bool FP8, int VPL>
 __global__ __launch_bounds__(256) void small_forward_kernel(SmallArgs a) {
   __shared__ SmallPlan P;
+  __shared__ f32x4 red[2 * kRedF4];
   GridSync gs{a.bar};
   const int w = threadIdx.x >> 6;
   const int gw = blockIdx.x * 4 + w;  // global wave
@@ -1835,7 +1937,7 @@ __global__ __launch_bounds__(256) void small_forward_kernel(SmallArgs a) {
   }
   gs.sync();
   small_plan(a.ids, S, a.E, P);
-  small_fc1<FP8, true>(a, P);
+  small_fc1<FP8, true>(a, P, red);
   gs.sync();
   if constexpr (FP8) {
     for (int r = gw; r < S; r += nw)
@@ -1885,15 +1987,16 @@ FfnWorkspace ffn_workspace_layout(int T, int H, int I, int k, int dtype) {
 }
 
 // Resident-capacity grid of a persistent kernel on the current device,
-// rounded down to a multiple of 8 (one share per XCD). Cached per device.
+// rounded down to a multiple of 8 (one share per XCD). Cached per device and
+// kernel.
 template <typename K>
-static int persistent_grid(K kernel, int slot, int threads = 256) {
+static int persistent_grid(K kernel, int threads = 256) {
   static std::mutex mu;
-  static int cache[64][32];
+  static std::map<std::pair<int, const void*>, int> cache;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
   std::lock_guard<std::mutex> lock(mu);
-  int& c = cache[dev][slot];
+  int& c = cache[{dev, (const void*)kernel}];
   if (c == 0) {
     int cus = 0, occ = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -1960,22 +2063,22 @@ hipError_t launch_ffn_bf16(const FfnProblem& p, hipStream_t stream) {
     Fc1Args a{p.x, nullptr, p.w1, nullptr, p.sorted_ids, p.block_expert, p.num_padded,
               p.H, p.I, p.k, S, log2m, remap, h, queue};
     if (dense)
-      dense_fc1_kernel<<<persistent_grid(dense_fc1_kernel, 4, kDThreads), kDThreads, 0, stream>>>(a);
+      dense_fc1_kernel<<<persistent_grid(dense_fc1_kernel, kDThreads), kDThreads, 0, stream>>>(a);
     else if (hot)
-      fc1_kernel<false, true><<<persistent_grid(fc1_kernel<false, true>, 0), 256, 0, stream>>>(a);
+      fc1_kernel<false, true><<<persistent_grid(fc1_kernel<false, true>), 256, 0, stream>>>(a);
     else
-      fc1_kernel<false, false><<<persistent_grid(fc1_kernel<false, false>, 6), 256, 0, stream>>>(a);
+      fc1_sliced_kernel<false><<<persistent_grid(fc1_sliced_kernel<false>), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_FC2) {
     Fc2Args a{h, nullptr, p.w2, nullptr, p.sorted_ids, p.block_expert, p.num_padded,
               p.H, p.I, S, log2m, remap, y, 1, queue + kQueues};
     if (dense)
-      dense_fc2_kernel<<<persistent_grid(dense_fc2_kernel, 5, kDThreads), kDThreads, 0, stream>>>(a);
+      dense_fc2_kernel<<<persistent_grid(dense_fc2_kernel, kDThreads), kDThreads, 0, stream>>>(a);
     else if (hot)
-      fc2_kernel<false, true><<<persistent_grid(fc2_kernel<false, true>, 1), 256, 0, stream>>>(a);
+      fc2_kernel<false, true><<<persistent_grid(fc2_kernel<false, true>), 256, 0, stream>>>(a);
     else
-      fc2_kernel<false, false><<<persistent_grid(fc2_kernel<false, false>, 7), 256, 0, stream>>>(a);
+      fc2_kernel<false, false><<<persistent_grid(fc2_kernel<false, false>), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_COMBINE) return launch_combine(p, L, MOE_DTYPE_BF16, stream);
@@ -2008,9 +2111,9 @@ hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
     Fc1Args a{xq, xs, p.w1, p.w1_scale, p.sorted_ids, p.block_expert, p.num_padded,
               p.H, p.I, p.k, S, log2m, remap, h, queue};
     if (hot)
-      fc1_kernel<true, true><<<persistent_grid(fc1_kernel<true, true>, 2), 256, 0, stream>>>(a);
+      fc1_kernel<true, true><<<persistent_grid(fc1_kernel<true, true>), 256, 0, stream>>>(a);
     else
-      fc1_kernel<true, false><<<persistent_grid(fc1_kernel<true, false>, 8), 256, 0, stream>>>(a);
+      fc1_sliced_kernel<true><<<persistent_grid(fc1_sliced_kernel<true>), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_FC2) {
@@ -2019,9 +2122,9 @@ hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
     Fc2Args a{hq, hs, p.w2, p.w2_scale, p.sorted_ids, p.block_expert, p.num_padded,
               p.H, p.I, S, log2m, remap, y, 0, queue + kQueues};
     if (hot)
-      fc2_kernel<true, true><<<persistent_grid(fc2_kernel<true, true>, 3), 256, 0, stream>>>(a);
+      fc2_kernel<true, true><<<persistent_grid(fc2_kernel<true, true>), 256, 0, stream>>>(a);
     else
-      fc2_kernel<true, false><<<persistent_grid(fc2_kernel<true, false>, 9), 256, 0, stream>>>(a);
+      fc2_kernel<true, false><<<persistent_grid(fc2_kernel<true, false>), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_COMBINE) return launch_combine(p, L, MOE_DTYPE_FP8, stream);
@@ -2039,13 +2142,13 @@ hipError_t launch_ffn_w8a16(const FfnProblem& p, hipStream_t stream) {
   if (st & MOE_FFN_STAGE_FC1) {
     Fc1Args a{p.x, nullptr, p.w1, p.w1_scale, p.sorted_ids, p.block_expert, p.num_padded,
               p.H, p.I, p.k, S, log2m, remap, h, nullptr};
-    fc1_w8a16_kernel<<<persistent_grid(fc1_w8a16_kernel, 10), 256, 0, stream>>>(a);
+    fc1_w8a16_kernel<<<persistent_grid(fc1_w8a16_kernel), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_FC2) {
     Fc2Args a{h, nullptr, p.w2, p.w2_scale, p.sorted_ids, p.block_expert, p.num_padded,
               p.H, p.I, S, log2m, remap, y, 1, nullptr};
-    fc2_w8a16_kernel<<<persistent_grid(fc2_w8a16_kernel, 11), 256, 0, stream>>>(a);
+    fc2_w8a16_kernel<<<persistent_grid(fc2_w8a16_kernel), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_COMBINE) return launch_combine(p, L, MOE_DTYPE_BF16, stream);
@@ -2072,7 +2175,7 @@ hipError_t launch_ffn_fp8_block(const FfnProblem& p, hipStream_t stream) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
     Fc1Args a{xq, xs, p.w1, p.w1_scale, p.sorted_ids, p.block_expert, p.num_padded,
               p.H, p.I, p.k, S, log2m, remap, h, nullptr};
-    fc1_blk_kernel<<<persistent_grid(fc1_blk_kernel, 12), 256, 0, stream>>>(a);
+    fc1_blk_kernel<<<persistent_grid(fc1_blk_kernel), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_FC2) {
@@ -2081,7 +2184,7 @@ hipError_t launch_ffn_fp8_block(const FfnProblem& p, hipStream_t stream) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
     Fc2Args a{hq, hs, p.w2, p.w2_scale, p.sorted_ids, p.block_expert, p.num_padded,
               p.H, p.I, S, log2m, remap, y, 0, nullptr};
-    fc2_blk_kernel<<<persistent_grid(fc2_blk_kernel, 13), 256, 0, stream>>>(a);
+    fc2_blk_kernel<<<persistent_grid(fc2_blk_kernel), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_COMBINE) return launch_combine(p, L, MOE_DTYPE_FP8, stream);
@@ -2098,14 +2201,13 @@ size_t small_workspace_bytes(int T, int H, int I, int k, int dtype) {
 template <bool FP8>
 static hipError_t launch_small(const SmallProblem& p, const SmallArgs& a, hipStream_t stream) {
   void* args[] = {(void*)&a};
-  auto go = [&](auto kernel, int slot) {
-    const int grid = persistent_grid(kernel, slot);
+  auto go = [&](auto kernel) {
+    const int grid = persistent_grid(kernel);
     return hipLaunchCooperativeKernel(kernel, dim3(grid), dim3(256), args, 0, stream);
   };
-  const int base = FP8 ? 19 : 16;
-  if (p.E <= 64) return go(small_forward_kernel<FP8, 1>, base);
-  if (p.E <= 256) return go(small_forward_kernel<FP8, 4>, base + 1);
-  return go(small_forward_kernel<FP8, 16>, base + 2);
+  if (p.E <= 64) return go(small_forward_kernel<FP8, 1>);
+  if (p.E <= 256) return go(small_forward_kernel<FP8, 4>);
+  return go(small_forward_kernel<FP8, 16>);
 }
 
 // The split small path: route, (fp8: quantise x), FC1, (fp8: quantise h), FC2,
@@ -2122,16 +2224,14 @@ static hipError_t launch_small_split(const SmallProblem& p, const SmallArgs& a,
     quant_rows_kernel<uint16_t><<<(p.T + 3) / 4, 256, 0, stream>>>(a.x, p.T, p.H, a.xq, a.xs);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  small_fc1_kernel<FP8><<<persistent_grid(small_fc1_kernel<FP8>, FP8 ? 24 : 22), 256, 0,
-                          stream>>>(a);
+  small_fc1_kernel<FP8><<<persistent_grid(small_fc1_kernel<FP8>), 256, 0, stream>>>(a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (FP8) {
     quant_rows_kernel<float><<<(S + 3) / 4, 256, 0, stream>>>((const float*)a.h, S, p.I, a.hq,
                                                               a.hs);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  small_fc2_kernel<FP8><<<persistent_grid(small_fc2_kernel<FP8>, FP8 ? 25 : 23), 256, 0,
-                          stream>>>(a);
+  small_fc2_kernel<FP8><<<persistent_grid(small_fc2_kernel<FP8>), 256, 0, stream>>>(a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const long n8 = (long)p.T * (p.H / 8);
   const dim3 grid((unsigned)((n8 + 255) / 256));
