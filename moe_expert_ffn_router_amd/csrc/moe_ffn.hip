@@ -1526,35 +1526,95 @@ __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
   }
 }
 
+// Encode 8 values of a row at column c with the row's scale (WT as store_h).
+template <bool WT>
+__device__ __forceinline__ void quant_store8(const float (&v)[8], float scale,
+                                             uint8_t* __restrict__ codes, int c) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo |= f32_to_e4m3fn(v[i] / scale) << (8 * i);
+    hi |= f32_to_e4m3fn(v[4 + i] / scale) << (8 * i);
+  }
+  if (WT) {
+    st_dev((uint32_t*)(codes + c), lo);
+    st_dev((uint32_t*)(codes + c) + 1, hi);
+  } else {
+    *(u32x2*)(codes + c) = u32x2{lo, hi};
+  }
+}
+
 // One row of C elements by the calling wave: codes and its scale (WT as
-// store_h).
+// store_h). A lane takes 8 consecutive elements at each of the columns
+// lane*8 + 512*b; up to kQB such vectors per lane are loaded together (all
+// in flight at once) and, for rows of at most 512*kQB elements, kept in
+// registers between the absmax and the encoding.
+constexpr int kQB = 8;
 template <typename InT, bool WT = false>
 __device__ __forceinline__ void quant_row(const InT* __restrict__ row, int C,
                                           uint8_t* __restrict__ codes, float* __restrict__ scale_out) {
   const int lane = threadIdx.x & 63;
+  constexpr int step = kWave * 8;
   float amax = 0.f;
-  for (int c = lane * 8; c < C; c += kWave * 8) {
-    float v[8];
-    load8(row + c, v);
+  if (C <= step * kQB) {
+    float v[kQB][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    for (int b = 0; b < kQB; ++b) {
+      const int c = lane * 8 + b * step;
+      if (c < C) {
+        load8(row + c, v[b]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[b][i] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kQB; ++b)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[b][i]));
+    amax = wave_max(amax);
+    const float scale = amax == 0.f ? 1.0f : amax / 448.0f;
+#pragma unroll
+    for (int b = 0; b < kQB; ++b) {
+      const int c = lane * 8 + b * step;
+      if (c < C) quant_store8<WT>(v[b], scale, codes, c);
+    }
+    if (lane == 0) {
+      if (WT) st_dev(scale_out, scale);
+      else *scale_out = scale;
+    }
+    return;
+  }
+  for (int c0 = lane * 8; c0 < C; c0 += step * kQB) {
+    float v[kQB][8];
+#pragma unroll
+    for (int b = 0; b < kQB; ++b) {
+      const int c = c0 + b * step;
+      if (c < C) {
+        load8(row + c, v[b]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[b][i] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kQB; ++b)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[b][i]));
   }
   amax = wave_max(amax);
   const float scale = amax == 0.f ? 1.0f : amax / 448.0f;
-  for (int c = lane * 8; c < C; c += kWave * 8) {
-    float v[8];
-    load8(row + c, v);
-    uint32_t lo = 0, hi = 0;
+  for (int c0 = lane * 8; c0 < C; c0 += step * kQB) {
+    float v[kQB][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo |= f32_to_e4m3fn(v[i] / scale) << (8 * i);
-      hi |= f32_to_e4m3fn(v[4 + i] / scale) << (8 * i);
+    for (int b = 0; b < kQB; ++b) {
+      const int c = c0 + b * step;
+      if (c < C) load8(row + c, v[b]);
     }
-    if (WT) {
-      st_dev((uint32_t*)(codes + c), lo);
-      st_dev((uint32_t*)(codes + c) + 1, hi);
-    } else {
-      *(u32x2*)(codes + c) = u32x2{lo, hi};
+#pragma unroll
+    for (int b = 0; b < kQB; ++b) {
+      const int c = c0 + b * step;
+      if (c < C) quant_store8<WT>(v[b], scale, codes, c);
     }
   }
   if (lane == 0) {
@@ -1570,6 +1630,59 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const InT* __restrict__
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= R) return;
   quant_row<InT>(in + (size_t)r * C, C, codes + (size_t)r * C, scales + r);
+}
+
+// One row per 256-thread workgroup: the same codes and scale as quant_row
+// (the absmax is exact in any order), with the per-element division and
+// encoding spread over 4 times as many lanes. Rows of at most 2048*kQB
+// elements (every row of this library's shapes).
+template <typename InT>
+__global__ __launch_bounds__(256) void quant_rows_wg_kernel(const InT* __restrict__ in, int C,
+                                                            uint8_t* __restrict__ codes,
+                                                            float* __restrict__ scales) {
+  __shared__ float wmax[4];
+  const int r = blockIdx.x, t = threadIdx.x;
+  const InT* row = in + (size_t)r * C;
+  uint8_t* crow = codes + (size_t)r * C;
+  constexpr int step = 256 * 8;
+  float v[kQB][8];
+#pragma unroll
+  for (int b = 0; b < kQB; ++b) {
+    const int c = t * 8 + b * step;
+    if (c < C) {
+      load8(row + c, v[b]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[b][i] = 0.f;
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int b = 0; b < kQB; ++b)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[b][i]));
+  amax = wave_max(amax);
+  if ((t & 63) == 0) wmax[t >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float scale = amax == 0.f ? 1.0f : amax / 448.0f;
+#pragma unroll
+  for (int b = 0; b < kQB; ++b) {
+    const int c = t * 8 + b * step;
+    if (c < C) quant_store8<false>(v[b], scale, crow, c);
+  }
+  if (t == 0) scales[r] = scale;
+}
+
+// Row quantiser launch: a workgroup per row while the rows are few (fewer than
+// one wave per SIMD of the chip), else a wave per row.
+template <typename InT>
+static void launch_quant_rows(const InT* in, int R, int C, uint8_t* codes, float* scales,
+                              hipStream_t stream) {
+  if (R <= 1024 && C <= 256 * 8 * kQB)
+    quant_rows_wg_kernel<InT><<<R, 256, 0, stream>>>(in, C, codes, scales);
+  else
+    quant_rows_kernel<InT><<<(R + 3) / 4, 256, 0, stream>>>(in, R, C, codes, scales);
 }
 
 // Per-group FP8 quantiser: groups of 128 consecutive elements of a row, 16
@@ -2105,8 +2218,7 @@ hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_FC1) {
-    quant_rows_kernel<uint16_t><<<(p.T + 3) / 4, 256, 0, stream>>>((const uint16_t*)p.x, p.T,
-                                                                   p.H, xq, xs);
+    launch_quant_rows<uint16_t>((const uint16_t*)p.x, p.T, p.H, xq, xs, stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     Fc1Args a{xq, xs, p.w1, p.w1_scale, p.sorted_ids, p.block_expert, p.num_padded,
               p.H, p.I, p.k, S, log2m, remap, h, queue};
@@ -2117,7 +2229,7 @@ hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_FC2) {
-    quant_rows_kernel<float><<<(S + 3) / 4, 256, 0, stream>>>(h, S, p.I, hq, hs);
+    launch_quant_rows<float>(h, S, p.I, hq, hs, stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     Fc2Args a{hq, hs, p.w2, p.w2_scale, p.sorted_ids, p.block_expert, p.num_padded,
               p.H, p.I, S, log2m, remap, y, 0, queue + kQueues};
@@ -2221,14 +2333,13 @@ static hipError_t launch_small_split(const SmallProblem& p, const SmallArgs& a,
     return err;
   const int S = p.T * p.k;
   if (FP8) {
-    quant_rows_kernel<uint16_t><<<(p.T + 3) / 4, 256, 0, stream>>>(a.x, p.T, p.H, a.xq, a.xs);
+    launch_quant_rows<uint16_t>(a.x, p.T, p.H, a.xq, a.xs, stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   small_fc1_kernel<FP8><<<persistent_grid(small_fc1_kernel<FP8>), 256, 0, stream>>>(a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (FP8) {
-    quant_rows_kernel<float><<<(S + 3) / 4, 256, 0, stream>>>((const float*)a.h, S, p.I, a.hq,
-                                                              a.hs);
+    launch_quant_rows<float>((const float*)a.h, S, p.I, a.hq, a.hs, stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   small_fc2_kernel<FP8><<<persistent_grid(small_fc2_kernel<FP8>), 256, 0, stream>>>(a);
