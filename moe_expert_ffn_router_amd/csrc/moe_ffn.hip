@@ -475,6 +475,29 @@ __device__ __forceinline__ int kslice(int n, int w) { return (w * n) >> 2; }
 // accumulators, alternating from one tile to the next.
 constexpr int kRedF4 = 4 * 2 * 64;
 
+// The meeting of a sliced tile's 4 waves: every wave leaves its partial
+// accumulators in buffer j & 1, and wave (j & 3) gets their sums in wave order
+// back in accp/accq (true); the other waves get false. One barrier per tile:
+// a buffer is written again two tiles later, after the next tile's barrier,
+// which its reader has passed only after reading it.
+__device__ __forceinline__ bool sliced_reduce(f32x4* __restrict__ red, int j, f32x4& accp,
+                                              f32x4& accq) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  f32x4* buf = red + (j & 1) * kRedF4;
+  buf[(2 * w) * 64 + lane] = accp;
+  buf[(2 * w + 1) * 64 + lane] = accq;
+  __syncthreads();
+  if (w != (j & 3)) return false;
+  accp = buf[lane];
+  accq = buf[64 + lane];
+#pragma unroll
+  for (int v = 1; v < 4; ++v) {
+    accp += buf[(2 * v) * 64 + lane];
+    accq += buf[(2 * v + 1) * 64 + lane];
+  }
+  return true;
+}
+
 // Cold FC1 tile r (as fc1_cold) computed by all 4 waves of the workgroup,
 // each over a quarter of K; the partial accumulators are summed in wave order
 // by wave (j & 3), which finishes the tile. j counts the workgroup's sliced
@@ -506,28 +529,17 @@ __device__ __forceinline__ void fc1_cold_sliced(const Fc1Args& p, int e, int r, 
   }
   f32x4 accp = {}, accq = {};
   cold_kloop<FP8, U>(ap, aq, bp, ok, kb, accp, accq);
-  f32x4* buf = red + (j & 1) * kRedF4;
-  buf[(2 * w) * 64 + lane] = accp;
-  buf[(2 * w + 1) * 64 + lane] = accq;
-  __syncthreads();
-  if (fin) {
-    f32x4 sp = buf[lane], sq = buf[64 + lane];
+  if (!sliced_reduce(red, j, accp, accq)) return;
+  f32x4 g = diag_sum(accp), u = diag_sum(accq);
+  if (holder && ok) {
+    if (FP8) {
 #pragma unroll
-    for (int v = 1; v < 4; ++v) {
-      sp += buf[(2 * v) * 64 + lane];
-      sq += buf[(2 * v + 1) * 64 + lane];
-    }
-    f32x4 g = diag_sum(sp), u = diag_sum(sq);
-    if (holder && ok) {
-      if (FP8) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          g[i] *= sg[i] * xs;
-          u[i] *= su[i] * xs;
-        }
+      for (int i = 0; i < 4; ++i) {
+        g[i] *= sg[i] * xs;
+        u[i] *= su[i] * xs;
       }
-      store_h<FP8, WT>(p, slot, col, g, u);
     }
+    store_h<FP8, WT>(p, slot, col, g, u);
   }
 }
 
@@ -809,6 +821,44 @@ __device__ __forceinline__ void fc1_cold_w8(const Fc1Args& p, int e, int r, int 
   }
 }
 
+// Cold FC1 tile r of the W8A16 path computed by all 4 waves of the workgroup,
+// one K quarter each (as fc1_cold_sliced).
+__device__ __forceinline__ void fc1_cold_w8_sliced(const Fc1Args& p, int e, int r, int slot,
+                                                   f32x4* __restrict__ red, int j) {
+  const int lane = threadIdx.x & 63, w8 = threadIdx.x >> 6;
+  const size_t rowq = (size_t)p.H;      // code bytes per weight row
+  const size_t rowx = (size_t)p.H * 2;  // bytes per activation row
+  const int nch = (int)(rowq / 128);
+  const int c0 = kslice(nch, w8), c1 = kslice(nch, w8 + 1);
+  const uint8_t* w = (const uint8_t*)p.w1 + (size_t)e * 2 * p.I * rowq;
+  const uint8_t* ap = w + (size_t)(r * 8 + (lane & 7)) * rowq + w8_code_off() + (size_t)c0 * 128;
+  const uint8_t* aq =
+      w + (size_t)(p.I + r * 8 + (lane & 7)) * rowq + w8_code_off() + (size_t)c0 * 128;
+  const bool ok = slot < p.S;
+  const uint8_t* bp = (const uint8_t*)p.x + (size_t)(ok ? slot / p.k : 0) * rowx + w8_act_off() +
+                      (size_t)c0 * 256;
+  const bool fin = w8 == (j & 3);
+  const bool holder = (lane & 8) == 0 && lane < 32;
+  const int col = r * 8 + 4 * (lane >> 4);
+  f32x4 sg = {1.f, 1.f, 1.f, 1.f}, su = sg;
+  if (fin && holder) {
+    sg = *(const f32x4*)(p.w1s + (size_t)e * 2 * p.I + col);
+    su = *(const f32x4*)(p.w1s + (size_t)e * 2 * p.I + p.I + col);
+  }
+  f32x4 accp = {}, accq = {};
+  w8_kloop<kW8U>(ap, aq, bp, ok, (c1 - c0) * 128, accp, accq);
+  if (!sliced_reduce(red, j, accp, accq)) return;
+  f32x4 g = diag_sum(accp), u = diag_sum(accq);
+  if (holder && ok) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      g[i] *= sg[i];
+      u[i] *= su[i];
+    }
+    store_h<false>(p, slot, col, g, u);
+  }
+}
+
 // Cold FC2 tile r of the W8A16 path (layout as fc2_cold).
 __device__ __forceinline__ void fc2_cold_w8(const Fc2Args& p, int e, int r, int slot) {
   const int lane = threadIdx.x & 63;
@@ -954,6 +1004,30 @@ __device__ __forceinline__ void fc1_cold_blk(const Fc1Args& p, int e, int r, int
   if ((lane & 8) == 0 && lane < 32 && ok) store_h<true>(p, slot, r * 8 + 4 * (lane >> 4), g, u);
 }
 
+// Cold FC1 tile r of the block-scaled path computed by all 4 waves of the
+// workgroup, one K quarter (a run of whole 128-column blocks) each.
+__device__ __forceinline__ void fc1_cold_blk_sliced(const Fc1Args& p, int e, int r, int slot,
+                                                    f32x4* __restrict__ red, int j) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int kb = p.H / kBlk, nb = 2 * p.I / kBlk;
+  const int c0 = kslice(kb, w), c1 = kslice(kb, w + 1);
+  const int off = half_split_off() + c0 * 128;
+  const uint8_t* wt = (const uint8_t*)p.w1 + (size_t)e * 2 * p.I * p.H;
+  const uint8_t* ap = wt + (size_t)(r * 8 + (lane & 7)) * p.H + off;
+  const uint8_t* aq = wt + (size_t)(p.I + r * 8 + (lane & 7)) * p.H + off;
+  const bool ok = slot < p.S;
+  const int t = ok ? slot / p.k : 0;
+  const uint8_t* bp = (const uint8_t*)p.x + (size_t)t * p.H + off;
+  const float* as = p.xs + (size_t)t * kb + c0;
+  const float* wsp = p.w1s + ((size_t)e * nb + (r * 8) / kBlk) * kb + c0;
+  const float* wsq = p.w1s + ((size_t)e * nb + (p.I + r * 8) / kBlk) * kb + c0;
+  f32x4 accp = {}, accq = {};
+  blk_kloop<kBlkU>(ap, aq, bp, as, wsp, wsq, ok, (c1 - c0) * 128, accp, accq);
+  if (!sliced_reduce(red, j, accp, accq)) return;
+  const f32x4 g = diag_sum(accp), u = diag_sum(accq);
+  if ((lane & 8) == 0 && lane < 32 && ok) store_h<true>(p, slot, r * 8 + 4 * (lane >> 4), g, u);
+}
+
 // Cold FC2 tile r of the block-scaled path (layout as fc2_cold). h: codes
 // [S, I]; hs: group scales [S, I/128]; w2s: block scales [E, H/128, I/128].
 // Both 8-row halves of the tile lie in one 128-row block.
@@ -1067,14 +1141,11 @@ __global__ __launch_bounds__(256) void fc1_kernel(Fc1Args p) {
             fc1_hot_pass<FP8, 3>, fc1_hot_pass<FP8, 4>>(p, p.I >> 3, lds);
 }
 
-// Cold-only FC1 launch (T <= 16 tokens): the work list is (block, tile) and
-// the 4 waves of a workgroup compute each tile together, one K quarter each,
-// so four times as many waves stream weights as with one tile per wave, each
-// along a dependent load chain a quarter as long. Blocks of more than 8 tokens
-// run one such tile per 8 tokens.
-template <bool FP8>
-__global__ __launch_bounds__(256) void fc1_sliced_kernel(Fc1Args p) {
-  __shared__ f32x4 red[2 * kRedF4];
+// The (block, tile) work list of a K-sliced FC1 launch: a workgroup takes a
+// contiguous share and its 4 waves compute each tile together; blocks of more
+// than 8 tokens run one such tile per 8 tokens.
+template <void (*Tile)(const Fc1Args&, int, int, int, f32x4*, int)>
+__device__ __forceinline__ void run_sliced_fc1(const Fc1Args& p, f32x4* __restrict__ red) {
   const int M = 1 << p.log2m, nb = p.num_padded[0] >> p.log2m, tpb = p.I >> 3;
   const int ti = threadIdx.x & 7;
   const Share sh = wg_share((long)nb * tpb, p.remap);
@@ -1088,9 +1159,20 @@ __global__ __launch_bounds__(256) void fc1_sliced_kernel(Fc1Args p) {
     }
     for (int t0 = 0; t0 < m; t0 += kColdMax, ++j) {
       const int slot = t0 + ti < m ? p.sorted_ids[(size_t)b * M + t0 + ti] : p.S;
-      fc1_cold_sliced<FP8, cold_u<FP8, false>()>(p, e, r, slot, red, j);
+      Tile(p, e, r, slot, red, j);
     }
   }
+}
+
+// Cold-only FC1 launch (T <= 16 tokens): the work list is (block, tile) and
+// the 4 waves of a workgroup compute each tile together, one K quarter each,
+// so four times as many waves stream weights as with one tile per wave, each
+// along a dependent load chain a quarter as long. Blocks of more than 8 tokens
+// run one such tile per 8 tokens.
+template <bool FP8>
+__global__ __launch_bounds__(256) void fc1_sliced_kernel(Fc1Args p) {
+  __shared__ f32x4 red[2 * kRedF4];
+  run_sliced_fc1<fc1_cold_sliced<FP8, cold_u<FP8, false>()>>(p, red);
 }
 
 template <bool FP8, bool HOT>
@@ -1104,10 +1186,8 @@ __global__ __launch_bounds__(256) void fc2_kernel(Fc2Args p) {
 // W8A16 runs every block by cold passes of 8 tokens (the weights stream once
 // per 8 tokens of a block): a decode path.
 __global__ __launch_bounds__(256) void fc1_w8a16_kernel(Fc1Args p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[16];
-  run_quads<false, false, false, Fc1Args, fc1_cold_w8, fc1_hot_pass<false, 1>,
-            fc1_hot_pass<false, 2>, fc1_hot_pass<false, 3>, fc1_hot_pass<false, 4>>(p, p.I >> 3,
-                                                                                     lds);
+  __shared__ f32x4 red[2 * kRedF4];
+  run_sliced_fc1<fc1_cold_w8_sliced>(p, red);
 }
 
 __global__ __launch_bounds__(256) void fc2_w8a16_kernel(Fc2Args p) {
@@ -1118,11 +1198,9 @@ __global__ __launch_bounds__(256) void fc2_w8a16_kernel(Fc2Args p) {
 }
 
 // Block-scaled FP8 runs every block by cold passes of 8 tokens, like W8A16.
-__global__ __launch_bounds__(256) void fc1_blk_kernel(Fc1Args p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[16];
-  run_quads<true, false, false, Fc1Args, fc1_cold_blk, fc1_hot_pass<true, 1>,
-            fc1_hot_pass<true, 2>, fc1_hot_pass<true, 3>, fc1_hot_pass<true, 4>>(p, p.I >> 3,
-                                                                                  lds);
+__global__ __launch_bounds__(256, 3) void fc1_blk_kernel(Fc1Args p) {
+  __shared__ f32x4 red[2 * kRedF4];
+  run_sliced_fc1<fc1_cold_blk_sliced>(p, red);
 }
 
 __global__ __launch_bounds__(256) void fc2_blk_kernel(Fc2Args p) {
