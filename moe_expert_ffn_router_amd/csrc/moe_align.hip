@@ -150,6 +150,88 @@ __global__ __launch_bounds__(NW * kWave) void align_kernel(
   align_body<NW>(ids, S, E, log2m, cap, sorted_ids, block_expert, num_padded, cnt, off);
 }
 
+// Alignment of a small batch (S <= 256 slots): one thread per slot. A slot's
+// rank among its expert's slots is the number of equal ids before it in slot
+// order (a pass over the ids in LDS), the expert counts come from LDS atomic
+// increments (order-free), and one scan of the padded counts over the first
+// 256 threads gives the offsets: the same placement as align_body, with three
+// barriers instead of its per-wave tables. ids may live in global memory or
+// in LDS; every thread of the workgroup (256 or more) calls this.
+constexpr int kAlignSmallSlots = 256;
+
+struct AlignSmallLds {
+  int ids[kAlignSmallSlots];
+  int cnt[kAlignMaxE];
+  int off[kAlignMaxE];
+  int wsum[kAlignSmallSlots / kWave];
+};
+
+__device__ __forceinline__ void align_small_body(const int32_t* ids, int S, int E, int log2m,
+                                                 int cap, int32_t* __restrict__ sorted_ids,
+                                                 int32_t* __restrict__ block_expert,
+                                                 int32_t* __restrict__ num_padded,
+                                                 AlignSmallLds& L) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, nt = blockDim.x;
+  const int M = 1 << log2m;
+  const int e = t < S ? ids[t] : -1;
+  if (t < kAlignSmallSlots) L.ids[t] = e;
+  for (int i = t; i < E; i += nt) L.cnt[i] = 0;
+  for (int i = t; i < cap; i += nt) sorted_ids[i] = S;
+  for (int i = t; i < (cap >> log2m); i += nt) block_expert[i] = -1;
+  __syncthreads();
+  const bool valid = (unsigned)e < (unsigned)E;  // else: remote slot or past S
+  int rank = 0;
+  if (valid) {
+    for (int q = 0; q < t; ++q) rank += L.ids[q] == e;
+    atomicAdd(&L.cnt[e], 1);
+  }
+  __syncthreads();
+  // exclusive scan of the padded counts: thread t < 256 owns experts [4t, 4t + 4)
+  constexpr int kPer = kAlignMaxE / kAlignSmallSlots;
+  const bool scan = t < kAlignSmallSlots;
+  int pc[kPer], local = 0, incl = 0;
+  if (scan) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int x = kPer * t + i;
+      pc[i] = x < E ? ((L.cnt[x] + M - 1) >> log2m) << log2m : 0;
+      local += pc[i];
+    }
+    incl = local;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    if (lane == kWave - 1) L.wsum[w] = incl;
+  }
+  __syncthreads();
+  if (scan) {
+    int run = incl - local;
+    for (int v = 0; v < w; ++v) run += L.wsum[v];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int x = kPer * t + i;
+      if (x < E) {
+        L.off[x] = run;
+        for (int b = run >> log2m; b < (run + pc[i]) >> log2m; ++b) block_expert[b] = x;
+      }
+      run += pc[i];
+    }
+    if (t == kAlignSmallSlots - 1) num_padded[0] = run;
+  }
+  __syncthreads();
+  if (valid) sorted_ids[L.off[e] + rank] = t;
+}
+
+__global__ __launch_bounds__(kAlignSmallSlots) void align_small_kernel(
+    const int32_t* __restrict__ ids, int S, int E, int log2m, int cap,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
+    int32_t* __restrict__ num_padded) {
+  __shared__ AlignSmallLds L;
+  align_small_body(ids, S, E, log2m, cap, sorted_ids, block_expert, num_padded, L);
+}
+
 // Routing and alignment of a small batch in one launch: wave w routes token w
 // (at most 8 tokens), keeping the ids in LDS as well, then the same workgroup
 // aligns them from LDS: one launch and one memory round trip less than the
@@ -162,8 +244,13 @@ __global__ __launch_bounds__(kAlignThreads) void route_align_kernel(
     int32_t* __restrict__ ids, float* __restrict__ wts, int log2m, int cap,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
     int32_t* __restrict__ num_padded) {
-  __shared__ int cnt[kAlignWaves][kAlignMaxE];
-  __shared__ int off[kAlignMaxE + 1];
+  __shared__ union {
+    struct {
+      int cnt[kAlignWaves][kAlignMaxE];
+      int off[kAlignMaxE + 1];
+    } wide;
+    AlignSmallLds small;
+  } lds;
   __shared__ int32_t ids_lds[kFuseMaxSlots];
   const int t = threadIdx.x >> 6;
   if (t < T) {  // uniform per wave
@@ -172,8 +259,12 @@ __global__ __launch_bounds__(kAlignThreads) void route_align_kernel(
     route_token<VPL>(v, t, E, k, renorm, ids, wts, ids_lds);
   }
   __syncthreads();
-  align_body<kAlignWaves>(ids_lds, T * k, E, log2m, cap, sorted_ids, block_expert, num_padded,
-                          cnt, off);
+  if (T * k <= kAlignSmallSlots)
+    align_small_body(ids_lds, T * k, E, log2m, cap, sorted_ids, block_expert, num_padded,
+                     lds.small);
+  else
+    align_body<kAlignWaves>(ids_lds, T * k, E, log2m, cap, sorted_ids, block_expert, num_padded,
+                            lds.wide.cnt, lds.wide.off);
 }
 
 static int ilog2_align(int block_m) {
@@ -216,7 +307,10 @@ hipError_t launch_align(const int32_t* ids, int S, int E, int block_m, int cap,
                         hipStream_t stream) {
   int log2m = 0;
   while ((1 << log2m) < block_m) ++log2m;
-  if (S >= kAlignWideSlots)  // many slots: 16 waves share the two passes over them
+  if (S <= kAlignSmallSlots)
+    align_small_kernel<<<1, kAlignSmallSlots, 0, stream>>>(ids, S, E, log2m, cap, sorted_ids,
+                                                            block_expert, num_padded);
+  else if (S >= kAlignWideSlots)  // many slots: 16 waves share the two passes over them
     align_kernel<kAlignWideWaves><<<1, kAlignWideWaves * kWave, 0, stream>>>(
         ids, S, E, log2m, cap, sorted_ids, block_expert, num_padded);
   else
