@@ -1141,6 +1141,12 @@ __global__ __launch_bounds__(256) void fc1_kernel(Fc1Args p) {
             fc1_hot_pass<FP8, 3>, fc1_hot_pass<FP8, 4>>(p, p.I >> 3, lds);
 }
 
+// Whether an FC1 launch of T tokens (at most 16: the cold-only launches) runs
+// K-sliced tiles rather than one tile per wave.
+__host__ __device__ constexpr bool sliced_fc1(bool bf16, int T) {
+  return bf16 || T <= kColdMax;
+}
+
 // The (block, tile) work list of a K-sliced FC1 launch: a workgroup takes a
 // contiguous share and its 4 waves compute each tile together; blocks of more
 // than 8 tokens run one such tile per 8 tokens.
@@ -1164,11 +1170,15 @@ __device__ __forceinline__ void run_sliced_fc1(const Fc1Args& p, f32x4* __restri
   }
 }
 
-// Cold-only FC1 launch (T <= 16 tokens): the work list is (block, tile) and
+// Cold-only FC1 launch with K-sliced tiles: the work list is (block, tile) and
 // the 4 waves of a workgroup compute each tile together, one K quarter each,
 // so four times as many waves stream weights as with one tile per wave, each
 // along a dependent load chain a quarter as long. Blocks of more than 8 tokens
-// run one such tile per 8 tokens.
+// run one such tile per 8 tokens. Taken for bf16 up to 16 tokens and for the
+// other formats up to 8 (sliced_fc1()): measured with kernel traces at E = 64,
+// H = 4096, I = 1536, k = 8 against one tile per wave, bf16 FC1 111.8 -> 91.3 us
+// at 4 tokens, 243.1 -> 237.1 us at 16; fp8 58.1 -> 49.0 us at 4 tokens but
+// 125.0 -> 126.8 us at 16; W8A16 and block FP8 5-8 % slower at 16 tokens.
 template <bool FP8>
 __global__ __launch_bounds__(256) void fc1_sliced_kernel(Fc1Args p) {
   __shared__ f32x4 red[2 * kRedF4];
@@ -1186,6 +1196,14 @@ __global__ __launch_bounds__(256) void fc2_kernel(Fc2Args p) {
 // W8A16 runs every block by cold passes of 8 tokens (the weights stream once
 // per 8 tokens of a block): a decode path.
 __global__ __launch_bounds__(256) void fc1_w8a16_kernel(Fc1Args p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[16];
+  run_quads<false, false, false, Fc1Args, fc1_cold_w8, fc1_hot_pass<false, 1>,
+            fc1_hot_pass<false, 2>, fc1_hot_pass<false, 3>, fc1_hot_pass<false, 4>>(p, p.I >> 3,
+                                                                                     lds);
+}
+
+// W8A16 FC1 with K-sliced tiles, for at most 8 tokens (see fc1_sliced_kernel).
+__global__ __launch_bounds__(256) void fc1_w8a16_sliced_kernel(Fc1Args p) {
   __shared__ f32x4 red[2 * kRedF4];
   run_sliced_fc1<fc1_cold_w8_sliced>(p, red);
 }
@@ -1198,7 +1216,15 @@ __global__ __launch_bounds__(256) void fc2_w8a16_kernel(Fc2Args p) {
 }
 
 // Block-scaled FP8 runs every block by cold passes of 8 tokens, like W8A16.
-__global__ __launch_bounds__(256, 3) void fc1_blk_kernel(Fc1Args p) {
+__global__ __launch_bounds__(256) void fc1_blk_kernel(Fc1Args p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[16];
+  run_quads<true, false, false, Fc1Args, fc1_cold_blk, fc1_hot_pass<true, 1>,
+            fc1_hot_pass<true, 2>, fc1_hot_pass<true, 3>, fc1_hot_pass<true, 4>>(p, p.I >> 3,
+                                                                                  lds);
+}
+
+// Block-scaled FC1 with K-sliced tiles, for at most 8 tokens.
+__global__ __launch_bounds__(256, 3) void fc1_blk_sliced_kernel(Fc1Args p) {
   __shared__ f32x4 red[2 * kRedF4];
   run_sliced_fc1<fc1_cold_blk_sliced>(p, red);
 }
@@ -2056,7 +2082,8 @@ __device__ __forceinline__ void small_plan(const int32_t* __restrict__ ids, int 
 }
 
 // FC1 over (unit, tile) shares, each tile of 8 h columns K-sliced over the 4
-// waves (as in the cold-only FC1 launch, so the results are the same bits).
+// waves, or over (unit, quad) shares with one tile per wave, by the rule of
+// the cold-only FC1 launches (so the results are the same bits).
 // WT: device-scope stores (the reader is in the same kernel on another XCD).
 template <bool FP8, bool WT>
 __device__ __forceinline__ void small_fc1(const SmallArgs& a, const SmallPlan& P,
@@ -2065,6 +2092,16 @@ __device__ __forceinline__ void small_fc1(const SmallArgs& a, const SmallPlan& P
   const int S = a.T * a.k;
   const Fc1Args f{FP8 ? (const void*)a.xq : (const void*)a.x, a.xs, a.w1, a.w1s, nullptr,
                   nullptr, nullptr, a.H, a.I, a.k, S, 0, a.remap, a.h, nullptr};
+  if (!sliced_fc1(!FP8, a.T)) {
+    const int w = threadIdx.x >> 6, qpu = a.I >> 5;
+    const Share sh = wg_share((long)P.nunits * qpu, a.remap);
+    for (long qd = sh.q0; qd < sh.q1; ++qd) {
+      const int u = (int)(qd / qpu), r = (int)(qd % qpu) * 4 + w;
+      const int slot = ti < P.ulen[u] ? P.sorted[P.upos[u] + ti] : S;
+      fc1_cold<FP8, cold_u<FP8, false>(), WT>(f, P.ue[u], r, slot);
+    }
+    return;
+  }
   const int tpu = a.I >> 3;
   const Share sh = wg_share((long)P.nunits * tpu, a.remap);
   int j = 0;
@@ -2302,8 +2339,10 @@ hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
               p.H, p.I, p.k, S, log2m, remap, h, queue};
     if (hot)
       fc1_kernel<true, true><<<persistent_grid(fc1_kernel<true, true>), 256, 0, stream>>>(a);
-    else
+    else if (sliced_fc1(false, p.T))
       fc1_sliced_kernel<true><<<persistent_grid(fc1_sliced_kernel<true>), 256, 0, stream>>>(a);
+    else
+      fc1_kernel<true, false><<<persistent_grid(fc1_kernel<true, false>), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_FC2) {
@@ -2332,7 +2371,10 @@ hipError_t launch_ffn_w8a16(const FfnProblem& p, hipStream_t stream) {
   if (st & MOE_FFN_STAGE_FC1) {
     Fc1Args a{p.x, nullptr, p.w1, p.w1_scale, p.sorted_ids, p.block_expert, p.num_padded,
               p.H, p.I, p.k, S, log2m, remap, h, nullptr};
-    fc1_w8a16_kernel<<<persistent_grid(fc1_w8a16_kernel), 256, 0, stream>>>(a);
+    if (sliced_fc1(false, p.T))
+      fc1_w8a16_sliced_kernel<<<persistent_grid(fc1_w8a16_sliced_kernel), 256, 0, stream>>>(a);
+    else
+      fc1_w8a16_kernel<<<persistent_grid(fc1_w8a16_kernel), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_FC2) {
@@ -2365,7 +2407,10 @@ hipError_t launch_ffn_fp8_block(const FfnProblem& p, hipStream_t stream) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
     Fc1Args a{xq, xs, p.w1, p.w1_scale, p.sorted_ids, p.block_expert, p.num_padded,
               p.H, p.I, p.k, S, log2m, remap, h, nullptr};
-    fc1_blk_kernel<<<persistent_grid(fc1_blk_kernel), 256, 0, stream>>>(a);
+    if (sliced_fc1(false, p.T))
+      fc1_blk_sliced_kernel<<<persistent_grid(fc1_blk_sliced_kernel), 256, 0, stream>>>(a);
+    else
+      fc1_blk_kernel<<<persistent_grid(fc1_blk_kernel), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_FC2) {
