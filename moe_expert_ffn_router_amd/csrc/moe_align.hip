@@ -150,31 +150,35 @@ __global__ __launch_bounds__(NW * kWave) void align_kernel(
   align_body<NW>(ids, S, E, log2m, cap, sorted_ids, block_expert, num_padded, cnt, off);
 }
 
-// Alignment of a small batch (S <= 256 slots): one thread per slot. A slot's
-// rank among its expert's slots is the number of equal ids before it in slot
-// order (a pass over the ids in LDS), the expert counts come from LDS atomic
-// increments (order-free), and one scan of the padded counts over the first
-// 256 threads gives the offsets: the same placement as align_body, with three
-// barriers instead of its per-wave tables. ids may live in global memory or
-// in LDS; every thread of the workgroup (256 or more) calls this.
-constexpr int kAlignSmallSlots = 256;
+// Alignment of a small batch (S <= NT slots, NT = 256, 512 or 1024 threads):
+// one thread per slot. A slot's rank among its expert's slots is the number
+// of equal ids before it in slot order (a pass over the ids in LDS), the
+// expert counts come from LDS atomic increments (order-free), and one scan of
+// the padded counts over the workgroup gives the offsets: the same placement
+// as align_body, with three barriers instead of its per-wave tables. ids may
+// live in global memory or in LDS; every thread of the workgroup (NT or more)
+// calls this.
+constexpr int kAlignSmallSlots = 1024;  // the largest NT
 
+template <int NT>
 struct AlignSmallLds {
-  int ids[kAlignSmallSlots];
+  alignas(16) int ids[NT];
   int cnt[kAlignMaxE];
   int off[kAlignMaxE];
-  int wsum[kAlignSmallSlots / kWave];
+  int wsum[NT / kWave];
 };
 
+template <int NT>
 __device__ __forceinline__ void align_small_body(const int32_t* ids, int S, int E, int log2m,
                                                  int cap, int32_t* __restrict__ sorted_ids,
                                                  int32_t* __restrict__ block_expert,
                                                  int32_t* __restrict__ num_padded,
-                                                 AlignSmallLds& L) {
+                                                 AlignSmallLds<NT>& L) {
+  static_assert(kAlignMaxE % NT == 0 && NT % kWave == 0, "small alignment width");
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, nt = blockDim.x;
   const int M = 1 << log2m;
   const int e = t < S ? ids[t] : -1;
-  if (t < kAlignSmallSlots) L.ids[t] = e;
+  if (t < NT) L.ids[t] = e;
   for (int i = t; i < E; i += nt) L.cnt[i] = 0;
   for (int i = t; i < cap; i += nt) sorted_ids[i] = S;
   for (int i = t; i < (cap >> log2m); i += nt) block_expert[i] = -1;
@@ -182,13 +186,21 @@ __device__ __forceinline__ void align_small_body(const int32_t* ids, int S, int 
   const bool valid = (unsigned)e < (unsigned)E;  // else: remote slot or past S
   int rank = 0;
   if (valid) {
-    for (int q = 0; q < t; ++q) rank += L.ids[q] == e;
+    // ids before this slot, four per LDS read
+    const int4* v4 = (const int4*)L.ids;
+    int q = 0;
+    for (; q + 4 <= t; q += 4) {
+      const int4 v = v4[q >> 2];
+      rank += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
+    }
+    for (; q < t; ++q) rank += L.ids[q] == e;
     atomicAdd(&L.cnt[e], 1);
   }
   __syncthreads();
-  // exclusive scan of the padded counts: thread t < 256 owns experts [4t, 4t + 4)
-  constexpr int kPer = kAlignMaxE / kAlignSmallSlots;
-  const bool scan = t < kAlignSmallSlots;
+  // exclusive scan of the padded counts: thread t < NT owns experts
+  // [kPer t, kPer t + kPer)
+  constexpr int kPer = kAlignMaxE / NT;
+  const bool scan = t < NT;
   int pc[kPer], local = 0, incl = 0;
   if (scan) {
 #pragma unroll
@@ -218,18 +230,19 @@ __device__ __forceinline__ void align_small_body(const int32_t* ids, int S, int 
       }
       run += pc[i];
     }
-    if (t == kAlignSmallSlots - 1) num_padded[0] = run;
+    if (t == NT - 1) num_padded[0] = run;
   }
   __syncthreads();
   if (valid) sorted_ids[L.off[e] + rank] = t;
 }
 
-__global__ __launch_bounds__(kAlignSmallSlots) void align_small_kernel(
+template <int NT>
+__global__ __launch_bounds__(NT) void align_small_kernel(
     const int32_t* __restrict__ ids, int S, int E, int log2m, int cap,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
     int32_t* __restrict__ num_padded) {
-  __shared__ AlignSmallLds L;
-  align_small_body(ids, S, E, log2m, cap, sorted_ids, block_expert, num_padded, L);
+  __shared__ AlignSmallLds<NT> L;
+  align_small_body<NT>(ids, S, E, log2m, cap, sorted_ids, block_expert, num_padded, L);
 }
 
 // Routing and alignment of a small batch in one launch: wave w routes token w
@@ -249,7 +262,7 @@ __global__ __launch_bounds__(kAlignThreads) void route_align_kernel(
       int cnt[kAlignWaves][kAlignMaxE];
       int off[kAlignMaxE + 1];
     } wide;
-    AlignSmallLds small;
+    AlignSmallLds<kAlignThreads> small;
   } lds;
   __shared__ int32_t ids_lds[kFuseMaxSlots];
   const int t = threadIdx.x >> 6;
@@ -259,9 +272,9 @@ __global__ __launch_bounds__(kAlignThreads) void route_align_kernel(
     route_token<VPL>(v, t, E, k, renorm, ids, wts, ids_lds);
   }
   __syncthreads();
-  if (T * k <= kAlignSmallSlots)
-    align_small_body(ids_lds, T * k, E, log2m, cap, sorted_ids, block_expert, num_padded,
-                     lds.small);
+  if (T * k <= kAlignThreads)
+    align_small_body<kAlignThreads>(ids_lds, T * k, E, log2m, cap, sorted_ids, block_expert,
+                                    num_padded, lds.small);
   else
     align_body<kAlignWaves>(ids_lds, T * k, E, log2m, cap, sorted_ids, block_expert, num_padded,
                             lds.wide.cnt, lds.wide.off);
@@ -307,9 +320,12 @@ hipError_t launch_align(const int32_t* ids, int S, int E, int block_m, int cap,
                         hipStream_t stream) {
   int log2m = 0;
   while ((1 << log2m) < block_m) ++log2m;
-  if (S <= kAlignSmallSlots)
-    align_small_kernel<<<1, kAlignSmallSlots, 0, stream>>>(ids, S, E, log2m, cap, sorted_ids,
-                                                            block_expert, num_padded);
+  if (S <= 256)
+    align_small_kernel<256><<<1, 256, 0, stream>>>(ids, S, E, log2m, cap, sorted_ids,
+                                                   block_expert, num_padded);
+  else if (S <= kAlignSmallSlots)
+    align_small_kernel<kAlignSmallSlots><<<1, kAlignSmallSlots, 0, stream>>>(
+        ids, S, E, log2m, cap, sorted_ids, block_expert, num_padded);
   else if (S >= kAlignWideSlots)  // many slots: 16 waves share the two passes over them
     align_kernel<kAlignWideWaves><<<1, kAlignWideWaves * kWave, 0, stream>>>(
         ids, S, E, log2m, cap, sorted_ids, block_expert, num_padded);

@@ -63,9 +63,10 @@ def test_route_empty_batch():
 @pytest.mark.parametrize("T,E,k,kind", [
     (16, 64, 8, "uniform"), (64, 128, 8, "zipf"), (37, 16, 3, "uniform"), (100, 8, 2, "one"),
     (1, 1, 1, "uniform"), (4096, 128, 8, "uniform"), (777, 1024, 5, "zipf"),
-    # around the one-thread-per-slot kernel's limit of 256 slots, with all 1024 experts
+    # around the limits of the one-thread-per-slot kernels (256 and 1024 slots), with up
+    # to 1024 experts
     (16, 1024, 16, "zipf"), (32, 1024, 8, "uniform"), (257, 8, 1, "uniform"),
-    (255, 3, 1, "one")])
+    (255, 3, 1, "one"), (128, 1024, 8, "zipf"), (1025, 8, 1, "uniform"), (512, 2, 2, "one")])
 def test_align_bit_exact(T, E, k, kind, block_m):
     say(f"align T={T} E={E} k={k} {kind} block_m={block_m}")
     ids = draw_topk_ids(T, E, k, seed=T + E + block_m, kind=kind)
@@ -110,7 +111,7 @@ def test_align_max_slots():
 @pytest.mark.parametrize("T,E,k,kind", [
     (1, 1, 1, "normal"), (8, 64, 8, "normal"), (5, 1024, 32, "normal"), (3, 65, 65, "ties"),
     (8, 1024, 512, "ties"),                       # 4096 slots: the largest single-launch batch
-    (8, 1024, 32, "ties"), (8, 1024, 33, "ties"),  # 256 and 264 slots: both alignment bodies
+    (8, 1024, 64, "ties"), (8, 1024, 65, "ties"),  # 512 and 520 slots: both alignment bodies
     (9, 64, 8, "normal"), (16, 64, 8, "normal"),  # larger batches: the two-kernel path
     (64, 128, 8, "ties"), (300, 16, 4, "ties")])
 def test_route_align_matches_separate_calls(T, E, k, kind, block_m):
