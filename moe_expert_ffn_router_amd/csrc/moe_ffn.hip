@@ -25,6 +25,13 @@
 //    in the plain 16x16 MFMA layout, reading next chunk's weights while it
 //    multiplies the current one, and takes B fragments from LDS, so the
 //    activations cross L2 once per quad instead of once per wave.
+// Batches of at most 16 tokens take launches without the hot path (more
+// registers for deeper load groups); their FC1 splits each cold tile's K range
+// over the 4 waves of a workgroup instead (bf16 up to 16 tokens, the other
+// formats up to 8), with (block, tile) units. When units are fewer than
+// workgroups, unit i goes to workgroup i, which spreads them over the CUs.
+// Prefill-sized
+// blocks (block_m >= 128) take grouped-GEMM tiles through LDS instead.
 // FC1 pairs gate rows with the matching up rows inside each tile so that
 // SiLU(gate) * up is formed in registers.
 #include "moe_common.h"
