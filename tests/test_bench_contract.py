@@ -42,3 +42,23 @@ def test_bench_json_line():
     for key in ("value", "unit", "cores", "kind", "sample"):
         assert key in cb, key
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("args,suffix", [
+    (["--config", "3", "--weight-only"], "_w8a16"),
+    (["--config", "3", "--block-fp8"], "_block128"),
+    (["--config", "2", "--small-path"], "_small_path"),
+    (["--config", "3", "--single-launch"], "_single_launch"),
+])
+def test_bench_modes(args, suffix):
+    """Every measurement mode of the benchmark prints one line naming its workload."""
+    r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--steps", "3",
+                        "--warmup", "1", "--no-cpu-baseline", *args],
+                       capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    assert d["config"]["workload"].endswith(suffix)
+    assert d["value"] > 0 and d["roofline"]["achieved"] > 0 and d["cpu_baseline"] is None
