@@ -1847,13 +1847,31 @@ __device__ __forceinline__ void combine8(const YT* __restrict__ y, const float* 
   const int per_row = H >> 3;
   const int t = (int)(i / per_row), n = (int)(i % per_row) * 8;
   float acc[8] = {};
-  for (int j = 0; j < k; ++j) {
-    if ((unsigned)ids[(size_t)t * k + j] >= (unsigned)E) continue;
-    const float wj = w[(size_t)t * k + j];
-    float v[8];
-    load8y(y + ((size_t)t * k + j) * H + n, v);
+  // up to 8 slots at a time: all their loads are issued before the sum, which
+  // then runs in j order and leaves out the slots of other shards (their y rows
+  // are read, in bounds, but never added)
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    const int jn = min(8, k - j0);
+    float v[8][8], wj[8];
+    bool mine[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] += wj * v[q];
+    for (int u = 0; u < 8; ++u) {
+      mine[u] = false;
+      wj[u] = 0.f;
+      if (u < jn) {
+        const size_t s = (size_t)t * k + j0 + u;
+        mine[u] = (unsigned)ids[s] < (unsigned)E;
+        wj[u] = w[s];
+        load8y(y + s * H + n, v[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (mine[u]) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] += wj[u] * v[u][q];
+      }
+    }
   }
   if constexpr (sizeof(OutT) == 2) {
     u32x4 o;
