@@ -48,6 +48,45 @@ def test_config_parity(n):
     assert np.all(np.isfinite(got))
 
 
+@pytest.mark.parametrize("block_m", [128, 256])
+def test_prefill_workload_block_sizes(block_m):
+    # the prefill workload through both grouped-GEMM tilings: 128-token blocks
+    # (512-row register-streamed tiles) and 256-token blocks (256-row tiles)
+    inp = cfg_inputs(5)
+    say(f"ffn config 5 block_m={block_m}")
+    ids, w, al, out = gpu_forward(inp, block_m)
+    tokens = SAMPLE[5]
+    ids_o, w_o, ref = oracle_forward(inp, tokens)
+    check_routing(ids, w, ids_o, w_o)
+    check_align(al, ids_o, inp.E, block_m, inp.S)
+    err = oracle.normwise_rel_err(out_f64(out)[tokens], ref)
+    say(f"  normwise rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+PREFILL_CASES = [  # T, E, H, I, k, routing: several row tiles, ragged blocks,
+    (700, 8, 1024, 384, 2, "normal"),    # FC1 2I = 768: half of the second 512-row tile idle
+    (333, 4, 640, 512, 3, "zipf"),       # FC2 H = 640: one full and one 128-row tile
+    (129, 1, 256, 128, 1, "normal"),     # one expert: a full block and a 1-token block
+]
+
+
+@pytest.mark.parametrize("block_m", [128, 256])
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: "T{}_E{}_H{}_I{}_k{}_{}".format(*c))
+def test_prefill_tiles_ragged(case, block_m):
+    T, E, H, I, k, routing = case
+    say(f"ffn prefill tiles T={T} E={E} H={H} I={I} k={k} {routing} block_m={block_m}")
+    inp = make_inputs(T, E, H, I, k, dtype="bf16", routing=routing, seed=T + block_m,
+                      device="cuda")
+    ids, w, al, out = gpu_forward(inp, block_m)
+    ids_o, w_o, ref = oracle_forward(inp)
+    check_routing(ids, w, ids_o, w_o)
+    check_align(al, ids_o, E, block_m, inp.S)
+    err = oracle.normwise_rel_err(out_f64(out), ref)
+    say(f"  normwise rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 CASES = [  # T, E, H, I, k, routing
     (37, 16, 256, 384, 3, "normal"),
     (5, 4, 128, 128, 4, "normal"),
