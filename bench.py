@@ -111,7 +111,8 @@ def cpu_baseline(inp, target_s: float, weight_only: bool = False):
     w1h, w2h = {}, {}
     t_spent, n, per_tok = 0.0, 0, []
     sample_out = None
-    while n < inp.T and t_spent < target_s:
+    reps, t_full = 0, 0.0  # whole-batch evaluations, once n reaches T
+    while (n < inp.T and t_spent < target_s) or (n == inp.T and t_full < target_s):
         n_next = min(inp.T, max(n + 1, 2 * n))
         for e in np.unique(ids_all[:n_next]):
             e = int(e)
@@ -142,13 +143,21 @@ def cpu_baseline(inp, target_s: float, weight_only: bool = False):
         dt = time.perf_counter() - t0
         t_spent += dt
         per_tok.append((n_next, dt))
+        if n_next == inp.T:
+            # a batch too small for target_s is evaluated again until it is reached
+            reps, t_full = reps + 1, t_full + dt
         n = n_next
-    n_last, dt_last = per_tok[-1]
-    return {"value": n_last / dt_last, "unit": "tokens/s",
-            "cores": blas_threads, "kind": "oracle",
-            "sample": f"first {n_last} of {inp.T} tokens of the same workload "
-                      f"(oracle route + fp64 FFN incl. bf16/e4m3 decode), {dt_last:.2f} s",
-            "host_cpus": len(os.sched_getaffinity(0))}, sample_out
+    if reps:
+        value = reps * inp.T / t_full
+        sample = (f"all {inp.T} tokens of the same workload, evaluated {reps} time(s) "
+                  f"(oracle route + fp64 FFN incl. bf16/e4m3 decode), {t_full:.2f} s")
+    else:
+        n_last, dt_last = per_tok[-1]
+        value = n_last / dt_last
+        sample = (f"first {n_last} of {inp.T} tokens of the same workload "
+                  f"(oracle route + fp64 FFN incl. bf16/e4m3 decode), {dt_last:.2f} s")
+    return {"value": value, "unit": "tokens/s", "cores": blas_threads, "kind": "oracle",
+            "sample": sample, "host_cpus": len(os.sched_getaffinity(0))}, sample_out
 
 
 def main():
