@@ -182,6 +182,15 @@ MUT_ORIG_FFN_FP8 = om.ffn_fp8
 MUT_ORIG_FFN_W8A16 = om.ffn_w8a16
 MUT_ORIG_FFN_FP8_BLOCK = om.ffn_fp8_block
 
+def _capacity_all_experts(S, E, block_m):
+    cap = S + E * (block_m - 1)
+    return -(-cap // block_m) * block_m
+
+
+def _capacity_not_rounded(S, E, block_m):
+    return S + min(E, S) * (block_m - 1)
+
+
 MUTATIONS = [
     ("route", _route_ascending, [lambda: R.test_topk_ids_match_brute_force(7, 64, 8)]),
     ("route", _route_ties_high, [R.test_topk_hand_worked_ties]),
@@ -206,6 +215,11 @@ MUTATIONS = [
      [lambda: B.test_ffn_fp8_block_matches_blockwise_loops(1, 1)]),
     ("ffn_w8a16", _ffn_w8a16_quantises_x,
      [lambda: F.test_ffn_w8a16_matches_brute_force_with_library_decode(2, 3, 5, 3, 2)]),
+    ("align_capacity", _capacity_all_experts,
+     [lambda: R.test_align_capacity_hand_worked(4, 8, 16, 64)]),
+    ("align_capacity", _capacity_not_rounded,
+     [lambda: R.test_align_capacity_hand_worked(5, 2, 4, 12),
+      lambda: R.test_align_capacity_bounds_every_routing(5, 2, 4)]),
 ]
 
 

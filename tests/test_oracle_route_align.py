@@ -131,3 +131,42 @@ def test_align_invariants_large():
         assert np.all(ids.reshape(-1)[valid] == b[blk])
         # padding only after an expert's run: valid entries form a prefix
         assert np.all(rows[:valid.size] < S)
+
+
+# align_capacity: the length the caller allocates for sorted_ids. Worked by
+# hand from its definition (every active expert, of which there are at most
+# min(E, S), pads its run by fewer than block_m entries; the total is rounded
+# up to a whole block), one case per branch of that definition.
+@pytest.mark.parametrize("S,E,M,want", [
+    (4, 8, 16, 64),     # S < E: 4 active at most -> 4 + 4*15 = 64, already a multiple of 16
+    (128, 64, 64, 4160),  # S >= E: 128 + 64*63 = 4160 = 65*64
+    (7, 3, 1, 7),       # M = 1: no padding at all
+    (5, 2, 4, 12),      # 5 + 2*3 = 11, rounded up to 12
+    (6, 2, 4, 12),      # 6 + 2*3 = 12: an exact multiple stays as it is
+    (0, 8, 16, 0),      # no slot, no block
+    (1, 1024, 256, 256),  # one slot: one block
+])
+def test_align_capacity_hand_worked(S, E, M, want):
+    assert oracle.align_capacity(S, E, M) == want
+
+
+def _compositions(S, E):
+    """Every way of giving S slots to E experts (count vectors)."""
+    if E == 1:
+        yield (S,)
+        return
+    for c in range(S + 1):
+        for rest in _compositions(S - c, E - 1):
+            yield (c,) + rest
+
+
+@pytest.mark.parametrize("S,E,M", [(5, 2, 4), (6, 3, 4), (7, 4, 2), (3, 5, 8), (8, 3, 3)])
+def test_align_capacity_bounds_every_routing(S, E, M):
+    # brute force over all expert-count vectors: the padded length of any
+    # routing fits, and the capacity is a whole number of blocks
+    cap = oracle.align_capacity(S, E, M)
+    assert cap % M == 0
+    worst = max(sum(-(-c // M) * M for c in cnt) for cnt in _compositions(S, E))
+    assert worst <= cap
+    # the bound is not loose by a whole block per expert
+    assert cap - worst < min(E, S) * M
