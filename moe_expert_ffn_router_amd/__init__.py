@@ -115,31 +115,73 @@ def _stream(stream: Optional[torch.cuda.Stream]) -> int:
     return s.cuda_stream
 
 
-def _need(t: torch.Tensor, name: str, dtypes, device=None) -> None:
+def _need(t: torch.Tensor, name: str, dtypes, device=None, shape=None,
+          min_numel: Optional[int] = None) -> None:
+    """Check one tensor argument before its pointer reaches the library (the C
+    ABI sees only addresses, so a wrong shape, dtype or device would be read or
+    written out of bounds on the GPU): a contiguous device tensor of one of
+    ``dtypes``, on ``device``, of exactly ``shape`` and/or at least
+    ``min_numel`` elements."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
-        raise ValueError(f"{name} must be a device (cuda/hip) tensor")
-    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be a device (cuda/hip) tensor, got {t.device}")
+    if device is not None and t.device != torch.device(device):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs at least {min_numel}")
+
+
+def _dims(t: torch.Tensor, name: str, ndim: int) -> tuple:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    return tuple(t.shape)
+
+
+_FP8 = (torch.uint8, torch.float8_e4m3fn)
 
 
 # ------------------------------------------------------------- routing ---
 
+def _routing_outputs(out, T, k, dev):
+    if out is None:
+        return (torch.empty((T, k), dtype=torch.int32, device=dev),
+                torch.empty((T, k), dtype=torch.float32, device=dev))
+    ids, wts = out
+    _need(ids, "topk_ids", (torch.int32,), dev, (T, k))
+    _need(wts, "topk_weights", (torch.float32,), dev, (T, k))
+    return ids, wts
+
+
+def _align_outputs(out, T, k, E, block_m, dev):
+    cap = align_capacity(T, k, E, block_m)
+    nblk = cap // block_m if block_m > 0 else 0
+    if out is None:
+        return (torch.empty(cap, dtype=torch.int32, device=dev),
+                torch.empty(nblk, dtype=torch.int32, device=dev),
+                torch.empty(1, dtype=torch.int32, device=dev))
+    sorted_ids, block_expert, num_padded = out
+    _need(sorted_ids, "sorted_ids", (torch.int32,), dev, min_numel=cap)
+    _need(block_expert, "block_expert", (torch.int32,), dev, min_numel=nblk)
+    _need(num_padded, "num_padded", (torch.int32,), dev, min_numel=1)
+    return sorted_ids, block_expert, num_padded
+
+
 def route_topk(logits: torch.Tensor, k: int, renormalize: bool = False, out=None,
                stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Router softmax + top-k (moe_route_topk). logits [T, E] float32."""
+    """Router softmax + top-k (moe_route_topk). logits [T, E] float32; ``out``
+    = (topk_ids [T, k] int32, topk_weights [T, k] float32) to write into."""
+    T, E = _dims(logits, "logits", 2)
     _need(logits, "logits", (torch.float32,))
-    T, E = logits.shape
-    if out is None:
-        ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
-        wts = torch.empty((T, k), dtype=torch.float32, device=logits.device)
-    else:
-        ids, wts = out
+    ids, wts = _routing_outputs(out, T, k, logits.device)
     _check(lib.moe_route_topk(_ptr(logits), T, E, k, int(bool(renormalize)), _ptr(ids),
                               _ptr(wts), _stream(stream)))
     return ids, wts
@@ -156,17 +198,12 @@ def default_block_m(T: int, E: int, k: int) -> int:
 
 def align_block(topk_ids: torch.Tensor, E: int, block_m: int, out=None, stream=None):
     """Token-to-expert alignment (moe_align_block). Returns device tensors
-    (sorted_ids [cap], block_expert [cap/block_m], num_padded [1])."""
+    (sorted_ids [cap], block_expert [cap/block_m], num_padded [1]); ``out`` may
+    supply them (at least that many elements each)."""
+    T, k = _dims(topk_ids, "topk_ids", 2)
     _need(topk_ids, "topk_ids", (torch.int32,))
-    T, k = topk_ids.shape
-    cap = align_capacity(T, k, E, block_m)
-    if out is None:
-        dev = topk_ids.device
-        sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
-        block_expert = torch.empty(cap // max(block_m, 1), dtype=torch.int32, device=dev)
-        num_padded = torch.empty(1, dtype=torch.int32, device=dev)
-    else:
-        sorted_ids, block_expert, num_padded = out
+    sorted_ids, block_expert, num_padded = _align_outputs(out, T, k, E, block_m,
+                                                          topk_ids.device)
     _check(lib.moe_align_block(_ptr(topk_ids), T, k, E, block_m, _ptr(sorted_ids),
                                _ptr(block_expert), _ptr(num_padded), _stream(stream)))
     return sorted_ids, block_expert, num_padded
@@ -180,18 +217,15 @@ def route_align(logits: torch.Tensor, k: int, block_m: int, renormalize: bool = 
     """Routing and alignment in one call (moe_route_align). logits [T, E] float32.
     Returns (topk_ids, topk_weights, sorted_ids, block_expert, num_padded), or
     fills `out`, a tuple of those five tensors."""
+    T, E = _dims(logits, "logits", 2)
     _need(logits, "logits", (torch.float32,))
-    T, E = logits.shape
     dev = logits.device
     if out is None:
-        cap = align_capacity(T, k, E, block_m)
-        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-        wts = torch.empty((T, k), dtype=torch.float32, device=dev)
-        sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
-        block_expert = torch.empty(cap // max(block_m, 1), dtype=torch.int32, device=dev)
-        num_padded = torch.empty(1, dtype=torch.int32, device=dev)
+        ids, wts = _routing_outputs(None, T, k, dev)
+        sorted_ids, block_expert, num_padded = _align_outputs(None, T, k, E, block_m, dev)
     else:
-        ids, wts, sorted_ids, block_expert, num_padded = out
+        ids, wts = _routing_outputs(out[:2], T, k, dev)
+        sorted_ids, block_expert, num_padded = _align_outputs(out[2:], T, k, E, block_m, dev)
     _check(lib.moe_route_align(_ptr(logits), T, E, k, int(bool(renormalize)), block_m, _ptr(ids),
                                _ptr(wts), _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded),
                                _stream(stream)))
@@ -209,54 +243,76 @@ def alloc_workspace(T, E, H, I, k, block_m, dtype, device) -> torch.Tensor:
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
-def _ffn_common(x, ids, wts, sorted_ids, block_expert, num_padded):
-    _need(ids, "topk_ids", (torch.int32,), x.device)
-    _need(wts, "topk_weights", (torch.float32,), x.device)
-    _need(sorted_ids, "sorted_ids", (torch.int32,), x.device)
-    _need(block_expert, "block_expert", (torch.int32,), x.device)
-    _need(num_padded, "num_padded", (torch.int32,), x.device)
+def _ffn_args(x, w1, w2, wdtypes, xdtypes, topk_ids, topk_weights, sorted_ids, block_expert,
+              num_padded, block_m):
+    """Shapes of an FFN call, checked against each other: x [T, H], w1 [E, 2I, H],
+    w2 [E, H, I], routing [T, k], alignment buffers that hold the capacity of
+    ``block_m``. Returns (T, E, H, I, k)."""
+    T, H = _dims(x, "x", 2)
+    _need(x, "x", xdtypes)
+    dev = x.device
+    E, I2, H1 = _dims(w1, "w1", 3)
+    if H1 != H or I2 % 2:
+        raise ValueError(f"w1 has shape {tuple(w1.shape)}, expected [E, 2I, H={H}]")
+    I = I2 // 2
+    _need(w1, "w1", wdtypes, dev)
+    _need(w2, "w2", wdtypes, dev, (E, H, I))
+    Tk = _dims(topk_ids, "topk_ids", 2)
+    if Tk[0] != T:
+        raise ValueError(f"topk_ids has {Tk[0]} rows, x has {T}")
+    k = Tk[1]
+    _need(topk_ids, "topk_ids", (torch.int32,), dev, (T, k))
+    _need(topk_weights, "topk_weights", (torch.float32,), dev, (T, k))
+    _align_outputs((sorted_ids, block_expert, num_padded), T, k, E, block_m, dev)
+    return T, E, H, I, k
+
+
+def _ffn_buffers(x, T, E, H, I, k, block_m, dtype, out_dtype, workspace, out):
+    dev = x.device
+    if workspace is None:
+        workspace = alloc_workspace(T, E, H, I, k, block_m, dtype, dev)
+    else:
+        _need(workspace, "workspace", (torch.uint8,), dev,
+              min_numel=workspace_bytes(T, E, H, I, k, block_m, dtype))
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=dev)
+    else:
+        _need(out, "out", (out_dtype,), dev, (T, H))
+    return workspace, out
 
 
 def ffn_bf16(x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert, num_padded,
              block_m: int, flags: int = 0, workspace=None, out=None, stream=None):
     """moe_ffn_bf16: x [T,H], w1 [E,2I,H], w2 [E,H,I] bfloat16 -> out [T,H] bfloat16."""
-    _need(x, "x", (torch.bfloat16,))
-    _need(w1, "w1", (torch.bfloat16,), x.device)
-    _need(w2, "w2", (torch.bfloat16,), x.device)
-    _ffn_common(x, topk_ids, topk_weights, sorted_ids, block_expert, num_padded)
-    T, H = x.shape
-    E, I2, _ = w1.shape
-    k = topk_ids.shape[1]
-    if workspace is None:
-        workspace = alloc_workspace(T, E, H, I2 // 2, k, block_m, MOE_DTYPE_BF16, x.device)
-    if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    T, E, H, I, k = _ffn_args(x, w1, w2, (torch.bfloat16,), (torch.bfloat16,), topk_ids,
+                              topk_weights, sorted_ids, block_expert, num_padded, block_m)
+    workspace, out = _ffn_buffers(x, T, E, H, I, k, block_m, MOE_DTYPE_BF16, torch.bfloat16,
+                                  workspace, out)
     _check(lib.moe_ffn_bf16(_ptr(x), _ptr(w1), _ptr(w2), _ptr(topk_ids), _ptr(topk_weights),
                             _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded), T, E, H,
-                            I2 // 2, k, block_m, flags, _ptr(workspace), workspace.numel(),
+                            I, k, block_m, flags, _ptr(workspace), workspace.numel(),
                             _ptr(out), _stream(stream)))
     return out
 
 
+def _scale_shapes(dtype, E, H, I):
+    if dtype == MOE_DTYPE_FP8_BLOCK:
+        return (E, 2 * I // 128, H // 128), (E, H // 128, I // 128)
+    return (E, 2 * I), (E, H)
+
+
 def _ffn_scaled(fn, dtype, x, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids,
-                block_expert, num_padded, block_m, flags, workspace, out, stream):
-    fp8 = (torch.uint8, torch.float8_e4m3fn)
-    _need(x, "x", (torch.bfloat16,))
-    _need(w1, "w1", fp8, x.device)
-    _need(w2, "w2", fp8, x.device)
-    _need(w1_scale, "w1_scale", (torch.float32,), x.device)
-    _need(w2_scale, "w2_scale", (torch.float32,), x.device)
-    _ffn_common(x, topk_ids, topk_weights, sorted_ids, block_expert, num_padded)
-    T, H = x.shape
-    E, I2, _ = w1.shape
-    k = topk_ids.shape[1]
-    if workspace is None:
-        workspace = alloc_workspace(T, E, H, I2 // 2, k, block_m, dtype, x.device)
-    if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+                block_m, flags, workspace, out, stream, block_expert, num_padded):
+    T, E, H, I, k = _ffn_args(x, w1, w2, _FP8, (torch.bfloat16,), topk_ids, topk_weights,
+                              sorted_ids, block_expert, num_padded, block_m)
+    s1, s2 = _scale_shapes(dtype, E, H, I)
+    _need(w1_scale, "w1_scale", (torch.float32,), x.device, s1)
+    _need(w2_scale, "w2_scale", (torch.float32,), x.device, s2)
+    workspace, out = _ffn_buffers(x, T, E, H, I, k, block_m, dtype, torch.bfloat16,
+                                  workspace, out)
     _check(fn(_ptr(x), _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale), _ptr(topk_ids),
               _ptr(topk_weights), _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded), T, E,
-              H, I2 // 2, k, block_m, flags, _ptr(workspace), workspace.numel(), _ptr(out),
+              H, I, k, block_m, flags, _ptr(workspace), workspace.numel(), _ptr(out),
               _stream(stream)))
     return out
 
@@ -266,8 +322,8 @@ def ffn_fp8(x, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids, b
     """moe_ffn_fp8: x [T,H] bfloat16; w1 [E,2I,H], w2 [E,H,I] e4m3fn codes (uint8 or
     float8_e4m3fn) with float32 per-output-row scales -> out [T,H] bfloat16."""
     return _ffn_scaled(lib.moe_ffn_fp8, MOE_DTYPE_FP8, x, w1, w1_scale, w2, w2_scale, topk_ids,
-                       topk_weights, sorted_ids, block_expert, num_padded, block_m, flags,
-                       workspace, out, stream)
+                       topk_weights, sorted_ids, block_m, flags, workspace, out, stream,
+                       block_expert, num_padded)
 
 
 def ffn_w8a16(x, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids, block_expert,
@@ -275,8 +331,8 @@ def ffn_w8a16(x, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids,
     """moe_ffn_w8a16: weight-only fp8. Arguments as ffn_fp8; activations stay
     bfloat16 -> out [T,H] bfloat16."""
     return _ffn_scaled(lib.moe_ffn_w8a16, MOE_DTYPE_W8A16, x, w1, w1_scale, w2, w2_scale,
-                       topk_ids, topk_weights, sorted_ids, block_expert, num_padded, block_m,
-                       flags, workspace, out, stream)
+                       topk_ids, topk_weights, sorted_ids, block_m, flags, workspace, out,
+                       stream, block_expert, num_padded)
 
 
 def ffn_fp8_block(x, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids,
@@ -286,27 +342,20 @@ def ffn_fp8_block(x, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sorted_
     float32 scales per 128x128 block (w1_scale [E,2I/128,H/128], w2_scale [E,H/128,I/128])
     -> out [T,H] bfloat16."""
     return _ffn_scaled(lib.moe_ffn_fp8_block, MOE_DTYPE_FP8_BLOCK, x, w1, w1_scale, w2,
-                       w2_scale, topk_ids, topk_weights, sorted_ids, block_expert, num_padded,
-                       block_m, flags, workspace, out, stream)
+                       w2_scale, topk_ids, topk_weights, sorted_ids, block_m, flags, workspace,
+                       out, stream, block_expert, num_padded)
 
 
 def ffn_f32(x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert, num_padded,
             block_m: int, flags: int = 0, workspace=None, out=None, stream=None):
     """moe_ffn_f32: float32 throughout."""
-    _need(x, "x", (torch.float32,))
-    _need(w1, "w1", (torch.float32,), x.device)
-    _need(w2, "w2", (torch.float32,), x.device)
-    _ffn_common(x, topk_ids, topk_weights, sorted_ids, block_expert, num_padded)
-    T, H = x.shape
-    E, I2, _ = w1.shape
-    k = topk_ids.shape[1]
-    if workspace is None:
-        workspace = alloc_workspace(T, E, H, I2 // 2, k, block_m, MOE_DTYPE_F32, x.device)
-    if out is None:
-        out = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    T, E, H, I, k = _ffn_args(x, w1, w2, (torch.float32,), (torch.float32,), topk_ids,
+                              topk_weights, sorted_ids, block_expert, num_padded, block_m)
+    workspace, out = _ffn_buffers(x, T, E, H, I, k, block_m, MOE_DTYPE_F32, torch.float32,
+                                  workspace, out)
     _check(lib.moe_ffn_f32(_ptr(x), _ptr(w1), _ptr(w2), _ptr(topk_ids), _ptr(topk_weights),
                            _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded), T, E, H,
-                           I2 // 2, k, block_m, flags, _ptr(workspace), workspace.numel(),
+                           I, k, block_m, flags, _ptr(workspace), workspace.numel(),
                            _ptr(out), _stream(stream)))
     return out
 
@@ -317,17 +366,18 @@ def forward(x, logits, w1, w2, k: int, block_m: Optional[int] = None, renormaliz
     """route_align -> ffn_{f32,bf16,fp8,w8a16,fp8_block}, dtype taken from w1 (fp8
     codes with 3-d block scales run ffn_fp8_block; with per-row scales ffn_w8a16
     if ``weight_only``, else ffn_fp8); block_m defaults to moe_default_block_m."""
-    E = w1.shape[0]
+    E = _dims(w1, "w1", 3)[0]
     if block_m is None:
         block_m = default_block_m(x.shape[0], E, k)
     ids, wts, sorted_ids, block_expert, num_padded = route_align(logits, k, block_m, renormalize,
                                                                  stream=stream)
-    if w1.dtype in (torch.uint8, torch.float8_e4m3fn):
+    if w1.dtype in _FP8:
         if w1_scale is not None and w1_scale.dim() == 3:
             return ffn_fp8_block(x, w1, w1_scale, w2, w2_scale, ids, wts, sorted_ids,
                                  block_expert, num_padded, block_m, flags, stream=stream)
-        return (ffn_w8a16 if weight_only else ffn_fp8)(x, w1, w1_scale, w2, w2_scale, ids, wts, sorted_ids, block_expert,
-                       num_padded, block_m, flags, stream=stream)
+        return (ffn_w8a16 if weight_only else ffn_fp8)(x, w1, w1_scale, w2, w2_scale, ids, wts,
+                                                       sorted_ids, block_expert, num_padded,
+                                                       block_m, flags, stream=stream)
     if w1.dtype == torch.bfloat16:
         return ffn_bf16(x, w1, w2, ids, wts, sorted_ids, block_expert, num_padded, block_m,
                         flags, stream=stream)
@@ -335,12 +385,52 @@ def forward(x, logits, w1, w2, k: int, block_m: Optional[int] = None, renormaliz
                    stream=stream)
 
 
+# ----------------------------------------------------- small-batch path ---
+
 def small_max_tokens() -> int:
     return int(lib.moe_small_max_tokens())
 
 
 def forward_small_workspace_bytes(T, E, H, I, k, dtype) -> int:
     return int(lib.moe_forward_small_workspace_bytes(T, E, H, I, k, dtype))
+
+
+def _small_args(logits, x, w1, w2, k, fp8, w1_scale, w2_scale):
+    """Shapes of a small-batch forward, checked against each other: logits
+    [T, E], x [T, H], w1 [E, 2I, H], w2 [E, H, I], fp8 scales [E, 2I] and
+    [E, H]. Returns (T, H, E, I, dtype)."""
+    T, H = _dims(x, "x", 2)
+    _need(x, "x", (torch.bfloat16,))
+    dev = x.device
+    E, I2, H1 = _dims(w1, "w1", 3)
+    if H1 != H or I2 % 2:
+        raise ValueError(f"w1 has shape {tuple(w1.shape)}, expected [E, 2I, H={H}]")
+    I = I2 // 2
+    _need(logits, "logits", (torch.float32,), dev, (T, E))
+    wdt = _FP8 if fp8 else (torch.bfloat16,)
+    _need(w1, "w1", wdt, dev)
+    _need(w2, "w2", wdt, dev, (E, H, I))
+    if fp8:
+        _need(w1_scale, "w1_scale", (torch.float32,), dev, (E, 2 * I))
+        _need(w2_scale, "w2_scale", (torch.float32,), dev, (E, H))
+    return T, H, E, I, MOE_DTYPE_FP8 if fp8 else MOE_DTYPE_BF16
+
+
+def _small_outputs(x, T, H, k, out, topk_ids, topk_weights):
+    dev = x.device
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    else:
+        _need(topk_ids, "topk_ids", (torch.int32,), dev, (T, k))
+    if topk_weights is None:
+        topk_weights = torch.empty((T, k), dtype=torch.float32, device=dev)
+    else:
+        _need(topk_weights, "topk_weights", (torch.float32,), dev, (T, k))
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", (torch.bfloat16,), dev, (T, H))
+    return out, topk_ids, topk_weights
 
 
 def forward_small(logits, x, w1, w2, k: int, renormalize: bool = False, w1_scale=None,
@@ -351,30 +441,18 @@ def forward_small(logits, x, w1, w2, k: int, renormalize: bool = False, w1_scale
     flags | FORWARD_ONE_KERNEL). bf16 weights, or e4m3fn codes with per-row
     float32 scales (W8A8). Returns
     (out [T,H] bfloat16, topk_ids [T,k] int32, topk_weights [T,k] float32)."""
-    fp8 = w1.dtype in (torch.uint8, torch.float8_e4m3fn)
-    wdt = (torch.uint8, torch.float8_e4m3fn) if fp8 else (torch.bfloat16,)
-    _need(x, "x", (torch.bfloat16,))
-    _need(logits, "logits", (torch.float32,), x.device)
-    _need(w1, "w1", wdt, x.device)
-    _need(w2, "w2", wdt, x.device)
-    if fp8:
-        _need(w1_scale, "w1_scale", (torch.float32,), x.device)
-        _need(w2_scale, "w2_scale", (torch.float32,), x.device)
-    T, H = x.shape
-    E, I2, _ = w1.shape
-    dtype = MOE_DTYPE_FP8 if fp8 else MOE_DTYPE_BF16
-    if topk_ids is None:
-        topk_ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
-    if topk_weights is None:
-        topk_weights = torch.empty((T, k), dtype=torch.float32, device=x.device)
-    if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    fp8 = w1.dtype in _FP8
+    T, H, E, I, dtype = _small_args(logits, x, w1, w2, k, fp8, w1_scale, w2_scale)
+    out, topk_ids, topk_weights = _small_outputs(x, T, H, k, out, topk_ids, topk_weights)
+    n = forward_small_workspace_bytes(T, E, H, I, k, dtype)
     if workspace is None:
-        n = forward_small_workspace_bytes(T, E, H, I2 // 2, k, dtype)
         workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
+    else:
+        _need(workspace, "workspace", (torch.uint8,), x.device, min_numel=n)
     _check(lib.moe_forward_small(_ptr(logits), _ptr(x), _ptr(w1), _ptr(w1_scale) if fp8 else None,
-                                 _ptr(w2), _ptr(w2_scale) if fp8 else None, T, E, H, I2 // 2, k,
+                                 _ptr(w2), _ptr(w2_scale) if fp8 else None, T, E, H, I, k,
                                  1 if renormalize else 0, dtype, flags, _ptr(topk_ids),
                                  _ptr(topk_weights), _ptr(workspace), workspace.numel(),
                                  _ptr(out), _stream(stream)))
     return out, topk_ids, topk_weights
+

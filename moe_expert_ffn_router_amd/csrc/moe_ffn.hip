@@ -118,6 +118,18 @@ __device__ __forceinline__ int block_valid(const int32_t* __restrict__ sorted_id
   return m;
 }
 
+// Aligned blocks to run: *num_padded / M, clamped to the capacity the
+// alignment buffers hold for this block size, round_up(S + min(E, S)(M - 1),
+// M) / M, so that a num_padded written for another block size cannot make a
+// launch index past sorted_ids or block_expert.
+__device__ __forceinline__ int num_blocks(const int32_t* __restrict__ num_padded, int S, int E,
+                                          int log2m) {
+  const long M = 1L << log2m;
+  const long cap = (S + (long)min(E, S) * (M - 1) + M - 1) >> log2m;
+  const long nb = (long)max(num_padded[0], 0) >> log2m;
+  return (int)min(nb, cap);
+}
+
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 // -------------------------------------------------- operand fragments ---
@@ -402,6 +414,7 @@ struct Fc1Args {
   int H, I, k, S, log2m, remap;
   void* h;             // bf16 [S, I] (bf16 path) or f32 [S, I] (fp8 path)
   int* queue;          // work counters, zero at launch (dense and hot launches)
+  int E;               // experts: a block whose expert lies outside [0, E) is skipped
 };
 
 // Store SiLU(g)*u for 4 consecutive h columns of one slot (WT: device-scope
@@ -606,6 +619,7 @@ struct Fc2Args {
   void* y;             // per-slot FC2 output [S, H]: bf16 (bf16 path) or f32
   int y_bf16;
   int* queue;          // work counters, zero at launch (dense and hot launches)
+  int E;               // experts: a block whose expert lies outside [0, E) is skipped
 };
 
 // Store 4 consecutive FC2 outputs of one slot (WT as store_h).
@@ -1088,7 +1102,7 @@ struct QuadRunner {
     if (b != cur_b) {
       cur_b = b;
       e = p.block_expert[b];
-      m = block_valid(p.sorted_ids, b, M, p.S);
+      m = (unsigned)e < (unsigned)p.E ? block_valid(p.sorted_ids, b, M, p.S) : 0;
       cslot = ti < m ? p.sorted_ids[(size_t)b * M + ti] : p.S;
     }
     if (HOT && m > kColdMax) {
@@ -1127,7 +1141,7 @@ template <bool FP8, bool HOT, bool DYN, typename Args, void (*Cold_)(const Args&
           void (*H4)(const Args&, int, int, int, int, int, int, uint8_t*)>
 __device__ __forceinline__ void run_quads(const Args& p, int n_rt, uint8_t* lds) {
   const int M = 1 << p.log2m;
-  const int nb = p.num_padded[0] >> p.log2m;
+  const int nb = num_blocks(p.num_padded, p.S, p.E, p.log2m);
   const int qpb = n_rt >> 2;  // quads per block (n_rt is a multiple of 4)
   QuadRunner<FP8, HOT, Args, Cold_, H1, H2, H3, H4> qr(p, lds);
   if constexpr (!DYN) {
@@ -1159,7 +1173,7 @@ __host__ __device__ constexpr bool sliced_fc1(bool bf16, int T) {
 // than 8 tokens run one such tile per 8 tokens.
 template <void (*Tile)(const Fc1Args&, int, int, int, f32x4*, int)>
 __device__ __forceinline__ void run_sliced_fc1(const Fc1Args& p, f32x4* __restrict__ red) {
-  const int M = 1 << p.log2m, nb = p.num_padded[0] >> p.log2m, tpb = p.I >> 3;
+  const int M = 1 << p.log2m, nb = num_blocks(p.num_padded, p.S, p.E, p.log2m), tpb = p.I >> 3;
   const int ti = threadIdx.x & 7;
   const Share sh = wg_share((long)nb * tpb, p.remap);
   int j = 0, cur_b = -1, e = 0, m = 0;
@@ -1168,7 +1182,7 @@ __device__ __forceinline__ void run_sliced_fc1(const Fc1Args& p, f32x4* __restri
     if (b != cur_b) {
       cur_b = b;
       e = p.block_expert[b];
-      m = block_valid(p.sorted_ids, b, M, p.S);
+      m = (unsigned)e < (unsigned)p.E ? block_valid(p.sorted_ids, b, M, p.S) : 0;
     }
     for (int t0 = 0; t0 < m; t0 += kColdMax, ++j) {
       const int slot = t0 + ti < m ? p.sorted_ids[(size_t)b * M + t0 + ti] : p.S;
@@ -1512,7 +1526,7 @@ struct UnitMap {
 __global__ __launch_bounds__(kDThreads) void dense_fc1_kernel(Fc1Args p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kDLds];
   const int M = 1 << p.log2m;
-  const int nb = p.num_padded[0] >> p.log2m;
+  const int nb = num_blocks(p.num_padded, p.S, p.E, p.log2m);
   const int n_rt = (2 * p.I) / kDRows;  // 128 gate + 128 up rows per unit
   const int units = nb * n_rt;
   const int w = threadIdx.x >> 6, wr = w & 3, wc = w >> 2, lane = threadIdx.x & 63;
@@ -1524,7 +1538,7 @@ __global__ __launch_bounds__(kDThreads) void dense_fc1_kernel(Fc1Args p) {
     int r, b;
     um.locate(p.block_expert, u, r, b);
     const int e = um.e;
-    const int mb = block_valid(p.sorted_ids, b, M, p.S);
+    const int mb = (unsigned)e < (unsigned)p.E ? block_valid(p.sorted_ids, b, M, p.S) : 0;
     for (int t0 = 0; t0 < mb; t0 += kDTok) {
       const int m = mb - t0;
       DenseStage st;
@@ -1570,7 +1584,7 @@ __global__ __launch_bounds__(kDThreads) void dense_fc1_kernel(Fc1Args p) {
 __global__ __launch_bounds__(kDThreads) void dense_fc2_kernel(Fc2Args p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kDLds];
   const int M = 1 << p.log2m;
-  const int nb = p.num_padded[0] >> p.log2m;
+  const int nb = num_blocks(p.num_padded, p.S, p.E, p.log2m);
   const int n_rt = (p.H + kDRows - 1) / kDRows;  // the last row tile may be partial
   const int units = nb * n_rt;
   const int w = threadIdx.x >> 6, wr = w & 3, wc = w >> 2, lane = threadIdx.x & 63;
@@ -1582,7 +1596,7 @@ __global__ __launch_bounds__(kDThreads) void dense_fc2_kernel(Fc2Args p) {
     int r, b;
     um.locate(p.block_expert, u, r, b);
     const int e = um.e;
-    const int mb = block_valid(p.sorted_ids, b, M, p.S);
+    const int mb = (unsigned)e < (unsigned)p.E ? block_valid(p.sorted_ids, b, M, p.S) : 0;
     for (int t0 = 0; t0 < mb; t0 += kDTok) {
       const int m = mb - t0;
       DenseStage st;
@@ -1920,16 +1934,17 @@ __global__ __launch_bounds__(256) void fc1_f32_kernel(const float* __restrict__ 
                                                       const int32_t* __restrict__ sorted_ids,
                                                       const int32_t* __restrict__ block_expert,
                                                       const int32_t* __restrict__ num_padded,
-                                                      int H, int I, int k, int S, int log2m,
-                                                      float* __restrict__ h) {
+                                                      int E, int H, int I, int k, int S,
+                                                      int log2m, float* __restrict__ h) {
   const int lane = threadIdx.x & 63;
   const long W = (long)gridDim.x * 4;
-  const long total = (long)num_padded[0] * I;
+  const long total = ((long)num_blocks(num_padded, S, E, log2m) << log2m) * I;
   for (long u = (long)blockIdx.x * 4 + (threadIdx.x >> 6); u < total; u += W) {
     const int pos = (int)(u / I), n = (int)(u % I);
     const int slot = sorted_ids[pos];
     if (slot >= S) continue;
     const int e = block_expert[pos >> log2m];
+    if ((unsigned)e >= (unsigned)E) continue;
     const float* xr = x + (size_t)(slot / k) * H;
     const float* gr = w1 + ((size_t)e * 2 * I + n) * H;
     const float* ur = gr + (size_t)I * H;
@@ -1954,16 +1969,17 @@ __global__ __launch_bounds__(256) void fc2_f32_kernel(const float* __restrict__ 
                                                       const int32_t* __restrict__ sorted_ids,
                                                       const int32_t* __restrict__ block_expert,
                                                       const int32_t* __restrict__ num_padded,
-                                                      int H, int I, int S, int log2m,
+                                                      int E, int H, int I, int S, int log2m,
                                                       float* __restrict__ y) {
   const int lane = threadIdx.x & 63;
   const long W = (long)gridDim.x * 4;
-  const long total = (long)num_padded[0] * H;
+  const long total = ((long)num_blocks(num_padded, S, E, log2m) << log2m) * H;
   for (long u = (long)blockIdx.x * 4 + (threadIdx.x >> 6); u < total; u += W) {
     const int pos = (int)(u / H), n = (int)(u % H);
     const int slot = sorted_ids[pos];
     if (slot >= S) continue;
     const int e = block_expert[pos >> log2m];
+    if ((unsigned)e >= (unsigned)E) continue;
     const float* hr = h + (size_t)slot * I;
     const float* wr = w2 + ((size_t)e * H + n) * I;
     float s = 0.f;
@@ -2116,7 +2132,7 @@ __device__ __forceinline__ void small_fc1(const SmallArgs& a, const SmallPlan& P
   const int ti = threadIdx.x & 7;
   const int S = a.T * a.k;
   const Fc1Args f{FP8 ? (const void*)a.xq : (const void*)a.x, a.xs, a.w1, a.w1s, nullptr,
-                  nullptr, nullptr, a.H, a.I, a.k, S, 0, a.remap, a.h, nullptr};
+                  nullptr, nullptr, a.H, a.I, a.k, S, 0, a.remap, a.h, nullptr, a.E};
   if (!sliced_fc1(!FP8, a.T)) {
     const int w = threadIdx.x >> 6, qpu = a.I >> 5;
     const Share sh = wg_share((long)P.nunits * qpu, a.remap);
@@ -2143,7 +2159,7 @@ __device__ __forceinline__ void small_fc2(const SmallArgs& a, const SmallPlan& P
   const int w = threadIdx.x >> 6, ti = threadIdx.x & 7;
   const int S = a.T * a.k;
   const Fc2Args f{FP8 ? (const void*)a.hq : (const void*)a.h, a.hs, a.w2, a.w2s, nullptr,
-                  nullptr, nullptr, a.H, a.I, S, 0, a.remap, a.y, FP8 ? 0 : 1, nullptr};
+                  nullptr, nullptr, a.H, a.I, S, 0, a.remap, a.y, FP8 ? 0 : 1, nullptr, a.E};
   const int qpu = a.H >> 6;
   const Share sh = wg_share((long)P.nunits * qpu, a.remap);
   for (long qd = sh.q0; qd < sh.q1; ++qd) {
@@ -2314,7 +2330,7 @@ hipError_t launch_ffn_bf16(const FfnProblem& p, hipStream_t stream) {
   }
   if (st & MOE_FFN_STAGE_FC1) {
     Fc1Args a{p.x, nullptr, p.w1, nullptr, p.sorted_ids, p.block_expert, p.num_padded,
-              p.H, p.I, p.k, S, log2m, remap, h, queue};
+              p.H, p.I, p.k, S, log2m, remap, h, queue, p.E};
     if (dense)
       dense_fc1_kernel<<<persistent_grid(dense_fc1_kernel, kDThreads), kDThreads, 0, stream>>>(a);
     else if (hot)
@@ -2325,7 +2341,7 @@ hipError_t launch_ffn_bf16(const FfnProblem& p, hipStream_t stream) {
   }
   if (st & MOE_FFN_STAGE_FC2) {
     Fc2Args a{h, nullptr, p.w2, nullptr, p.sorted_ids, p.block_expert, p.num_padded,
-              p.H, p.I, S, log2m, remap, y, 1, queue + kQueues};
+              p.H, p.I, S, log2m, remap, y, 1, queue + kQueues, p.E};
     if (dense)
       dense_fc2_kernel<<<persistent_grid(dense_fc2_kernel, kDThreads), kDThreads, 0, stream>>>(a);
     else if (hot)
@@ -2361,7 +2377,7 @@ hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
     launch_quant_rows<uint16_t>((const uint16_t*)p.x, p.T, p.H, xq, xs, stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     Fc1Args a{xq, xs, p.w1, p.w1_scale, p.sorted_ids, p.block_expert, p.num_padded,
-              p.H, p.I, p.k, S, log2m, remap, h, queue};
+              p.H, p.I, p.k, S, log2m, remap, h, queue, p.E};
     if (hot)
       fc1_kernel<true, true><<<persistent_grid(fc1_kernel<true, true>), 256, 0, stream>>>(a);
     else if (sliced_fc1(false, p.T))
@@ -2374,7 +2390,7 @@ hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
     launch_quant_rows<float>(h, S, p.I, hq, hs, stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     Fc2Args a{hq, hs, p.w2, p.w2_scale, p.sorted_ids, p.block_expert, p.num_padded,
-              p.H, p.I, S, log2m, remap, y, 0, queue + kQueues};
+              p.H, p.I, S, log2m, remap, y, 0, queue + kQueues, p.E};
     if (hot)
       fc2_kernel<true, true><<<persistent_grid(fc2_kernel<true, true>), 256, 0, stream>>>(a);
     else
@@ -2395,7 +2411,7 @@ hipError_t launch_ffn_w8a16(const FfnProblem& p, hipStream_t stream) {
   hipError_t err;
   if (st & MOE_FFN_STAGE_FC1) {
     Fc1Args a{p.x, nullptr, p.w1, p.w1_scale, p.sorted_ids, p.block_expert, p.num_padded,
-              p.H, p.I, p.k, S, log2m, remap, h, nullptr};
+              p.H, p.I, p.k, S, log2m, remap, h, nullptr, p.E};
     if (sliced_fc1(false, p.T))
       fc1_w8a16_sliced_kernel<<<persistent_grid(fc1_w8a16_sliced_kernel), 256, 0, stream>>>(a);
     else
@@ -2404,7 +2420,7 @@ hipError_t launch_ffn_w8a16(const FfnProblem& p, hipStream_t stream) {
   }
   if (st & MOE_FFN_STAGE_FC2) {
     Fc2Args a{h, nullptr, p.w2, p.w2_scale, p.sorted_ids, p.block_expert, p.num_padded,
-              p.H, p.I, S, log2m, remap, y, 1, nullptr};
+              p.H, p.I, S, log2m, remap, y, 1, nullptr, p.E};
     fc2_w8a16_kernel<<<persistent_grid(fc2_w8a16_kernel), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
@@ -2431,7 +2447,7 @@ hipError_t launch_ffn_fp8_block(const FfnProblem& p, hipStream_t stream) {
         (const uint16_t*)p.x, p.T, p.H, xq, xs);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     Fc1Args a{xq, xs, p.w1, p.w1_scale, p.sorted_ids, p.block_expert, p.num_padded,
-              p.H, p.I, p.k, S, log2m, remap, h, nullptr};
+              p.H, p.I, p.k, S, log2m, remap, h, nullptr, p.E};
     if (sliced_fc1(false, p.T))
       fc1_blk_sliced_kernel<<<persistent_grid(fc1_blk_sliced_kernel), 256, 0, stream>>>(a);
     else
@@ -2443,7 +2459,7 @@ hipError_t launch_ffn_fp8_block(const FfnProblem& p, hipStream_t stream) {
     quant_groups_kernel<float><<<(unsigned)((ng + 15) / 16), 256, 0, stream>>>(h, S, p.I, hq, hs);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     Fc2Args a{hq, hs, p.w2, p.w2_scale, p.sorted_ids, p.block_expert, p.num_padded,
-              p.H, p.I, S, log2m, remap, y, 0, nullptr};
+              p.H, p.I, S, log2m, remap, y, 0, nullptr, p.E};
     fc2_blk_kernel<<<persistent_grid(fc2_blk_kernel), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
@@ -2533,14 +2549,14 @@ hipError_t launch_ffn_f32(const FfnProblem& p, hipStream_t stream) {
   const int grid = 1024;
   if (st & MOE_FFN_STAGE_FC1) {
     fc1_f32_kernel<<<grid, 256, 0, stream>>>((const float*)p.x, (const float*)p.w1,
-                                             p.sorted_ids, p.block_expert, p.num_padded, p.H,
-                                             p.I, p.k, S, log2m, h);
+                                             p.sorted_ids, p.block_expert, p.num_padded, p.E,
+                                             p.H, p.I, p.k, S, log2m, h);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_FC2) {
     fc2_f32_kernel<<<grid, 256, 0, stream>>>(h, (const float*)p.w2, p.sorted_ids,
-                                             p.block_expert, p.num_padded, p.H, p.I, S, log2m,
-                                             y);
+                                             p.block_expert, p.num_padded, p.E, p.H, p.I, S,
+                                             log2m, y);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_COMBINE) return launch_combine(p, L, MOE_DTYPE_F32, stream);

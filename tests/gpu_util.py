@@ -45,6 +45,20 @@ def oracle_forward(inp, tokens=None, renormalize=False):
     return ids, w, out
 
 
+@functools.lru_cache(maxsize=None)
+def oracle_full(n: int):
+    """Oracle routing and every output row of workload n (cached: the two
+    largest workloads take seconds of fp64 work, and several tests compare
+    against the same layer)."""
+    return oracle_forward(cfg_inputs(n))
+
+
+def check_finite(out: torch.Tensor) -> None:
+    """Every element of the GPU output is finite (checked on all rows, also
+    where only a subset is compared)."""
+    assert bool(torch.isfinite(out.float()).all()), "non-finite values in the GPU output"
+
+
 def bench_block_m(inp) -> int:
     """The block size bench.py times for this workload."""
     return moe().default_block_m(inp.T, inp.E, inp.k)
