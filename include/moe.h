@@ -25,7 +25,8 @@
  *    `stream` (NULL = the null stream) and returns; it never synchronises the
  *    host, never allocates device memory and keeps no state between calls
  *    other than a per-device cache of launch geometry (CU count and resident
- *    workgroups per kernel).
+ *    workgroups per kernel) and, for moe_forward_small_static only, the
+ *    device address of its static scratch array.
  *  - On a bad argument nothing is launched and the status says why. A launch
  *    failure returns MOE_ERR_HIP. Faults inside a kernel surface at the
  *    caller's next synchronisation, as usual in HIP. Device-resident values
@@ -337,6 +338,32 @@ moe_status moe_forward_small(const float* logits, const uint16_t* x, const void*
                              unsigned flags, int32_t* topk_ids, float* topk_weights,
                              void* workspace, size_t workspace_bytes, uint16_t* out,
                              moe_stream_t stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same
+ * computation, arguments, limits, flags and results (bit for bit) as
+ * moe_forward_small, without the workspace arguments: the intermediates live
+ * in a static device array of MOE_STATIC_SCRATCH_BYTES owned by the library,
+ * one per GPU, allocated when the library's device code is loaded on that
+ * GPU and held until the process ends. The call allocates nothing.
+ *
+ *  Errors: as moe_forward_small; MOE_ERR_WORKSPACE when the layer needs more
+ *  than MOE_STATIC_SCRATCH_BYTES, i.e. when
+ *  moe_forward_small_workspace_bytes(T, E, H, I, k, dtype) exceeds it;
+ *  MOE_ERR_HIP if the array's device address cannot be obtained.
+ *  Every call on one GPU uses that GPU's single array and leaves its
+ *  contents behind; calls that overlap in time on one GPU (two streams, two
+ *  host threads) race and give undefined results. Calls in one stream are
+ *  ordered and safe. The device is the current device, as for every entry
+ *  point.
+ */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+moe_status moe_forward_small_static(const float* logits, const uint16_t* x, const void* w1,
+                                    const float* w1_scale, const void* w2, const float* w2_scale,
+                                    int T, int E, int H, int I, int k, int renormalize,
+                                    int dtype, unsigned flags, int32_t* topk_ids,
+                                    float* topk_weights, uint16_t* out, moe_stream_t stream);
 
 #ifdef __cplusplus
 }

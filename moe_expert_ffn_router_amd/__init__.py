@@ -16,6 +16,7 @@ The names mirror the C ABI in include/moe.h:
     ffn_f32(x, w1, w2, ids, wts, ..., block_m, ...)                                 -> out
     forward(x, logits, w1, w2, k, ...)   convenience chaining of the three calls
     forward_small(logits, x, w1, w2, k, ...) -> (out, topk_ids, topk_weights)   one launch, T <= 16
+    forward_small_static(logits, x, w1, w2, k, ...)   the same without a workspace (allocates nothing)
 """
 from __future__ import annotations
 
@@ -39,7 +40,8 @@ EXPORTS = ("moe_status_str", "moe_abi_version", "moe_route_topk", "moe_align_cap
            "moe_align_block", "moe_route_align", "moe_default_block_m",
            "moe_ffn_workspace_bytes", "moe_ffn_bf16", "moe_ffn_fp8", "moe_ffn_w8a16",
            "moe_ffn_fp8_block", "moe_ffn_f32", "moe_small_max_tokens",
-           "moe_forward_small_workspace_bytes", "moe_forward_small")
+           "moe_forward_small_workspace_bytes", "moe_forward_small", "moe_forward_small_static")
+STATIC_SCRATCH_BYTES = 32 << 20  # MOE_STATIC_SCRATCH_BYTES
 
 
 class MoEError(RuntimeError):
@@ -89,6 +91,8 @@ def _load() -> ctypes.CDLL:
     lib.moe_forward_small_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.moe_forward_small.restype = I
     lib.moe_forward_small.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, U, P, P, P, Z, P, P]
+    lib.moe_forward_small_static.restype = I
+    lib.moe_forward_small_static.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, U, P, P, P, P]
     if lib.moe_abi_version() != ABI_VERSION:
         raise ImportError(f"libmoe ABI {lib.moe_abi_version()} != binding ABI {ABI_VERSION}")
     return lib
@@ -456,3 +460,20 @@ def forward_small(logits, x, w1, w2, k: int, renormalize: bool = False, w1_scale
                                  _ptr(out), _stream(stream)))
     return out, topk_ids, topk_weights
 
+
+def forward_small_static(logits, x, w1, w2, k: int, renormalize: bool = False, w1_scale=None,
+                         w2_scale=None, flags: int = 0, out=None, topk_ids=None,
+                         topk_weights=None, stream=None):
+    """moe_forward_small_static: forward_small with the intermediates in the
+    library's static per-GPU scratch (STATIC_SCRATCH_BYTES) instead of a
+    workspace; the library call allocates nothing (pass ``out``, ``topk_ids``
+    and ``topk_weights`` to allocate nothing here either). Calls that overlap
+    in time on one GPU race. Returns (out, topk_ids, topk_weights)."""
+    fp8 = w1.dtype in (torch.uint8, torch.float8_e4m3fn)
+    T, H, E, I, dtype = _small_args(logits, x, w1, w2, k, fp8, w1_scale, w2_scale)
+    out, topk_ids, topk_weights = _small_outputs(x, T, H, k, out, topk_ids, topk_weights)
+    _check(lib.moe_forward_small_static(
+        _ptr(logits), _ptr(x), _ptr(w1), _ptr(w1_scale) if fp8 else None, _ptr(w2),
+        _ptr(w2_scale) if fp8 else None, T, E, H, I, k, 1 if renormalize else 0, dtype, flags,
+        _ptr(topk_ids), _ptr(topk_weights), _ptr(out), _stream(stream)))
+    return out, topk_ids, topk_weights

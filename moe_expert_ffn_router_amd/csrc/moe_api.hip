@@ -192,6 +192,33 @@ MOE_EXPORT moe_status moe_forward_small(const float* logits, const uint16_t* x, 
   return hip_status(moe::launch_forward_small(p, (hipStream_t)stream));
 }
 
+MOE_EXPORT moe_status moe_forward_small_static(const float* logits, const uint16_t* x,
+                                               const void* w1, const float* w1_scale,
+                                               const void* w2, const float* w2_scale, int T,
+                                               int E, int H, int I, int k, int renormalize,
+                                               int dtype, unsigned flags, int32_t* topk_ids,
+                                               float* topk_weights, uint16_t* out,
+                                               moe_stream_t stream) {
+  static_assert(moe::kStaticScratchBytes == MOE_STATIC_SCRATCH_BYTES, "scratch size");
+  moe_status s = check_small(T, E, H, I, k, dtype, flags);
+  if (s != MOE_OK || T == 0) return s;
+  if (moe::small_workspace_bytes(T, H, I, k, dtype) > moe::kStaticScratchBytes)
+    return MOE_ERR_WORKSPACE;
+  const bool fp8 = dtype == MOE_DTYPE_FP8;
+  if (!logits || !x || !w1 || !w2 || !topk_ids || !topk_weights || !out) return MOE_ERR_NULL;
+  if (fp8 && (!w1_scale || !w2_scale)) return MOE_ERR_NULL;
+  if (!aligned(logits, 4) || !aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) ||
+      !aligned(out, 16) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4) ||
+      (fp8 && (!aligned(w1_scale, 16) || !aligned(w2_scale, 16))))
+    return MOE_ERR_ALIGN;
+  void* ws = nullptr;
+  if (moe::static_scratch(&ws) != hipSuccess) return MOE_ERR_HIP;
+  moe::SmallProblem p{logits, x, w1, fp8 ? w1_scale : nullptr, w2, fp8 ? w2_scale : nullptr,
+                      T, E, H, I, k, renormalize ? 1 : 0, flags, dtype, topk_ids, topk_weights,
+                      ws, out};
+  return hip_status(moe::launch_forward_small(p, (hipStream_t)stream));
+}
+
 MOE_EXPORT int moe_default_block_m(int T, int E, int k) {
   if (check_common(T, E, k) != MOE_OK) return 0;
   return (long)T * k >= 128L * E ? 256 : 64;

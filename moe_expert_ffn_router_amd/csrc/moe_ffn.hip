@@ -2539,6 +2539,34 @@ hipError_t launch_forward_small(const SmallProblem& p, hipStream_t stream) {
   return fp8 ? launch_small<true>(p, a, stream) : launch_small<false>(p, a, stream);
 }
 
+// Scratch of the allocation-free small-batch forward: one copy of this array
+// per GPU, zero at load, held until the process ends. In host code its name
+// is only a stand-in: kernels get the device address hipGetSymbolAddress
+// returns for the current device, fetched once per device and kept. Every
+// call on a GPU reuses the same bytes; whatever must start at zero (the
+// one-kernel mode's barrier words) is cleared by a kernel in each call.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* a = nullptr;
+    err = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (a == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
 hipError_t launch_ffn_f32(const FfnProblem& p, hipStream_t stream) {
   const FfnWorkspace L = ffn_workspace_layout(p.T, p.H, p.I, p.k, MOE_DTYPE_F32);
   const unsigned st = stages(p.flags);

@@ -82,6 +82,12 @@ struct SmallProblem {
 // bytes: the status word).
 size_t small_workspace_bytes(int T, int H, int I, int k, int dtype);
 hipError_t launch_forward_small(const SmallProblem& p, hipStream_t stream);
+
+// Device address (current device) of the static scratch array of the
+// allocation-free small-batch forward, kStaticScratchBytes long; looked up
+// once per device.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+hipError_t static_scratch(void** ptr);
 hipError_t launch_ffn_f32(const FfnProblem& p, hipStream_t stream);
 
 }  // namespace moe

@@ -185,6 +185,32 @@ def test_small_path_validation():
     assert wsb(17, 64, 4096, 1536, 8, 1) == 0 and wsb(16, 64, 4096, 1536, 8, 0) == 0
 
 
+def call_small_static(logits=P, x=P, w1=P, s1=P, w2=P, s2=P, T=16, E=64, H=4096, I=1536, k=8,
+                      renorm=0, dtype=1, flags=0, ids=P, wts=P, out=P):
+    return lib.moe_forward_small_static(logits, x, w1, s1, w2, s2, T, E, H, I, k, renorm, dtype,
+                                        flags, ids, wts, out, None)
+
+
+def test_small_static_validation():
+    # every rejection happens on the host, before the scratch's device address
+    # is looked up (no GPU here)
+    assert call_small_static(T=17) == SHAPE
+    assert call_small_static(H=200) == SHAPE
+    assert call_small_static(dtype=0) == UNSUP
+    assert call_small_static(flags=1) == UNSUP
+    assert call_small_static(logits=None) == NULL
+    assert call_small_static(out=None) == NULL
+    assert call_small_static(dtype=2, s1=None) == NULL
+    assert call_small_static(x=P + 2) == ALIGN
+    assert call_small_static(T=0, logits=None, x=None, out=None) == OK
+    # intermediates beyond the static scratch (32 MiB): y alone is
+    # 256 slots x 32768 x 4 bytes = 32 MiB
+    wsb = lib.moe_forward_small_workspace_bytes
+    assert wsb(16, 16, 32768, 4096, 16, 2) > m.STATIC_SCRATCH_BYTES
+    assert call_small_static(T=16, E=16, H=32768, I=4096, k=16, dtype=2) == WORKSPACE
+    assert wsb(16, 64, 4096, 1536, 8, 2) <= m.STATIC_SCRATCH_BYTES  # the decode workloads fit
+
+
 def test_default_block_m():
     f = lib.moe_default_block_m
     assert f(16, 64, 8) == 64          # decode: 2 slots per expert

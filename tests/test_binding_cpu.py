@@ -26,6 +26,8 @@ def test_host_tensors_are_refused():
         m.ffn_bf16(x, w1, w2, ids, wts, sid, be, npad, 16)
     with pytest.raises(ValueError, match="device"):
         m.forward_small(logits, x, w1, w2, 2)
+    with pytest.raises(ValueError, match="device"):
+        m.forward_small_static(logits, x, w1, w2, 2)
 
 
 def test_non_tensors_and_wrong_ranks_are_refused():

@@ -80,6 +80,9 @@ def test_scaled_and_small_argument_checks(setup):
                                                             device="cuda")))
     _expect(ValueError, lambda: small(topk_ids=torch.empty((6, 3), dtype=torch.int32,
                                                            device="cuda")))
+    _expect(ValueError, lambda: m.forward_small_static(inp.logits, inp.x, inp.w1, inp.w2, inp.k,
+                                                       w1_scale=inp.w1_scale,
+                                                       w2_scale=inp.w2_scale[:, :64].contiguous()))
     _expect(ValueError, lambda: m.route_topk(inp.logits, 2, out=(ids[:3].contiguous(), w)))
     _expect(ValueError, lambda: m.align_block(ids, inp.E, 16, out=(sid[:8], be, npad)))
     call()
