@@ -76,11 +76,17 @@ enum {
  *   FC2      : [fp8: per-slot quantisation of h +] FC2
  *   COMBINE  : top-k weighted combine into `out`
  * MOE_FFN_NO_XCD_REMAP turns off the placement of contiguous weight ranges
- * on one XCD (for A/B measurement); results are identical either way. */
+ * on one XCD (for A/B measurement); results are identical either way.
+ * MOE_FFN_RANGE_GEMM (bf16, block_m >= 128, H and I multiples of 128 and at
+ * least 256): run FC1 and FC2 as 256 x 256 tiles over balanced token ranges
+ * of each expert (up to 256 of its tokens x 256 weight rows) instead of the
+ * default 128-row tiles of the aligned blocks; results agree within the bf16
+ * tolerance. Ignored where its conditions do not hold. */
 #define MOE_FFN_STAGE_FC1 (1u << 0)
 #define MOE_FFN_STAGE_FC2 (1u << 1)
 #define MOE_FFN_STAGE_COMBINE (1u << 2)
 #define MOE_FFN_NO_XCD_REMAP (1u << 8)
+#define MOE_FFN_RANGE_GEMM (1u << 10)
 /* moe_forward_small only: run the whole layer as one cooperative kernel */
 #define MOE_FORWARD_ONE_KERNEL (1u << 9)
 

@@ -34,6 +34,7 @@ MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_FP8, MOE_DTYPE_W8A16, MOE_DTYPE_FP8_BLO
 STAGE_FC1, STAGE_FC2, STAGE_COMBINE = 1 << 0, 1 << 1, 1 << 2
 NO_XCD_REMAP = 1 << 8
 FORWARD_ONE_KERNEL = 1 << 9  # forward_small: the whole layer as one cooperative launch
+RANGE_GEMM = 1 << 10  # bf16 prefill blocks: 256 x 256 tiles over per-expert token ranges
 ABI_VERSION = 1
 
 EXPORTS = ("moe_status_str", "moe_abi_version", "moe_route_topk", "moe_align_capacity",

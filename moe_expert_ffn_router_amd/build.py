@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmoe.so")
-SOURCES = ["moe_api.hip", "moe_route.hip", "moe_align.hip", "moe_ffn.hip"]
+SOURCES = ["moe_api.hip", "moe_route.hip", "moe_align.hip", "moe_ffn.hip", "moe_gemm.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 CFLAGS = [

@@ -43,7 +43,7 @@ moe_status check_ffn(const void* x, const void* w1, const void* w2, const int32_
   if (H < mult || I < mult || H % mult != 0 || I % mult != 0) return MOE_ERR_SHAPE;
   if (!is_pow2_le256(block_m)) return MOE_ERR_SHAPE;
   const unsigned known = MOE_FFN_STAGE_FC1 | MOE_FFN_STAGE_FC2 | MOE_FFN_STAGE_COMBINE |
-                         MOE_FFN_NO_XCD_REMAP;
+                         MOE_FFN_NO_XCD_REMAP | MOE_FFN_RANGE_GEMM;
   if (flags & ~known) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !w1 || !w2 || !topk_ids || !topk_weights || !sorted_ids || !block_expert ||
@@ -53,7 +53,7 @@ moe_status check_ffn(const void* x, const void* w1, const void* w2, const int32_
       !aligned(workspace, 256) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4) ||
       !aligned(sorted_ids, 4) || !aligned(block_expert, 4) || !aligned(num_padded, 4))
     return MOE_ERR_ALIGN;
-  if (workspace_bytes < moe::ffn_workspace_layout(T, H, I, k, dtype).total)
+  if (workspace_bytes < moe::ffn_workspace_layout(T, E, H, I, k, dtype).total)
     return MOE_ERR_WORKSPACE;
   return MOE_OK;
 }
@@ -226,14 +226,14 @@ MOE_EXPORT int moe_default_block_m(int T, int E, int k) {
 
 MOE_EXPORT size_t moe_ffn_workspace_bytes(int T, int E, int H, int I, int k, int block_m,
                                           int dtype) {
-  (void)E;
   (void)block_m;
   if (dtype != MOE_DTYPE_F32 && dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8 &&
       dtype != MOE_DTYPE_W8A16 && dtype != MOE_DTYPE_FP8_BLOCK)
     return 0;
-  if (T < 0 || H < 1 || I < 1 || k < 1) return 0;
+  if (T < 0 || E < 1 || H < 1 || I < 1 || k < 1) return 0;
   // W8A16 keeps the bf16 path's intermediates
-  return moe::ffn_workspace_layout(T, H, I, k, dtype == MOE_DTYPE_W8A16 ? MOE_DTYPE_BF16 : dtype)
+  return moe::ffn_workspace_layout(T, E, H, I, k,
+                                   dtype == MOE_DTYPE_W8A16 ? MOE_DTYPE_BF16 : dtype)
       .total;
 }
 

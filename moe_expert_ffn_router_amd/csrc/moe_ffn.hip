@@ -2229,7 +2229,7 @@ __global__ __launch_bounds__(256) void small_forward_kernel(SmallArgs a) {
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-FfnWorkspace ffn_workspace_layout(int T, int H, int I, int k, int dtype) {
+FfnWorkspace ffn_workspace_layout(int T, int E, int H, int I, int k, int dtype) {
   FfnWorkspace L{};
   const size_t S = (size_t)T * k;
   size_t o = 0;
@@ -2251,6 +2251,7 @@ FfnWorkspace ffn_workspace_layout(int T, int H, int I, int k, int dtype) {
   }
   put(L.y_off, L.y_bytes, S * H * (dtype == MOE_DTYPE_BF16 ? 2 : 4));
   put(L.q_off, L.q_bytes, S ? 2 * kQueues * sizeof(int) : 0);
+  put(L.plan_off, L.plan_bytes, S && E > 0 ? gemm_plan_ints((int)S, E) * sizeof(int) : 0);
   L.total = o;
   return L;
 }
@@ -2314,14 +2315,35 @@ static hipError_t launch_combine(const FfnProblem& p, const FfnWorkspace& L, int
 }
 
 hipError_t launch_ffn_bf16(const FfnProblem& p, hipStream_t stream) {
-  const FfnWorkspace L = ffn_workspace_layout(p.T, p.H, p.I, p.k, MOE_DTYPE_BF16);
+  const FfnWorkspace L = ffn_workspace_layout(p.T, p.E, p.H, p.I, p.k, MOE_DTYPE_BF16);
   const unsigned st = stages(p.flags);
   const int remap = (p.flags & MOE_FFN_NO_XCD_REMAP) ? 0 : 1;
   const int S = p.T * p.k, log2m = ilog2(p.block_m);
   void* h = (char*)p.workspace + L.h_off;
   float* y = (float*)((char*)p.workspace + L.y_off);
   int* queue = (int*)((char*)p.workspace + L.q_off);  // FC1: [0, 8), FC2: [8, 16)
+  int* plan = (int*)((char*)p.workspace + L.plan_off);
   hipError_t err;
+  // prefill-sized blocks, on request: 256 x 256 tiles over token ranges
+  if ((p.flags & MOE_FFN_RANGE_GEMM) && p.block_m >= 128 && gemm_supported(p.T, p.k, p.H, p.I)) {
+    if (st & (MOE_FFN_STAGE_FC1 | MOE_FFN_STAGE_FC2)) {
+      err = launch_gemm_plan(p.sorted_ids, p.block_expert, p.num_padded, S, p.E, log2m, plan,
+                             queue, stream);
+      if (err != hipSuccess) return err;
+    }
+    if (st & MOE_FFN_STAGE_FC1) {
+      err = launch_gemm_fc1(p.x, p.w1, p.sorted_ids, plan, queue, p.H, p.I, p.k, S, remap, h,
+                            stream);
+      if (err != hipSuccess) return err;
+    }
+    if (st & MOE_FFN_STAGE_FC2) {
+      err = launch_gemm_fc2(h, p.w2, p.sorted_ids, plan, queue + kQueues, p.H, p.I, S, remap, y,
+                            stream);
+      if (err != hipSuccess) return err;
+    }
+    if (st & MOE_FFN_STAGE_COMBINE) return launch_combine(p, L, MOE_DTYPE_BF16, stream);
+    return hipSuccess;
+  }
   const bool dense = p.block_m >= 128;  // prefill-sized blocks: grouped GEMM tiles
   const bool hot = p.T > 2 * kColdMax;  // see run_quads
   if ((dense || hot) && (st & (MOE_FFN_STAGE_FC1 | MOE_FFN_STAGE_FC2))) {
@@ -2355,7 +2377,7 @@ hipError_t launch_ffn_bf16(const FfnProblem& p, hipStream_t stream) {
 }
 
 hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
-  const FfnWorkspace L = ffn_workspace_layout(p.T, p.H, p.I, p.k, MOE_DTYPE_FP8);
+  const FfnWorkspace L = ffn_workspace_layout(p.T, p.E, p.H, p.I, p.k, MOE_DTYPE_FP8);
   const unsigned st = stages(p.flags);
   const int remap = (p.flags & MOE_FFN_NO_XCD_REMAP) ? 0 : 1;
   const int S = p.T * p.k, log2m = ilog2(p.block_m);
@@ -2402,7 +2424,7 @@ hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
 }
 
 hipError_t launch_ffn_w8a16(const FfnProblem& p, hipStream_t stream) {
-  const FfnWorkspace L = ffn_workspace_layout(p.T, p.H, p.I, p.k, MOE_DTYPE_BF16);
+  const FfnWorkspace L = ffn_workspace_layout(p.T, p.E, p.H, p.I, p.k, MOE_DTYPE_BF16);
   const unsigned st = stages(p.flags);
   const int remap = (p.flags & MOE_FFN_NO_XCD_REMAP) ? 0 : 1;
   const int S = p.T * p.k, log2m = ilog2(p.block_m);
@@ -2429,7 +2451,7 @@ hipError_t launch_ffn_w8a16(const FfnProblem& p, hipStream_t stream) {
 }
 
 hipError_t launch_ffn_fp8_block(const FfnProblem& p, hipStream_t stream) {
-  const FfnWorkspace L = ffn_workspace_layout(p.T, p.H, p.I, p.k, MOE_DTYPE_FP8_BLOCK);
+  const FfnWorkspace L = ffn_workspace_layout(p.T, p.E, p.H, p.I, p.k, MOE_DTYPE_FP8_BLOCK);
   const unsigned st = stages(p.flags);
   const int remap = (p.flags & MOE_FFN_NO_XCD_REMAP) ? 0 : 1;
   const int S = p.T * p.k, log2m = ilog2(p.block_m);
@@ -2471,7 +2493,7 @@ static_assert(kSmallTokens == kSmallMaxT && kSmallExperts == kSmallMaxE &&
               kSmallSlots == kSmallMaxS, "small-path limits");
 
 size_t small_workspace_bytes(int T, int H, int I, int k, int dtype) {
-  return align_up(ffn_workspace_layout(T, H, I, k, dtype).total, 256) + kBarInts * sizeof(int);
+  return align_up(ffn_workspace_layout(T, 0, H, I, k, dtype).total, 256) + kBarInts * sizeof(int);
 }
 
 template <bool FP8>
@@ -2521,7 +2543,7 @@ static hipError_t launch_small_split(const SmallProblem& p, const SmallArgs& a,
 
 hipError_t launch_forward_small(const SmallProblem& p, hipStream_t stream) {
   const bool fp8 = p.dtype == MOE_DTYPE_FP8;
-  const FfnWorkspace L = ffn_workspace_layout(p.T, p.H, p.I, p.k, p.dtype);
+  const FfnWorkspace L = ffn_workspace_layout(p.T, 0, p.H, p.I, p.k, p.dtype);
   char* ws = (char*)p.workspace;
   int* bar = (int*)(ws + align_up(L.total, 256));
   SmallArgs a{p.logits, (const uint16_t*)p.x, p.w1, p.w1_scale, p.w2, p.w2_scale,
@@ -2568,7 +2590,7 @@ hipError_t static_scratch(void** ptr) {
 }
 
 hipError_t launch_ffn_f32(const FfnProblem& p, hipStream_t stream) {
-  const FfnWorkspace L = ffn_workspace_layout(p.T, p.H, p.I, p.k, MOE_DTYPE_F32);
+  const FfnWorkspace L = ffn_workspace_layout(p.T, p.E, p.H, p.I, p.k, MOE_DTYPE_F32);
   const unsigned st = stages(p.flags);
   const int S = p.T * p.k, log2m = ilog2(p.block_m);
   float* h = (float*)((char*)p.workspace + L.h_off);

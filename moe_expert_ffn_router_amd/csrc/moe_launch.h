@@ -32,9 +32,27 @@ struct FfnWorkspace {
   size_t xs_off, xs_bytes;  // fp8: scales of x, per token [T] (block FP8: [T, H/128])
   size_t y_off, y_bytes;    // per-slot FC2 output [S, H]: bf16 (bf16), f32 (fp8, f32)
   size_t q_off, q_bytes;    // work counters of the dense kernels, int32 [16]
+  size_t plan_off, plan_bytes;  // token-range plan of the grouped-GEMM tiles (E > 0)
   size_t total;
 };
-FfnWorkspace ffn_workspace_layout(int T, int H, int I, int k, int dtype);
+// E = 0 leaves out the plan region (the small-batch forward has no use for it).
+FfnWorkspace ffn_workspace_layout(int T, int E, int H, int I, int k, int dtype);
+
+// Grouped-GEMM tiles of prefill-sized batches (moe_gemm.hip): a one-workgroup
+// plan kernel cuts every expert's run of the aligned list into token ranges of
+// at most 256 and zeroes the 2 x 8 work counters; FC1 / FC2 then run
+// (range, 256-row tile) units.
+size_t gemm_plan_ints(int S, int E);
+bool gemm_supported(int T, int k, int H, int I);
+hipError_t launch_gemm_plan(const int32_t* sorted_ids, const int32_t* block_expert,
+                            const int32_t* num_padded, int S, int E, int log2m, int* plan,
+                            int* queues, hipStream_t stream);
+hipError_t launch_gemm_fc1(const void* x, const void* w1, const int32_t* sorted_ids,
+                           const int* plan, int* queue, int H, int I, int k, int S, int remap,
+                           void* h, hipStream_t stream);
+hipError_t launch_gemm_fc2(const void* h, const void* w2, const int32_t* sorted_ids,
+                           const int* plan, int* queue, int H, int I, int S, int remap, void* y,
+                           hipStream_t stream);
 
 struct FfnProblem {
   const void* x;

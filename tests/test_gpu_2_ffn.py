@@ -46,14 +46,17 @@ def test_config_parity(n):
     assert err <= TOL[inp.dtype]
 
 
+TILES = {"dense": 0, "range": 1 << 10}  # default 128-row tiles / RANGE_GEMM 256 x 256 tiles
+
+
+@pytest.mark.parametrize("tiles", list(TILES))
 @pytest.mark.parametrize("block_m", [128, 256])
-def test_prefill_workload_block_sizes(block_m):
-    # the prefill workload through the grouped-GEMM tiles at both block sizes
-    # that take them (128-token blocks leave half of each tile's token columns
-    # idle), every output row against the oracle
+def test_prefill_workload_block_sizes(block_m, tiles):
+    # the prefill workload through both prefill tilings at both block sizes
+    # that take them, every output row against the oracle
     inp = cfg_inputs(5)
-    say(f"ffn config 5 block_m={block_m}")
-    ids, w, al, out = gpu_forward(inp, block_m)
+    say(f"ffn config 5 block_m={block_m} tiles={tiles}")
+    ids, w, al, out = gpu_forward(inp, block_m, flags=TILES[tiles])
     check_finite(out)
     ids_o, w_o, ref = oracle_full(5)
     check_routing(ids, w, ids_o, w_o)
@@ -70,14 +73,16 @@ PREFILL_CASES = [  # T, E, H, I, k, routing: several row tiles, ragged blocks,
 ]
 
 
+@pytest.mark.parametrize("tiles", list(TILES))
 @pytest.mark.parametrize("block_m", [128, 256])
 @pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: "T{}_E{}_H{}_I{}_k{}_{}".format(*c))
-def test_prefill_tiles_ragged(case, block_m):
+def test_prefill_tiles_ragged(case, block_m, tiles):
     T, E, H, I, k, routing = case
-    say(f"ffn prefill tiles T={T} E={E} H={H} I={I} k={k} {routing} block_m={block_m}")
+    say(f"ffn prefill tiles T={T} E={E} H={H} I={I} k={k} {routing} block_m={block_m} "
+        f"tiles={tiles}")
     inp = make_inputs(T, E, H, I, k, dtype="bf16", routing=routing, seed=T + block_m,
                       device="cuda")
-    ids, w, al, out = gpu_forward(inp, block_m)
+    ids, w, al, out = gpu_forward(inp, block_m, flags=TILES[tiles])
     check_finite(out)
     ids_o, w_o, ref = oracle_forward(inp)
     check_routing(ids, w, ids_o, w_o)
