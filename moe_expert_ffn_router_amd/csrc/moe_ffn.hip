@@ -52,6 +52,10 @@ constexpr int kHotChunk = 256;  // bytes of K per staged chunk (both dtypes)
 // c ^ (r & 7), so the staging stores and the MFMA fragment reads (rows
 // r0..r0+15 at one column) hit distinct banks.
 constexpr int kLdsRow = kHotChunk;
+// LDS of a hot launch: two staging buffers, the queue's two pick words, then
+// the hot-first block order (hot_first_order: kOrdMax + 8 ints)
+constexpr int kHotLds = 2 * kHotTok * kLdsRow + 16;
+constexpr int kHotLdsTotal = kHotLds + 4 * (2048 + 8);
 __device__ __forceinline__ int hswz(int row, int col16) { return row * kLdsRow + ((col16 ^ (row & 7)) << 4); }
 
 // ------------------------------------------------- work partitioning ---
@@ -104,6 +108,57 @@ struct QuadQueue {
     return u < total ? u : -1;
   }
 };
+
+// Hot-first block order of the dynamic queue. ord[0, nb) receives the blocks
+// holding more than kColdMax tokens first (list order), then the others
+// (reverse list order): hot quads cost more than cold ones (they stage the
+// block's token rows as well), so handing them out first lets the cold quads
+// fill the tail, like a longest-first schedule. A block is hot iff its entry
+// kColdMax is a real slot (real entries form a prefix): one load per block.
+// All threads of the workgroup call it; returns the number of hot blocks, or
+// -1 (ord untouched) when nb exceeds kOrdMax. `wcnt` is 8 ints of LDS.
+constexpr int kOrdMax = 2048;
+static_assert(kHotLdsTotal == kHotLds + 4 * (kOrdMax + 8), "hot LDS layout");
+__device__ int hot_first_order(const int32_t* __restrict__ sorted_ids,
+                               const int32_t* __restrict__ block_expert, int nb, int M, int S,
+                               int E, int* ord, int* wcnt) {
+  if (nb > kOrdMax) return -1;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const uint64_t below = (1ull << lane) - 1;
+  int hot_base = 0, cold_base = 0;
+  for (int b0 = 0; b0 < nb; b0 += 256) {
+    const int b = b0 + t;
+    bool hot = false;
+    if (b < nb && M > kColdMax) {
+      const int e = block_expert[b];
+      hot = (unsigned)e < (unsigned)E &&
+            (unsigned)sorted_ids[(size_t)b * M + kColdMax] < (unsigned)S;
+    }
+    const uint64_t hb = __ballot(hot), cb = __ballot(b < nb && !hot);
+    if (lane == 0) {
+      wcnt[w] = __popcll(hb);
+      wcnt[4 + w] = __popcll(cb);
+    }
+    __syncthreads();
+    int hp = hot_base, cp = cold_base, ht = 0, ct = 0;
+    for (int i = 0; i < 4; ++i) {
+      if (i < w) {
+        hp += wcnt[i];
+        cp += wcnt[4 + i];
+      }
+      ht += wcnt[i];
+      ct += wcnt[4 + i];
+    }
+    if (b < nb) {
+      if (hot) ord[hp + __popcll(hb & below)] = b;
+      else ord[nb - 1 - (cp + __popcll(cb & below))] = b;
+    }
+    hot_base += ht;
+    cold_base += ct;
+    __syncthreads();
+  }
+  return hot_base;
+}
 
 // Number of real (non-sentinel) entries of block b; they form a prefix.
 __device__ __forceinline__ int block_valid(const int32_t* __restrict__ sorted_ids, int b, int M,
@@ -319,13 +374,15 @@ struct HotA {
   }
 };
 
-// One chunk of MFMAs: A from registers, B fragments from the LDS buffer.
-// A B fragment of k-step s takes the 16-byte column s*kKstep/16 + g (and, for
-// fp8, the column 4 further); fragment rows are 16-aligned bases + (lane & 15),
-// so the swizzle term is lane & 7.
-template <bool FP8, int MT>
-__device__ __forceinline__ void hot_compute(const HotA<FP8>& a, const uint8_t* __restrict__ buf,
-                                            f32x4 (&acc)[4]) {
+// One chunk of MFMAs for this wave's NT tiles: A from registers, B fragments
+// from the LDS buffer, each B fragment read once for all NT tiles. A B
+// fragment of k-step s takes the 16-byte column s*kKstep/16 + g (and, for fp8,
+// the column 4 further); fragment rows are 16-aligned bases + (lane & 15), so
+// the swizzle term is lane & 7.
+template <bool FP8, int MT, int NT>
+__device__ __forceinline__ void hot_compute(const HotA<FP8> (&a)[NT],
+                                            const uint8_t* __restrict__ buf,
+                                            f32x4 (&acc)[NT][4]) {
   const int lane = threadIdx.x & 63;
   const uint8_t* base = buf + (lane & 15) * kLdsRow;
   const int x = lane & 7, g = lane >> 4;
@@ -337,7 +394,8 @@ __device__ __forceinline__ void hot_compute(const HotA<FP8>& a, const uint8_t* _
     for (int t = 0; t < MT; ++t) {
       Frag<FP8> b;
       b.lds(base + t * 16 * kLdsRow + c0, c1 - c0);
-      acc[t] = mfma(a.f[s], b, acc[t]);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[n][t] = mfma(a[n].f[s], b, acc[n][t]);
     }
   }
 }
@@ -361,42 +419,53 @@ struct Stage {
   }
 };
 
-// acc[t] += A (16 rows: this lane's a) . B (token tile t from the staged
-// rows) over kbytes of K. `stage` holds this thread's source rows. All 256
-// threads of the workgroup call this together.
-template <bool FP8, int MT>
-__device__ __forceinline__ void hot_kloop(const uint8_t* __restrict__ a, Stage& stage, int kbytes,
-                                          uint8_t* __restrict__ lds, f32x4 (&acc)[4]) {
+// A chunk of this wave's NT weight tiles into registers (the trailing half
+// chunk of fp8 rows zero-padded).
+template <bool FP8, int NT>
+__device__ __forceinline__ void hot_load_a(HotA<FP8> (&f)[NT], const uint8_t* const (&a)[NT],
+                                           int chunk, bool half) {
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    if (half) f[n].load_tail(a[n], chunk);
+    else f[n].load(a[n], chunk);
+  }
+}
+
+// acc[n][t] += A (16 rows of tile n: this lane's a[n]) . B (token tile t from
+// the staged rows) over kbytes of K. `stage` holds this thread's source rows.
+// All 256 threads of the workgroup call this together; the token rows are
+// staged once for the NT tiles of every wave.
+template <bool FP8, int MT, int NT>
+__device__ __forceinline__ void hot_kloop(const uint8_t* const (&a)[NT], Stage& stage,
+                                          int kbytes, uint8_t* __restrict__ lds,
+                                          f32x4 (&acc)[NT][4]) {
   uint8_t* buf0 = lds;
   uint8_t* buf1 = lds + kHotTok * kLdsRow;
   const int nch = (kbytes + kHotChunk - 1) / kHotChunk;
   const bool tail = (kbytes % kHotChunk) != 0;  // fp8 only: last chunk is 128 bytes
-  HotA<FP8> a0, a1;
+  HotA<FP8> a0[NT], a1[NT];
   stage.load(0, kbytes);
-  if (tail && nch == 1) a0.load_tail(a, 0);
-  else a0.load(a, 0);
+  hot_load_a<FP8, NT>(a0, a, 0, tail && nch == 1);
   stage.store(buf0);
   __syncthreads();
   int c = 0;
   for (; c + 1 < nch; c += 2) {
     // chunk c from buf0 / a0 while chunk c+1 loads into buf1 / a1
     stage.load(c + 1, kbytes);
-    if (tail && c + 2 == nch) a1.load_tail(a, c + 1);
-    else a1.load(a, c + 1);
-    hot_compute<FP8, MT>(a0, buf0, acc);
+    hot_load_a<FP8, NT>(a1, a, c + 1, tail && c + 2 == nch);
+    hot_compute<FP8, MT, NT>(a0, buf0, acc);
     stage.store(buf1);
     __syncthreads();
     if (c + 2 < nch) {
       stage.load(c + 2, kbytes);
-      if (tail && c + 3 == nch) a0.load_tail(a, c + 2);
-      else a0.load(a, c + 2);
+      hot_load_a<FP8, NT>(a0, a, c + 2, tail && c + 3 == nch);
     }
-    hot_compute<FP8, MT>(a1, buf1, acc);
+    hot_compute<FP8, MT, NT>(a1, buf1, acc);
     if (c + 2 < nch) stage.store(buf0);
     __syncthreads();
   }
   if (c < nch) {
-    hot_compute<FP8, MT>(a0, buf0, acc);
+    hot_compute<FP8, MT, NT>(a0, buf0, acc);
     __syncthreads();
   }
 }
@@ -563,16 +632,21 @@ __device__ __forceinline__ void fc1_cold_sliced(const Fc1Args& p, int e, int r, 
   }
 }
 
-// Hot FC1 tile r: rows 0..7 of the 16-row tile are gate rows [8r, 8r+8),
-// rows 8..15 the matching up rows; lanes l and l^32 hold g and u of the same
-// (column, token) after the MFMAs.
-template <bool FP8, int MT>
-__device__ __forceinline__ void fc1_hot_pass(const Fc1Args& p, int e, int r, int b, int M, int m,
-                                             int t0, uint8_t* lds) {
+// Hot FC1 tiles r0 .. r0+NT-1 (NT per wave): rows 0..7 of a 16-row tile r are
+// gate rows [8r, 8r+8), rows 8..15 the matching up rows; lanes l and l^32 hold
+// g and u of the same (column, token) after the MFMAs.
+template <bool FP8, int MT, int NT>
+__device__ __forceinline__ void fc1_hot_pass(const Fc1Args& p, int e, int r0, int b, int M,
+                                             int m, int t0, uint8_t* lds) {
   const int lane = threadIdx.x & 63, g = lane >> 4, rho = lane & 15;
   const size_t rowb = (size_t)p.H * (FP8 ? 1 : 2);
-  const int wrow = rho < 8 ? (r * 8 + rho) : (p.I + r * 8 + rho - 8);
-  const uint8_t* a = (const uint8_t*)p.w1 + ((size_t)e * 2 * p.I + wrow) * rowb + 16 * g;
+  const uint8_t* a[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int r = r0 + n;
+    const int wrow = rho < 8 ? (r * 8 + rho) : (p.I + r * 8 + rho - 8);
+    a[n] = (const uint8_t*)p.w1 + ((size_t)e * 2 * p.I + wrow) * rowb + 16 * g;
+  }
   Stage st;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -580,30 +654,46 @@ __device__ __forceinline__ void fc1_hot_pass(const Fc1Args& p, int e, int r, int
     const int slot = ti < m ? p.sorted_ids[(size_t)b * M + ti] : p.S;
     st.src[i] = slot < p.S ? (const uint8_t*)p.x + (size_t)(slot / p.k) * rowb : nullptr;
   }
-  f32x4 acc[4] = {};
-  hot_kloop<FP8, MT>(a, st, (int)rowb, lds, acc);
-  f32x4 sc = {1.f, 1.f, 1.f, 1.f};
-  if (FP8) {
-    const int srow = g < 2 ? (r * 8 + 4 * g) : (p.I + r * 8 + 4 * (g - 2));
-    sc = *(const f32x4*)(p.w1s + (size_t)e * 2 * p.I + srow);
-  }
+  f32x4 acc[NT][4] = {};
+  hot_kloop<FP8, MT, NT>(a, st, (int)rowb, lds, acc);
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int ti = t0 + 16 * t + rho;
-    const int slot = ti < m ? p.sorted_ids[(size_t)b * M + ti] : p.S;
-    const bool ok = slot < p.S;
-    f32x4 v = acc[t];
+  for (int n = 0; n < NT; ++n) {
+    const int r = r0 + n;
+    f32x4 sc = {1.f, 1.f, 1.f, 1.f};
     if (FP8) {
-      const float xs = ok ? p.xs[slot / p.k] : 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] *= sc[i] * xs;
+      const int srow = g < 2 ? (r * 8 + 4 * g) : (p.I + r * 8 + 4 * (g - 2));
+      sc = *(const f32x4*)(p.w1s + (size_t)e * 2 * p.I + srow);
     }
-    f32x4 o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = __shfl_xor(v[i], 32);
-    if (lane < 32 && ok) store_h<FP8>(p, slot, r * 8 + 4 * g, v, o);
+    for (int t = 0; t < MT; ++t) {
+      const int ti = t0 + 16 * t + rho;
+      const int slot = ti < m ? p.sorted_ids[(size_t)b * M + ti] : p.S;
+      const bool ok = slot < p.S;
+      f32x4 v = acc[n][t];
+      if (FP8) {
+        const float xs = ok ? p.xs[slot / p.k] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] *= sc[i] * xs;
+      }
+      f32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = __shfl_xor(v[i], 32);
+      if (lane < 32 && ok) store_h<FP8>(p, slot, r * 8 + 4 * g, v, o);
+    }
   }
 }
+
+// Hot-pass policies of run_quads. kOcts: hot blocks run as octs (two tiles per
+// wave); bf16 only, the fp8 passes would drop to one wave per SIMD.
+template <bool FP8>
+struct Fc1Hot {
+  static constexpr bool kOcts = !FP8;
+  template <int MT, int NT>
+  static __device__ __forceinline__ void pass(const Fc1Args& p, int e, int r0, int b, int M,
+                                              int m, int t0, uint8_t* lds) {
+    fc1_hot_pass<FP8, MT, NT>(p, e, r0, b, M, m, t0, lds);
+  }
+};
 
 // --------------------------------------------------------------- FC2 ---
 
@@ -683,13 +773,17 @@ __device__ __forceinline__ void fc2_cold(const Fc2Args& p, int e, int r, int slo
   }
 }
 
-// Hot FC2 tile r: output rows [16r, 16r+16).
-template <bool FP8, int MT>
-__device__ __forceinline__ void fc2_hot_pass(const Fc2Args& p, int e, int r, int b, int M, int m,
-                                             int t0, uint8_t* lds) {
+// Hot FC2 tiles r0 .. r0+NT-1 (NT per wave): tile r is output rows
+// [16r, 16r+16).
+template <bool FP8, int MT, int NT>
+__device__ __forceinline__ void fc2_hot_pass(const Fc2Args& p, int e, int r0, int b, int M,
+                                             int m, int t0, uint8_t* lds) {
   const int lane = threadIdx.x & 63, g = lane >> 4, rho = lane & 15;
   const size_t rowb = (size_t)p.I * (FP8 ? 1 : 2);
-  const uint8_t* a = (const uint8_t*)p.w2 + ((size_t)e * p.H + r * 16 + rho) * rowb + 16 * g;
+  const uint8_t* a[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+    a[n] = (const uint8_t*)p.w2 + ((size_t)e * p.H + (r0 + n) * 16 + rho) * rowb + 16 * g;
   Stage st;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -697,26 +791,39 @@ __device__ __forceinline__ void fc2_hot_pass(const Fc2Args& p, int e, int r, int
     const int slot = ti < m ? p.sorted_ids[(size_t)b * M + ti] : p.S;
     st.src[i] = slot < p.S ? (const uint8_t*)p.h + (size_t)slot * rowb : nullptr;
   }
-  f32x4 acc[4] = {};
-  hot_kloop<FP8, MT>(a, st, (int)rowb, lds, acc);
-  const int row = r * 16 + 4 * g;
-  f32x4 sc = {1.f, 1.f, 1.f, 1.f};
-  if (FP8) sc = *(const f32x4*)(p.w2s + (size_t)e * p.H + row);
+  f32x4 acc[NT][4] = {};
+  hot_kloop<FP8, MT, NT>(a, st, (int)rowb, lds, acc);
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int ti = t0 + 16 * t + rho;
-    const int slot = ti < m ? p.sorted_ids[(size_t)b * M + ti] : p.S;
-    if (slot < p.S) {
-      f32x4 v = acc[t];
-      if (FP8) {
-        const float hs = p.hs[slot];
+  for (int n = 0; n < NT; ++n) {
+    const int row = (r0 + n) * 16 + 4 * g;
+    f32x4 sc = {1.f, 1.f, 1.f, 1.f};
+    if (FP8) sc = *(const f32x4*)(p.w2s + (size_t)e * p.H + row);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] *= sc[i] * hs;
+    for (int t = 0; t < MT; ++t) {
+      const int ti = t0 + 16 * t + rho;
+      const int slot = ti < m ? p.sorted_ids[(size_t)b * M + ti] : p.S;
+      if (slot < p.S) {
+        f32x4 v = acc[n][t];
+        if (FP8) {
+          const float hs = p.hs[slot];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] *= sc[i] * hs;
+        }
+        store_y(p, slot, row, v);
       }
-      store_y(p, slot, row, v);
     }
   }
 }
+
+template <bool FP8>
+struct Fc2Hot {
+  static constexpr bool kOcts = !FP8;
+  template <int MT, int NT>
+  static __device__ __forceinline__ void pass(const Fc2Args& p, int e, int r0, int b, int M,
+                                              int m, int t0, uint8_t* lds) {
+    fc2_hot_pass<FP8, MT, NT>(p, e, r0, b, M, m, t0, lds);
+  }
+};
 
 // ----------------------------------------- W8A16: e4m3 weights, bf16 x ---
 // Weight-only FP8 ("vLLM SM architecture adaptation", sections 4.2 and 5.2:
@@ -1084,10 +1191,7 @@ __device__ __forceinline__ void fc2_cold_blk(const Fc2Args& p, int e, int r, int
 // fewer registers, so more waves stream weights at once; it stays correct for
 // any block, reading the weights once per 8 tokens.
 template <bool FP8, bool HOT, typename Args, void (*Cold_)(const Args&, int, int, int),
-          void (*H1)(const Args&, int, int, int, int, int, int, uint8_t*),
-          void (*H2)(const Args&, int, int, int, int, int, int, uint8_t*),
-          void (*H3)(const Args&, int, int, int, int, int, int, uint8_t*),
-          void (*H4)(const Args&, int, int, int, int, int, int, uint8_t*)>
+          typename HotOps>
 struct QuadRunner {
   const Args& p;
   int M, w, ti;
@@ -1096,9 +1200,12 @@ struct QuadRunner {
   uint8_t* lds;
   __device__ QuadRunner(const Args& a, uint8_t* l)
       : p(a), M(1 << a.log2m), w(threadIdx.x >> 6), ti(threadIdx.x & 7), lds(l) {}
-  // quad q of block b: wave w takes tile 4q + w
+  // NT = 1: quad q of block b, wave w taking tile 4q + w; NT = 2: oct q,
+  // wave w taking tiles 8q + 2w and 8q + 2w + 1 (a hot block's token rows are
+  // then staged once for twice the weight rows)
+  template <int NT>
   __device__ __forceinline__ void run(int b, int q) {
-    const int r = q * 4 + w;
+    const int r = NT == 1 ? q * 4 + w : q * 8 + 2 * w;
     if (b != cur_b) {
       cur_b = b;
       e = p.block_expert[b];
@@ -1108,17 +1215,19 @@ struct QuadRunner {
     if (HOT && m > kColdMax) {
       for (int t0 = 0; t0 < m; t0 += kHotTok) {
         const int mt = min(4, (m - t0 + 15) >> 4);
-        if (mt == 1) H1(p, e, r, b, M, m, t0, lds);
-        else if (mt == 2) H2(p, e, r, b, M, m, t0, lds);
-        else if (mt == 3) H3(p, e, r, b, M, m, t0, lds);
-        else H4(p, e, r, b, M, m, t0, lds);
+        if (mt == 1) HotOps::template pass<1, NT>(p, e, r, b, M, m, t0, lds);
+        else if (mt == 2) HotOps::template pass<2, NT>(p, e, r, b, M, m, t0, lds);
+        else if (mt == 3) HotOps::template pass<3, NT>(p, e, r, b, M, m, t0, lds);
+        else HotOps::template pass<4, NT>(p, e, r, b, M, m, t0, lds);
       }
     } else {
-      for (int t0 = 0; t0 < m; t0 += kColdMax) {
-        const int slot =
-            t0 == 0 ? cslot : (t0 + ti < m ? p.sorted_ids[(size_t)b * M + t0 + ti] : p.S);
-        Cold_(p, e, r, slot);
-      }
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+        for (int t0 = 0; t0 < m; t0 += kColdMax) {
+          const int slot =
+              t0 == 0 ? cslot : (t0 + ti < m ? p.sorted_ids[(size_t)b * M + t0 + ti] : p.S);
+          Cold_(p, e, r + n, slot);
+        }
     }
   }
 };
@@ -1129,37 +1238,46 @@ struct QuadRunner {
 // passes of 8 tokens: the host picks that launch when blocks of more than 8
 // tokens are unlikely (T <= 16 tokens), where it needs far fewer registers,
 // so more waves stream weights at once; it stays correct for any block,
-// reading the weights once per 8 tokens. With DYN, quads are handed out by a
-// QuadQueue, else each workgroup takes one contiguous equal share of the list.
-// Measured on skewed decode (mixed hot and cold blocks): FC2, whose hot quads
-// cost about twice a cold one, gains ~10% from DYN; FC1 (longer rows, hot
-// quads ~1.3x a cold one) loses ~5% with it, so only FC2 uses it.
+// reading the weights once per 8 tokens. With DYN, units are handed out by a
+// QuadQueue over the hot-first block order (hot_first_order): the octs of the
+// hot blocks, then the quads of the others; else each workgroup takes one
+// contiguous equal share of the quad list.
 template <bool FP8, bool HOT, bool DYN, typename Args, void (*Cold_)(const Args&, int, int, int),
-          void (*H1)(const Args&, int, int, int, int, int, int, uint8_t*),
-          void (*H2)(const Args&, int, int, int, int, int, int, uint8_t*),
-          void (*H3)(const Args&, int, int, int, int, int, int, uint8_t*),
-          void (*H4)(const Args&, int, int, int, int, int, int, uint8_t*)>
+          typename HotOps>
 __device__ __forceinline__ void run_quads(const Args& p, int n_rt, uint8_t* lds) {
   const int M = 1 << p.log2m;
   const int nb = num_blocks(p.num_padded, p.S, p.E, p.log2m);
   const int qpb = n_rt >> 2;  // quads per block (n_rt is a multiple of 4)
-  QuadRunner<FP8, HOT, Args, Cold_, H1, H2, H3, H4> qr(p, lds);
+  QuadRunner<FP8, HOT, Args, Cold_, HotOps> qr(p, lds);
   if constexpr (!DYN) {
     const Share sh = wg_share((long)nb * qpb, p.remap);
-    for (long qd = sh.q0; qd < sh.q1; ++qd) qr.run((int)(qd / qpb), (int)(qd % qpb));
+    for (long qd = sh.q0; qd < sh.q1; ++qd) qr.template run<1>((int)(qd / qpb), (int)(qd % qpb));
   } else {
-    QuadQueue qq(p.queue, nb * qpb, p.remap);
     auto* slots = (volatile __attribute__((address_space(3))) int*)(lds + 2 * kHotTok * kLdsRow);
-    for (int u = qq.first(p.remap); u >= 0; u = qq.next(slots)) qr.run(u / qpb, u % qpb);
+    int* ord = (int*)(lds + kHotLds);
+    const int nh = hot_first_order(p.sorted_ids, p.block_expert, nb, M, p.S, p.E, ord,
+                                   ord + kOrdMax);
+    // hot blocks as octs (two tiles per wave) where the policy takes them
+    constexpr int kHotNT = HotOps::kOcts ? 2 : 1;
+    const bool order = nh >= 0 && (n_rt & (4 * kHotNT - 1)) == 0;
+    const int hpb = n_rt / (4 * kHotNT);        // units per hot block
+    const int hot_units = order ? nh * hpb : 0;  // they come first
+    QuadQueue qq(p.queue, hot_units + (nb - (order ? nh : 0)) * qpb, p.remap);
+    for (int u = qq.first(p.remap); u >= 0; u = qq.next(slots)) {
+      const bool hot = u < hot_units;
+      const int v = hot ? u : u - hot_units, per = hot ? hpb : qpb;
+      const int b = order ? ord[(hot ? 0 : nh) + v / per] : v / per;
+      if (kHotNT == 2 && hot) qr.template run<kHotNT>(b, v % per);
+      else qr.template run<1>(b, v % per);
+    }
   }
 }
 
 template <bool FP8, bool HOT>
 __global__ __launch_bounds__(256) void fc1_kernel(Fc1Args p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[HOT ? 2 * kHotTok * kLdsRow + 16 : 16];
-  run_quads<FP8, HOT, false, Fc1Args, fc1_cold<FP8, cold_u<FP8, HOT>()>, fc1_hot_pass<FP8, 1>,
-            fc1_hot_pass<FP8, 2>,
-            fc1_hot_pass<FP8, 3>, fc1_hot_pass<FP8, 4>>(p, p.I >> 3, lds);
+  __shared__ __attribute__((aligned(16))) uint8_t lds[HOT ? kHotLdsTotal : 16];
+  run_quads<FP8, HOT, HOT, Fc1Args, fc1_cold<FP8, cold_u<FP8, HOT>()>, Fc1Hot<FP8>>(p, p.I >> 3,
+                                                                                   lds);
 }
 
 // Whether an FC1 launch of T tokens (at most 16: the cold-only launches) runs
@@ -1208,18 +1326,16 @@ __global__ __launch_bounds__(256) void fc1_sliced_kernel(Fc1Args p) {
 
 template <bool FP8, bool HOT>
 __global__ __launch_bounds__(256) void fc2_kernel(Fc2Args p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[HOT ? 2 * kHotTok * kLdsRow + 16 : 16];
-  run_quads<FP8, HOT, HOT, Fc2Args, fc2_cold<FP8, cold_u<FP8, HOT>()>, fc2_hot_pass<FP8, 1>,
-            fc2_hot_pass<FP8, 2>,
-            fc2_hot_pass<FP8, 3>, fc2_hot_pass<FP8, 4>>(p, p.H >> 4, lds);
+  __shared__ __attribute__((aligned(16))) uint8_t lds[HOT ? kHotLdsTotal : 16];
+  run_quads<FP8, HOT, HOT, Fc2Args, fc2_cold<FP8, cold_u<FP8, HOT>()>, Fc2Hot<FP8>>(p, p.H >> 4,
+                                                                                   lds);
 }
 
 // W8A16 runs every block by cold passes of 8 tokens (the weights stream once
 // per 8 tokens of a block): a decode path.
 __global__ __launch_bounds__(256) void fc1_w8a16_kernel(Fc1Args p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[16];
-  run_quads<false, false, false, Fc1Args, fc1_cold_w8, fc1_hot_pass<false, 1>,
-            fc1_hot_pass<false, 2>, fc1_hot_pass<false, 3>, fc1_hot_pass<false, 4>>(p, p.I >> 3,
+  run_quads<false, false, false, Fc1Args, fc1_cold_w8, Fc1Hot<false>>(p, p.I >> 3,
                                                                                      lds);
 }
 
@@ -1231,16 +1347,14 @@ __global__ __launch_bounds__(256) void fc1_w8a16_sliced_kernel(Fc1Args p) {
 
 __global__ __launch_bounds__(256) void fc2_w8a16_kernel(Fc2Args p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[16];
-  run_quads<false, false, false, Fc2Args, fc2_cold_w8, fc2_hot_pass<false, 1>,
-            fc2_hot_pass<false, 2>, fc2_hot_pass<false, 3>, fc2_hot_pass<false, 4>>(p, p.H >> 4,
+  run_quads<false, false, false, Fc2Args, fc2_cold_w8, Fc2Hot<false>>(p, p.H >> 4,
                                                                                      lds);
 }
 
 // Block-scaled FP8 runs every block by cold passes of 8 tokens, like W8A16.
 __global__ __launch_bounds__(256) void fc1_blk_kernel(Fc1Args p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[16];
-  run_quads<true, false, false, Fc1Args, fc1_cold_blk, fc1_hot_pass<true, 1>,
-            fc1_hot_pass<true, 2>, fc1_hot_pass<true, 3>, fc1_hot_pass<true, 4>>(p, p.I >> 3,
+  run_quads<true, false, false, Fc1Args, fc1_cold_blk, Fc1Hot<true>>(p, p.I >> 3,
                                                                                   lds);
 }
 
@@ -1252,8 +1366,7 @@ __global__ __launch_bounds__(256, 3) void fc1_blk_sliced_kernel(Fc1Args p) {
 
 __global__ __launch_bounds__(256) void fc2_blk_kernel(Fc2Args p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[16];
-  run_quads<true, false, false, Fc2Args, fc2_cold_blk, fc2_hot_pass<true, 1>,
-            fc2_hot_pass<true, 2>, fc2_hot_pass<true, 3>, fc2_hot_pass<true, 4>>(p, p.H >> 4,
+  run_quads<true, false, false, Fc2Args, fc2_cold_blk, Fc2Hot<true>>(p, p.H >> 4,
                                                                                   lds);
 }
 
