@@ -53,8 +53,8 @@ def parse():
                     help="T <= 16: the whole layer as one cooperative launch (moe_forward_small "
                          "with FORWARD_ONE_KERNEL)")
     ap.add_argument("--small-path", action="store_true",
-                    help="T <= 16: the whole layer through moe_forward_small's separate "
-                         "launches (no alignment step)")
+                    help="T <= 64: the whole layer through one moe_forward_small call "
+                         "(separate launches; no alignment step up to 16 tokens)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--event-stride", type=int, default=10,
                     help="bracket FC1 with timing events on every N-th timed step")
@@ -248,6 +248,8 @@ def main():
         if wo or blk or args.ep > 1 or args.tp > 1 or T > moe.small_max_tokens():
             sys.exit("bench.py: --single-launch/--small-path take an unsharded bf16/fp8 workload of at "
                      f"most {moe.small_max_tokens()} tokens")
+        if args.single_launch and (T > 16 or T * k > 256):
+            sys.exit("bench.py: --single-launch takes at most 16 tokens and 256 slots")
         ws_small = torch.empty(moe.forward_small_workspace_bytes(T, E, H, I, k, dt_code),
                                dtype=torch.uint8, device=dev)
 

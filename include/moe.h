@@ -302,18 +302,23 @@ moe_status moe_ffn_f32(const float* x, const float* w1, const float* w2,
                        float* out, moe_stream_t stream);
 
 /*
- * Forward of a small batch: router softmax + top-k, FC1 + SiLU*up, FC2 and
- * the combine without an alignment step. By default as separate launches
- * (routing; fp8: x quantiser; FC1; fp8: h quantiser; FC2; combine) in which
- * FC1 and FC2 each group the slots by expert in LDS from the routed ids, so
- * no alignment kernel runs. With MOE_FORWARD_ONE_KERNEL the whole layer is
- * one cooperative persistent kernel (plus a 256-thread kernel that clears its
- * barrier words). Passage: "vLLM SM architecture adaptation", section 4.3:
- * for a batch of at most 8 tokens the grouped-GEMM path's launch overhead is
- * what a single-kernel path avoids. Either way the results equal, bit for
- * bit, moe_route_topk -> moe_align_block -> moe_ffn_bf16 / moe_ffn_fp8 at
- * the same T (any block_m): every expert's slots are served by the same
- * 8-token streaming passes.
+ * Forward of a small batch in one call: router softmax + top-k, FC1 +
+ * SiLU*up, FC2 and the combine. Passage: "vLLM SM architecture adaptation",
+ * section 4.3: for a batch of at most 8 tokens the grouped-GEMM path's launch
+ * overhead is what a single-kernel path avoids.
+ * Up to 16 tokens and 256 slots it runs without an alignment step: by default
+ * as separate launches (routing; fp8: x quantiser; FC1; fp8: h quantiser; FC2;
+ * combine) in which FC1 and FC2 each group the slots by expert in LDS from the
+ * routed ids; with MOE_FORWARD_ONE_KERNEL the whole layer is one cooperative
+ * persistent kernel (plus a 256-thread kernel that clears its barrier words).
+ * The results equal, bit for bit, moe_route_topk -> moe_align_block ->
+ * moe_ffn_bf16 / moe_ffn_fp8 at the same T (any block_m): every expert's slots
+ * are served by the same 8-token streaming passes.
+ * From 17 to 64 tokens (or beyond 256 slots) it runs exactly those calls
+ * (moe_route_topk, moe_align_block at moe_default_block_m, then the FFN) in
+ * its own workspace: on MI355X the separate launches beat one cooperative
+ * kernel, and the aligned FFN stages the tokens of a popular expert once
+ * instead of once per 8 of them.
  *
  *  logits        [T, E] fp32; renormalize as in moe_route_topk.
  *  x             [T, H] bf16.
@@ -329,12 +334,14 @@ moe_status moe_ffn_f32(const float* x, const float* w1, const float* w2,
  *                0 after the call has run, nonzero if a device-side barrier
  *                wait gave up (out is then undefined; not expected, the launch
  *                guarantees residency).
- *  flags         0 or MOE_FFN_NO_XCD_REMAP, optionally | MOE_FORWARD_ONE_KERNEL.
- *  Limits: 0 <= T <= moe_small_max_tokens() (16), 1 <= E <= 1024,
- *  1 <= k <= E, T * k <= 256, H and I multiples of 128. Returns
- *  MOE_ERR_SHAPE beyond them, MOE_ERR_UNSUPPORTED for another dtype or flag,
- *  MOE_ERR_HIP if a launch (the cooperative one) is refused. Calls that share a
- *  workspace must not overlap in time.
+ *  flags         0 or MOE_FFN_NO_XCD_REMAP, optionally | MOE_FORWARD_ONE_KERNEL
+ *                (T <= 16 and T * k <= 256 only).
+ *  Limits: 0 <= T <= moe_small_max_tokens() (64), 1 <= E <= 1024,
+ *  1 <= k <= E, T * k <= 512, H and I multiples of 128. Returns
+ *  MOE_ERR_SHAPE beyond them, MOE_ERR_UNSUPPORTED for another dtype or flag
+ *  (or MOE_FORWARD_ONE_KERNEL beyond its batches), MOE_ERR_HIP if a launch
+ *  (the cooperative one) is refused. Calls that share a workspace must not
+ *  overlap in time.
  */
 int moe_small_max_tokens(void);
 size_t moe_forward_small_workspace_bytes(int T, int E, int H, int I, int k, int dtype);

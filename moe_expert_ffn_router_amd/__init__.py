@@ -441,10 +441,11 @@ def _small_outputs(x, T, H, k, out, topk_ids, topk_weights):
 def forward_small(logits, x, w1, w2, k: int, renormalize: bool = False, w1_scale=None,
                   w2_scale=None, flags: int = 0, out=None, topk_ids=None, topk_weights=None,
                   workspace=None, stream=None):
-    """moe_forward_small: the whole layer for T <= small_max_tokens() without an
-    alignment step (separate launches; one cooperative launch with
-    flags | FORWARD_ONE_KERNEL). bf16 weights, or e4m3fn codes with per-row
-    float32 scales (W8A8). Returns
+    """moe_forward_small: the whole layer in one call for T <= small_max_tokens():
+    up to 16 tokens (and 256 slots) without an alignment step (separate
+    launches; one cooperative launch with flags | FORWARD_ONE_KERNEL), beyond
+    that routing, alignment and the FFN launches in its workspace. bf16 weights,
+    or e4m3fn codes with per-row float32 scales (W8A8). Returns
     (out [T,H] bfloat16, topk_ids [T,k] int32, topk_weights [T,k] float32)."""
     fp8 = w1.dtype in _FP8
     T, H, E, I, dtype = _small_args(logits, x, w1, w2, k, fp8, w1_scale, w2_scale)

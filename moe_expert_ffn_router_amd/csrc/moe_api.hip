@@ -25,11 +25,7 @@ moe_status check_common(int T, int E, int k) {
   return MOE_OK;
 }
 
-size_t capacity(long S, int E, int block_m) {
-  const long active = S < E ? S : E;
-  const long cap = S + active * (block_m - 1);
-  return (size_t)((cap + block_m - 1) / block_m * block_m);
-}
+size_t capacity(long S, int E, int block_m) { return moe::align_capacity(S, E, block_m); }
 
 // Validation shared by the three FFN entry points.
 moe_status check_ffn(const void* x, const void* w1, const void* w2, const int32_t* topk_ids,
@@ -159,13 +155,15 @@ static moe_status check_small(int T, int E, int H, int I, int k, int dtype, unsi
     return MOE_ERR_SHAPE;
   if (H < 128 || I < 128 || H % 128 != 0 || I % 128 != 0) return MOE_ERR_SHAPE;
   if (flags & ~(unsigned)(MOE_FFN_NO_XCD_REMAP | MOE_FORWARD_ONE_KERNEL)) return MOE_ERR_UNSUPPORTED;
+  // the single cooperative kernel exists for the small kernels' batches only
+  if ((flags & MOE_FORWARD_ONE_KERNEL) && !moe::small_kernels(T, k)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
 MOE_EXPORT size_t moe_forward_small_workspace_bytes(int T, int E, int H, int I, int k,
                                                     int dtype) {
   if (check_small(T, E, H, I, k, dtype, 0) != MOE_OK) return 0;
-  return moe::small_workspace_bytes(T, H, I, k, dtype);
+  return moe::small_workspace_bytes(T, E, H, I, k, dtype);
 }
 
 MOE_EXPORT moe_status moe_forward_small(const float* logits, const uint16_t* x, const void* w1,
@@ -185,7 +183,7 @@ MOE_EXPORT moe_status moe_forward_small(const float* logits, const uint16_t* x, 
       !aligned(out, 16) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4) ||
       !aligned(workspace, 256) || (fp8 && (!aligned(w1_scale, 16) || !aligned(w2_scale, 16))))
     return MOE_ERR_ALIGN;
-  if (workspace_bytes < moe::small_workspace_bytes(T, H, I, k, dtype)) return MOE_ERR_WORKSPACE;
+  if (workspace_bytes < moe::small_workspace_bytes(T, E, H, I, k, dtype)) return MOE_ERR_WORKSPACE;
   moe::SmallProblem p{logits, x, w1, fp8 ? w1_scale : nullptr, w2, fp8 ? w2_scale : nullptr,
                       T, E, H, I, k, renormalize ? 1 : 0, flags, dtype, topk_ids, topk_weights,
                       workspace, out};
@@ -202,7 +200,7 @@ MOE_EXPORT moe_status moe_forward_small_static(const float* logits, const uint16
   static_assert(moe::kStaticScratchBytes == MOE_STATIC_SCRATCH_BYTES, "scratch size");
   moe_status s = check_small(T, E, H, I, k, dtype, flags);
   if (s != MOE_OK || T == 0) return s;
-  if (moe::small_workspace_bytes(T, H, I, k, dtype) > moe::kStaticScratchBytes)
+  if (moe::small_workspace_bytes(T, E, H, I, k, dtype) > moe::kStaticScratchBytes)
     return MOE_ERR_WORKSPACE;
   const bool fp8 = dtype == MOE_DTYPE_FP8;
   if (!logits || !x || !w1 || !w2 || !topk_ids || !topk_weights || !out) return MOE_ERR_NULL;
@@ -221,7 +219,7 @@ MOE_EXPORT moe_status moe_forward_small_static(const float* logits, const uint16
 
 MOE_EXPORT int moe_default_block_m(int T, int E, int k) {
   if (check_common(T, E, k) != MOE_OK) return 0;
-  return (long)T * k >= 128L * E ? 256 : 64;
+  return moe::default_block_m(T, E, k);
 }
 
 MOE_EXPORT size_t moe_ffn_workspace_bytes(int T, int E, int H, int I, int k, int block_m,

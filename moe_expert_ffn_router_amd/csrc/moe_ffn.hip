@@ -2602,10 +2602,28 @@ hipError_t launch_ffn_fp8_block(const FfnProblem& p, hipStream_t stream) {
   return hipSuccess;
 }
 
-static_assert(kSmallTokens == kSmallMaxT && kSmallExperts == kSmallMaxE &&
-              kSmallSlots == kSmallMaxS, "small-path limits");
+static_assert(kSmallKernelTokens == kSmallMaxT && kSmallExperts == kSmallMaxE &&
+              kSmallKernelSlots == kSmallMaxS, "small-path limits");
 
-size_t small_workspace_bytes(int T, int H, int I, int k, int dtype) {
+// Carve-up of the small-batch forward's workspace beyond the small kernels:
+// the alignment outputs, then the FFN workspace.
+struct SmallAligned {
+  int block_m;
+  size_t cap, be_off, np_off, ffn_off, total;
+};
+static SmallAligned small_aligned_layout(int T, int E, int H, int I, int k, int dtype) {
+  SmallAligned L;
+  L.block_m = default_block_m(T, E, k);
+  L.cap = align_capacity((long)T * k, E, L.block_m);
+  L.be_off = align_up(L.cap * sizeof(int32_t), 256);
+  L.np_off = L.be_off + align_up(L.cap / L.block_m * sizeof(int32_t), 256);
+  L.ffn_off = L.np_off + 256;
+  L.total = L.ffn_off + ffn_workspace_layout(T, E, H, I, k, dtype).total;
+  return L;
+}
+
+size_t small_workspace_bytes(int T, int E, int H, int I, int k, int dtype) {
+  if (!small_kernels(T, k)) return small_aligned_layout(T, E, H, I, k, dtype).total;
   return align_up(ffn_workspace_layout(T, 0, H, I, k, dtype).total, 256) + kBarInts * sizeof(int);
 }
 
@@ -2654,7 +2672,33 @@ static hipError_t launch_small_split(const SmallProblem& p, const SmallArgs& a,
   return hipGetLastError();
 }
 
+// Batches beyond the small kernels: routing, alignment at the default block
+// size and the FFN launchers, in the forward's own workspace (the same kernels
+// and results as the separate calls).
+static hipError_t launch_small_aligned(const SmallProblem& p, hipStream_t stream) {
+  const SmallAligned L = small_aligned_layout(p.T, p.E, p.H, p.I, p.k, p.dtype);
+  char* ws = (char*)p.workspace;
+  int32_t* sorted_ids = (int32_t*)ws;
+  int32_t* block_expert = (int32_t*)(ws + L.be_off);
+  int32_t* num_padded = (int32_t*)(ws + L.np_off);
+  const int S = p.T * p.k;
+  hipError_t err;
+  if ((err = launch_route_topk(p.logits, p.T, p.E, p.k, p.renorm, p.ids, p.wts, stream)) !=
+      hipSuccess)
+    return err;
+  if ((err = launch_align(p.ids, S, p.E, L.block_m, (int)L.cap, sorted_ids, block_expert,
+                          num_padded, stream)) != hipSuccess)
+    return err;
+  const bool fp8 = p.dtype == MOE_DTYPE_FP8;
+  const FfnProblem f{p.x, p.w1, fp8 ? p.w1_scale : nullptr, p.w2, fp8 ? p.w2_scale : nullptr,
+                     p.ids, p.wts, sorted_ids, block_expert, num_padded,
+                     p.T, p.E, p.H, p.I, p.k, L.block_m, p.flags & MOE_FFN_NO_XCD_REMAP,
+                     ws + L.ffn_off, p.out};
+  return fp8 ? launch_ffn_fp8(f, stream) : launch_ffn_bf16(f, stream);
+}
+
 hipError_t launch_forward_small(const SmallProblem& p, hipStream_t stream) {
+  if (!small_kernels(p.T, p.k)) return launch_small_aligned(p, stream);
   const bool fp8 = p.dtype == MOE_DTYPE_FP8;
   const FfnWorkspace L = ffn_workspace_layout(p.T, 0, p.H, p.I, p.k, p.dtype);
   char* ws = (char*)p.workspace;

@@ -76,11 +76,26 @@ hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream);
 hipError_t launch_ffn_w8a16(const FfnProblem& p, hipStream_t stream);
 hipError_t launch_ffn_fp8_block(const FfnProblem& p, hipStream_t stream);
 
-// Single-launch forward of a small batch (T <= kSmallTokens): routing,
-// alignment, FC1, FC2 and combine in one cooperative kernel.
-constexpr int kSmallTokens = 16;
+// Forward of a small batch (T <= kSmallTokens, T k <= kSmallSlots): up to
+// kSmallKernelTokens tokens and kSmallKernelSlots slots the small kernels
+// (no alignment; split launches or one cooperative kernel), beyond them
+// routing, alignment at the default block size and the FFN launchers.
+constexpr int kSmallTokens = 64;
 constexpr int kSmallExperts = 1024;
-constexpr int kSmallSlots = 256;
+constexpr int kSmallSlots = 512;
+constexpr int kSmallKernelTokens = 16;
+constexpr int kSmallKernelSlots = 256;
+inline bool small_kernels(int T, int k) {
+  return T <= kSmallKernelTokens && (long)T * k <= kSmallKernelSlots;
+}
+// The block size of the decode regime for this batch (moe_default_block_m).
+inline int default_block_m(int T, int E, int k) { return (long)T * k >= 128L * E ? 256 : 64; }
+// Entries of sorted_ids the alignment may write: round_up(S + min(E, S)(M - 1), M).
+inline size_t align_capacity(long S, int E, int block_m) {
+  const long active = S < E ? S : E;
+  const long cap = S + active * (block_m - 1);
+  return (size_t)((cap + block_m - 1) / block_m * block_m);
+}
 struct SmallProblem {
   const float* logits;
   const void* x;
@@ -96,9 +111,10 @@ struct SmallProblem {
   void* workspace;
   void* out;
 };
-// ffn_workspace_layout of the dtype, then the barrier words (the last 4
-// bytes: the status word).
-size_t small_workspace_bytes(int T, int H, int I, int k, int dtype);
+// Small kernels: ffn_workspace_layout of the dtype, then the barrier words
+// (the last 4 bytes: the status word). Beyond them: the alignment outputs,
+// then the FFN workspace.
+size_t small_workspace_bytes(int T, int E, int H, int I, int k, int dtype);
 hipError_t launch_forward_small(const SmallProblem& p, hipStream_t stream);
 
 // Device address (current device) of the static scratch array of the

@@ -7,6 +7,8 @@ import subprocess
 
 import pytest
 
+import oracle
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe.h")
 
@@ -165,9 +167,15 @@ def call_small(logits=P, x=P, w1=P, s1=P, w2=P, s2=P, T=16, E=64, H=4096, I=1536
 
 
 def test_small_path_validation():
-    assert lib.moe_small_max_tokens() == 16
-    assert call_small(T=17) == SHAPE
-    assert call_small(T=16, k=17, E=64) == SHAPE          # T * k > 256
+    assert lib.moe_small_max_tokens() == 64
+    assert call_small(T=65) == SHAPE
+    assert call_small(T=64, k=9, E=64) == SHAPE           # T * k > 512
+    # accepted shapes get as far as the workspace check (no GPU here to run them)
+    assert call_small(T=16, k=17, E=64, wsb=100) == WORKSPACE  # 272 slots: aligned launches
+    assert call_small(T=64, k=8, E=128, wsb=100) == WORKSPACE
+    assert call_small(T=17, flags=1 << 9) == UNSUP        # one kernel: 16 tokens at most
+    assert call_small(T=16, k=17, E=64, flags=1 << 9) == UNSUP  # ... and 256 slots
+    assert call_small(T=16, flags=1 << 9, wsb=100) == WORKSPACE
     assert call_small(E=1025, k=2) == SHAPE
     assert call_small(H=200) == SHAPE
     assert call_small(dtype=0) == UNSUP                   # f32
@@ -182,7 +190,12 @@ def test_small_path_validation():
     assert call_small(T=0, logits=None, x=None, out=None, ws=None) == OK
     wsb = lib.moe_forward_small_workspace_bytes
     assert wsb(16, 64, 4096, 1536, 8, 1) > lib.moe_ffn_workspace_bytes(16, 64, 4096, 1536, 8, 64, 1)
-    assert wsb(17, 64, 4096, 1536, 8, 1) == 0 and wsb(16, 64, 4096, 1536, 8, 0) == 0
+    # beyond the small kernels: the alignment outputs plus the FFN workspace
+    for T, E, dt in [(17, 64, 1), (64, 128, 1), (64, 128, 2), (32, 8, 2)]:
+        bm = lib.moe_default_block_m(T, E, 8)
+        assert wsb(T, E, 7168, 2048, 8, dt) >= (lib.moe_ffn_workspace_bytes(T, E, 7168, 2048, 8, bm, dt)
+                                              + 4 * oracle.align_capacity(T * 8, E, bm))
+    assert wsb(65, 64, 4096, 1536, 8, 1) == 0 and wsb(16, 64, 4096, 1536, 8, 0) == 0
 
 
 def call_small_static(logits=P, x=P, w1=P, s1=P, w2=P, s2=P, T=16, E=64, H=4096, I=1536, k=8,
@@ -194,7 +207,8 @@ def call_small_static(logits=P, x=P, w1=P, s1=P, w2=P, s2=P, T=16, E=64, H=4096,
 def test_small_static_validation():
     # every rejection happens on the host, before the scratch's device address
     # is looked up (no GPU here)
-    assert call_small_static(T=17) == SHAPE
+    assert call_small_static(T=65) == SHAPE
+    assert call_small_static(T=17, flags=1 << 9) == UNSUP
     assert call_small_static(H=200) == SHAPE
     assert call_small_static(dtype=0) == UNSUP
     assert call_small_static(flags=1) == UNSUP
@@ -209,6 +223,7 @@ def test_small_static_validation():
     assert wsb(16, 16, 32768, 4096, 16, 2) > m.STATIC_SCRATCH_BYTES
     assert call_small_static(T=16, E=16, H=32768, I=4096, k=16, dtype=2) == WORKSPACE
     assert wsb(16, 64, 4096, 1536, 8, 2) <= m.STATIC_SCRATCH_BYTES  # the decode workloads fit
+    assert wsb(64, 128, 7168, 2048, 8, 2) <= m.STATIC_SCRATCH_BYTES  # (the skewed one too)
 
 
 def test_default_block_m():

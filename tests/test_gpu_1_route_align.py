@@ -113,6 +113,7 @@ def test_align_max_slots():
     (8, 1024, 512, "ties"),                       # 4096 slots: the largest single-launch batch
     (8, 1024, 64, "ties"), (8, 1024, 65, "ties"),  # 512 and 520 slots: both alignment bodies
     (9, 64, 8, "normal"), (16, 64, 8, "normal"),  # larger batches: the two-kernel path
+    (16, 1024, 256, "ties"), (16, 1024, 65, "ties"), (17, 64, 8, "normal"),
     (64, 128, 8, "ties"), (300, 16, 4, "ties")])
 def test_route_align_matches_separate_calls(T, E, k, kind, block_m):
     say(f"route_align T={T} E={E} k={k} {kind} block_m={block_m}")

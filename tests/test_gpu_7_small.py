@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from synth import make_inputs
-from tests.gpu_util import TOL, cfg_inputs, moe, oracle_forward, out_f64, say
+from tests.gpu_util import TOL, cfg_inputs, moe, oracle_forward, oracle_full, out_f64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -127,6 +127,64 @@ def test_modes_agree_on_a_reused_workspace(dtype):
             out, _, _, status = _small(inp, flags=_flags(mode), workspace=ws)
             assert status == 0
             assert torch.equal(out.view(torch.int16), ref[id(inp)].view(torch.int16)), mode
+
+
+# Beyond the small kernels (more than 16 tokens or 256 slots) the forward runs
+# routing, alignment and the FFN launches in its own workspace: the same bits
+# as the separate calls, and the one-kernel mode is refused.
+LARGE_CASES = [  # T, E, H, I, k, routing
+    (17, 64, 256, 256, 8, "zipf"),
+    (32, 16, 384, 256, 8, "zipf"),      # hot blocks (more than 8 tokens per expert)
+    (64, 128, 512, 256, 8, "zipf"),
+    (16, 64, 256, 128, 17, "normal"),   # 272 slots
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("case", LARGE_CASES, ids=lambda c: "T{}_E{}_H{}_I{}_k{}_{}".format(*c))
+def test_small_forward_beyond_small_kernels(case, dtype):
+    T, E, H, I, k, routing = case
+    say(f"small forward (aligned launches) {dtype} T={T} E={E} H={H} I={I} k={k} {routing}")
+    inp = make_inputs(T, E, H, I, k, dtype=dtype, routing=routing, seed=T + E + k,
+                      device="cuda")
+    _check(inp, "split")
+    with pytest.raises(Exception):
+        moe().forward_small(inp.logits, inp.x, inp.w1, inp.w2, k, False, inp.w1_scale,
+                            inp.w2_scale, moe().FORWARD_ONE_KERNEL)
+
+
+def test_small_forward_skewed_decode_workload():
+    # the 64-token skewed decode workload through the one-call forward, every
+    # output row against the oracle and bit-equal to the separate calls
+    inp = cfg_inputs(4)
+    say(f"small forward config 4 T={inp.T} E={inp.E} H={inp.H} I={inp.I} k={inp.k}")
+    out, ids, wts, status = _small(inp)
+    ids_o, w_o, ref = oracle_full(4)
+    assert np.array_equal(ids.cpu().numpy(), ids_o)
+    err = oracle.normwise_rel_err(out_f64(out), ref)
+    say(f"  normwise rel err {err:.3e}")
+    assert err <= TOL[inp.dtype]
+    out_s, ids_s, w_s = _separate(inp)
+    assert torch.equal(out.view(torch.int16), out_s.view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_large_then_small_on_one_workspace(dtype):
+    """An aligned-launch batch, then a small-kernel batch, then again, on one
+    workspace sized for the first."""
+    m = moe()
+    say(f"small forward, large then small batch on one workspace {dtype}")
+    big = make_inputs(48, 32, 256, 256, 8, dtype=dtype, routing="zipf", seed=21, device="cuda")
+    small = make_inputs(5, 32, 256, 256, 8, dtype=dtype, routing="normal", seed=22,
+                        device="cuda")
+    code = m.MOE_DTYPE_FP8 if dtype == "fp8" else m.MOE_DTYPE_BF16
+    n = max(m.forward_small_workspace_bytes(48, 32, 256, 256, 8, code),
+            m.forward_small_workspace_bytes(5, 32, 256, 256, 8, code))
+    ws = torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda")
+    ref = {id(big): _separate(big)[0], id(small): _separate(small)[0]}
+    for inp in (big, small, big, small):
+        out, _, _, _ = _small(inp, workspace=ws)
+        assert torch.equal(out.view(torch.int16), ref[id(inp)].view(torch.int16))
 
 
 def test_empty_batch():

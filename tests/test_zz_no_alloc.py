@@ -73,6 +73,30 @@ def test_static_scratch_matches_workspace_entry_point(dtype, mode):
         assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_static_scratch_beyond_small_kernels(dtype):
+    # batches past the small kernels (routing, alignment and the FFN launches
+    # inside the scratch), a smaller one of them second, then one that takes
+    # the small kernels: each bit-equal to moe_forward_small
+    cases = [(64, 64, 512, 256, 8, 31, "zipf"), (24, 16, 256, 256, 4, 32, "zipf"),
+             (5, 16, 256, 256, 4, 33, "normal")]
+    for T, E, H, I, k, seed, routing in cases:
+        say(f"static-scratch forward {dtype} T={T} E={E} H={H} I={I} k={k} {routing}")
+        inp = make_inputs(T, E, H, I, k, dtype=dtype, routing=routing, seed=seed,
+                          device="cuda")
+        got, ids, wts = _static_call(inp, 0)
+        ref, ids_r, wts_r = _reference(inp, 0)
+        torch.cuda.synchronize()
+        assert torch.equal(ids, ids_r) and torch.equal(wts.view(torch.int32),
+                                                       wts_r.view(torch.int32))
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), \
+            "out differs from moe_forward_small"
+        ids_o, w_o, ref_o = oracle_forward(inp)
+        err = oracle.normwise_rel_err(out_f64(got), ref_o)
+        say(f"  bitwise equal to moe_forward_small; vs oracle {err:.3e}")
+        assert err <= TOL[dtype]
+
+
 def test_static_scratch_size_limit():
     # the layer's intermediates would not fit in the static scratch: refused on
     # the host with MOE_ERR_WORKSPACE, nothing launched, outputs untouched
