@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE FC1+FC2 layer tokens/s; expert-weight HBM GB/s (% of peak) at decode"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2516.6
+MFMA_FP8_PEAK_TFLOPS = 5033.2  # dense (no 2:1 sparsity)
 
 
 def parse():
@@ -49,6 +50,9 @@ def parse():
     ap.add_argument("--block-fp8", action="store_true",
                     help="FP8 workloads: weights quantised per 128x128 block (same master "
                          "weights), activations per 128-element group")
+    ap.add_argument("--fp8", action="store_true",
+                    help="bf16 workloads: the same shapes and master weights quantised to e4m3 "
+                         "(per-row scales), activations per token / per slot (moe_ffn_fp8)")
     ap.add_argument("--single-launch", action="store_true",
                     help="T <= 16: the whole layer as one cooperative launch (moe_forward_small "
                          "with FORWARD_ONE_KERNEL)")
@@ -184,7 +188,10 @@ def main():
         sys.exit("bench.py: --weight-only / --block-fp8 need an FP8 workload (config 3)")
     if args.weight_only and args.block_fp8:
         sys.exit("bench.py: --weight-only and --block-fp8 are separate measurements")
-    inp = config_inputs(args.config, device="cuda", dtype="fp8_block" if args.block_fp8 else None)
+    if args.fp8 and CONFIGS[args.config]["dtype"] != "bf16":
+        sys.exit("bench.py: --fp8 takes a bf16 workload (configs 2, 4, 5)")
+    inp = config_inputs(args.config, device="cuda",
+                        dtype="fp8_block" if args.block_fp8 else ("fp8" if args.fp8 else None))
     T, E, H, I, k = inp.T, inp.E, inp.H, inp.I, inp.k
     Eg = E                                   # experts of the whole layer (routing)
     w1, w2, s1, s2 = inp.w1, inp.w2, inp.w1_scale, inp.w2_scale
@@ -329,7 +336,8 @@ def main():
         + T * H * bx + S_loc * I * (2 if inp.dtype == "bf16" or wo else 4)
     fc1_gbs = fc1_bytes / (fc1_ms * 1e-3) / 1e9
     step_s = ms_per_step * 1e-3
-    wl = cfg["name"] + ("_w8a16" if wo else "") + ("_block128" if blk else "") \
+    wl = (cfg["name"].replace("_bf16_", "_fp8_") if args.fp8 else cfg["name"]) \
+        + ("_w8a16" if wo else "") + ("_block128" if blk else "") \
         + ("_single_launch" if args.single_launch else "") \
         + ("_small_path" if args.small_path else "") + (f"_ep{args.ep}_rank0" if args.ep > 1 else "") \
         + (f"_tp{args.tp}_rank0" if args.tp > 1 else "")
@@ -350,8 +358,9 @@ def main():
     elif M >= 128:  # grouped-GEMM tiles (prefill-sized blocks): FC1 is bound by MFMA
         fc1_flops = S_loc * 2 * I * H * 2
         fc1_tfs = fc1_flops / (fc1_ms * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(fc1_tfs, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(fc1_tfs / MFMA_BF16_PEAK_TFLOPS, 4),
+        peak = MFMA_FP8_PEAK_TFLOPS if inp.dtype == "fp8" else MFMA_BF16_PEAK_TFLOPS
+        roofline = {"bound": "mfma", "achieved": round(fc1_tfs, 1), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(fc1_tfs / peak, 4),
                     "traffic": measured_traffic("fc1", wl), "kernel": "fc1 (FC1 gate|up + SiLU*up)",
                     "kernel_ms": round(fc1_ms, 4), "alg_flops_per_launch": fc1_flops,
                     "alg_bytes_per_launch": fc1_bytes,

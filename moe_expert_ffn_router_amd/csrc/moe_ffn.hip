@@ -1442,9 +1442,13 @@ __device__ __forceinline__ int dstage_bgroups(int m) {
 }
 
 // acc[i][j] += A rows (64*wr + 16i ..) . B tokens (128*wc + 16j ..), j < NJ,
-// for the two MFMA k-steps of one chunk: per k-step the fragments are read,
-// then the MFMAs run on them. Waves whose tokens end early use NJ < 8.
-template <int NJ>
+// over one chunk. bf16: two MFMA k-steps; per k-step the fragments are read,
+// then the MFMAs run on them. fp8 (e4m3 codes, 128 per chunk row): one
+// 16x16x128 MFMA per tile pair; a lane's 32 bytes are the 16-byte columns
+// (lane >> 4) and 4 + (lane >> 4) of its row (the two the bf16 path reads for
+// its two k-steps), the same in A and B, so every product pairs equal k.
+// Waves whose tokens end early use NJ < 8.
+template <int NJ, bool FP8>
 __device__ __forceinline__ void dense_compute(const uint8_t* __restrict__ ta,
                                               const uint8_t* __restrict__ tb, int wr, int wc,
                                               f32x4 (&acc)[4][8]) {
@@ -1452,6 +1456,23 @@ __device__ __forceinline__ void dense_compute(const uint8_t* __restrict__ ta,
   // fragment rows are 16-aligned bases + (lane & 15), so row & 7 == lane & 7
   const uint8_t* pa = ta + (64 * wr + (lane & 15)) * kDChunk;
   const uint8_t* pb = tb + (128 * wc + (lane & 15)) * kDChunk;
+  if constexpr (FP8) {
+    const int c0 = ((lane >> 4) ^ (lane & 7)) << 4, c1 = ((4 + (lane >> 4)) ^ (lane & 7)) << 4;
+    Frag<true> fa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i].lds(pa + i * 16 * kDChunk + c0, c1 - c0);
+    // B fragments one token group ahead (all twelve at once would not fit
+    // beside the accumulators at two waves per SIMD)
+    Frag<true> fb[2];
+    fb[0].lds(pb + c0, c1 - c0);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      if (j + 1 < NJ) fb[(j + 1) & 1].lds(pb + (j + 1) * 16 * kDChunk + c0, c1 - c0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i][j] = mfma_fp8(fa[i].v, fb[j & 1].v, acc[i][j]);
+    }
+    return;
+  }
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int cs = (((s << 2) + (lane >> 4)) ^ (lane & 7)) << 4;
@@ -1496,6 +1517,7 @@ __device__ __forceinline__ void ring_barrier() {
 // and c+2 are in flight. Loads retire in issue order, so waiting for all but
 // the newest weight tile's loads leaves chunk c+1 complete. nj = 16-token
 // groups of this wave holding tokens (0 = idle wave, which only stages).
+template <bool FP8>
 __device__ __forceinline__ void dense_kloop(const DenseStage& st, int kbytes, int nj, int wr,
                                             int wc, uint8_t* __restrict__ lds, f32x4 (&acc)[4][8]) {
   const int nch = kbytes / kDChunk;  // at least 2 (K >= 128)
@@ -1516,11 +1538,11 @@ __device__ __forceinline__ void dense_kloop(const DenseStage& st, int kbytes, in
     const uint8_t* ta = ra + ia * kDTile;
     const uint8_t* tb = rb + (c & 1) * kDTile;
     if (nj > 4)
-      dense_compute<8>(ta, tb, wr, wc, acc);
+      dense_compute<8, FP8>(ta, tb, wr, wc, acc);
     else if (nj > 2)
-      dense_compute<4>(ta, tb, wr, wc, acc);
+      dense_compute<4, FP8>(ta, tb, wr, wc, acc);
     else if (nj > 0)
-      dense_compute<2>(ta, tb, wr, wc, acc);
+      dense_compute<2, FP8>(ta, tb, wr, wc, acc);
     if (c + 2 < nch)
       wait_vm<kDALoads>();
     else
@@ -1636,6 +1658,9 @@ struct UnitMap {
   }
 };
 
+// FC1 of prefill-sized blocks; FP8: e4m3 x codes and weights, scaled per
+// weight row and per token in the epilogue; h is written in bf16 either way.
+template <bool FP8>
 __global__ __launch_bounds__(kDThreads) void dense_fc1_kernel(Fc1Args p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kDLds];
   const int M = 1 << p.log2m;
@@ -1644,7 +1669,7 @@ __global__ __launch_bounds__(kDThreads) void dense_fc1_kernel(Fc1Args p) {
   const int units = nb * n_rt;
   const int w = threadIdx.x >> 6, wr = w & 3, wc = w >> 2, lane = threadIdx.x & 63;
   const int g = lane >> 4;
-  const size_t rowb = (size_t)p.H * 2;
+  const size_t rowb = (size_t)p.H * (FP8 ? 1 : 2);
   UnitMap um{nb, n_rt};
   DenseSched sched(p.queue, units, p.remap);
   for (int u; (u = sched.next(lds)) >= 0;) {
@@ -1669,12 +1694,31 @@ __global__ __launch_bounds__(kDThreads) void dense_fc1_kernel(Fc1Args p) {
       }
       f32x4 acc[4][8] = {};
       const int nj = min(8, max(0, (m - 128 * wc + 15) >> 4));
-      dense_kloop(st, (int)rowb, nj, wr, wc, lds, acc);
+      dense_kloop<FP8>(st, (int)rowb, nj, wr, wc, lds, acc);
       if (nj == 0) continue;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int ti = 128 * wc + 16 * j + (lane & 15);
         const int slot = ti < m ? p.sorted_ids[(size_t)b * M + t0 + ti] : p.S;
+        if constexpr (FP8) {
+          // lanes 0..31 hold gate rows, 32..63 the matching up rows
+          const float xs = slot < p.S ? p.xs[slot / p.k] : 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tt = 4 * wr + i;
+            const int srow =
+                g < 2 ? (r * 128 + tt * 8 + 4 * g) : (p.I + r * 128 + tt * 8 + 4 * (g - 2));
+            const f32x4 sc = *(const f32x4*)(p.w1s + (size_t)e * 2 * p.I + srow);
+            f32x4 v, o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = acc[i][j][q] * (sc[q] * xs);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = __shfl_xor(v[q], 32);
+            // h in bf16 (the per-slot quantiser reads it next)
+            if (lane < 32 && slot < p.S) store_h<false>(p, slot, r * 128 + tt * 8 + 4 * g, v, o);
+          }
+          continue;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           f32x4 o;
@@ -1694,6 +1738,9 @@ __global__ __launch_bounds__(kDThreads) void dense_fc1_kernel(Fc1Args p) {
   }
 }
 
+// FC2 of prefill-sized blocks; FP8: e4m3 h codes and weights, scaled per
+// weight row and per slot in the epilogue, y written as f32.
+template <bool FP8>
 __global__ __launch_bounds__(kDThreads) void dense_fc2_kernel(Fc2Args p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kDLds];
   const int M = 1 << p.log2m;
@@ -1702,7 +1749,7 @@ __global__ __launch_bounds__(kDThreads) void dense_fc2_kernel(Fc2Args p) {
   const int units = nb * n_rt;
   const int w = threadIdx.x >> 6, wr = w & 3, wc = w >> 2, lane = threadIdx.x & 63;
   const int g = lane >> 4;
-  const size_t rowb = (size_t)p.I * 2;
+  const size_t rowb = (size_t)p.I * (FP8 ? 1 : 2);
   UnitMap um{nb, n_rt};
   DenseSched sched(p.queue, units, p.remap);
   for (int u; (u = sched.next(lds)) >= 0;) {
@@ -1726,17 +1773,26 @@ __global__ __launch_bounds__(kDThreads) void dense_fc2_kernel(Fc2Args p) {
       }
       f32x4 acc[4][8] = {};
       const int nj = min(8, max(0, (m - 128 * wc + 15) >> 4));
-      dense_kloop(st, (int)rowb, nj, wr, wc, lds, acc);
+      dense_kloop<FP8>(st, (int)rowb, nj, wr, wc, lds, acc);
       if (nj == 0) continue;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int ti = 128 * wc + 16 * j + (lane & 15);
         const int slot = ti < m ? p.sorted_ids[(size_t)b * M + t0 + ti] : p.S;
         if (slot < p.S) {
+          const float hs = FP8 ? p.hs[slot] : 1.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int row = r * kDRows + 64 * wr + 16 * i + 4 * g;
-            if (row < p.H) store_y(p, slot, row, acc[i][j]);
+            if (row < p.H) {
+              f32x4 v = acc[i][j];
+              if constexpr (FP8) {
+                const f32x4 sc = *(const f32x4*)(p.w2s + (size_t)e * p.H + row);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] *= sc[q] * hs;
+              }
+              store_y(p, slot, row, v);
+            }
           }
         }
       }
@@ -2467,7 +2523,8 @@ hipError_t launch_ffn_bf16(const FfnProblem& p, hipStream_t stream) {
     Fc1Args a{p.x, nullptr, p.w1, nullptr, p.sorted_ids, p.block_expert, p.num_padded,
               p.H, p.I, p.k, S, log2m, remap, h, queue, p.E};
     if (dense)
-      dense_fc1_kernel<<<persistent_grid(dense_fc1_kernel, kDThreads), kDThreads, 0, stream>>>(a);
+      dense_fc1_kernel<false><<<persistent_grid(dense_fc1_kernel<false>, kDThreads), kDThreads, 0,
+                                stream>>>(a);
     else if (hot)
       fc1_kernel<false, true><<<persistent_grid(fc1_kernel<false, true>), 256, 0, stream>>>(a);
     else
@@ -2478,7 +2535,8 @@ hipError_t launch_ffn_bf16(const FfnProblem& p, hipStream_t stream) {
     Fc2Args a{h, nullptr, p.w2, nullptr, p.sorted_ids, p.block_expert, p.num_padded,
               p.H, p.I, S, log2m, remap, y, 1, queue + kQueues, p.E};
     if (dense)
-      dense_fc2_kernel<<<persistent_grid(dense_fc2_kernel, kDThreads), kDThreads, 0, stream>>>(a);
+      dense_fc2_kernel<false><<<persistent_grid(dense_fc2_kernel<false>, kDThreads), kDThreads, 0,
+                                stream>>>(a);
     else if (hot)
       fc2_kernel<false, true><<<persistent_grid(fc2_kernel<false, true>), 256, 0, stream>>>(a);
     else
@@ -2503,8 +2561,11 @@ hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
   float* y = (float*)(ws + L.y_off);
   int* queue = (int*)(ws + L.q_off);    // FC1: [0, 8), FC2: [8, 16)
   const bool hot = p.T > 2 * kColdMax;  // see run_quads
+  // prefill-sized blocks: the grouped-GEMM tiles on fp8 MFMA (two 128-code
+  // chunks of K at least)
+  const bool dense = p.block_m >= 128 && p.H >= 256 && p.I >= 256;
   hipError_t err;
-  if (hot && (st & (MOE_FFN_STAGE_FC1 | MOE_FFN_STAGE_FC2))) {
+  if ((dense || hot) && (st & (MOE_FFN_STAGE_FC1 | MOE_FFN_STAGE_FC2))) {
     zero_counters_kernel<<<1, 64, 0, stream>>>(queue, 2 * kQueues);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
@@ -2513,7 +2574,10 @@ hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
     Fc1Args a{xq, xs, p.w1, p.w1_scale, p.sorted_ids, p.block_expert, p.num_padded,
               p.H, p.I, p.k, S, log2m, remap, h, queue, p.E};
-    if (hot)
+    if (dense)
+      dense_fc1_kernel<true><<<persistent_grid(dense_fc1_kernel<true>, kDThreads), kDThreads, 0,
+                               stream>>>(a);
+    else if (hot)
       fc1_kernel<true, true><<<persistent_grid(fc1_kernel<true, true>), 256, 0, stream>>>(a);
     else if (sliced_fc1(false, p.T))
       fc1_sliced_kernel<true><<<persistent_grid(fc1_sliced_kernel<true>), 256, 0, stream>>>(a);
@@ -2522,17 +2586,26 @@ hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_FC2) {
-    launch_quant_rows<float>(h, S, p.I, hq, hs, stream);
+    if (dense)  // the grouped-GEMM tiles leave h in bf16
+      launch_quant_rows<uint16_t>((const uint16_t*)h, S, p.I, hq, hs, stream);
+    else
+      launch_quant_rows<float>(h, S, p.I, hq, hs, stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
+    // the grouped-GEMM tiles write y in bf16 (as the bf16 path does: at
+    // prefill sizes y is the largest intermediate), the streaming kernels in f32
     Fc2Args a{hq, hs, p.w2, p.w2_scale, p.sorted_ids, p.block_expert, p.num_padded,
-              p.H, p.I, S, log2m, remap, y, 0, queue + kQueues, p.E};
-    if (hot)
+              p.H, p.I, S, log2m, remap, y, dense ? 1 : 0, queue + kQueues, p.E};
+    if (dense)
+      dense_fc2_kernel<true><<<persistent_grid(dense_fc2_kernel<true>, kDThreads), kDThreads, 0,
+                               stream>>>(a);
+    else if (hot)
       fc2_kernel<true, true><<<persistent_grid(fc2_kernel<true, true>), 256, 0, stream>>>(a);
     else
       fc2_kernel<true, false><<<persistent_grid(fc2_kernel<true, false>), 256, 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  if (st & MOE_FFN_STAGE_COMBINE) return launch_combine(p, L, MOE_DTYPE_FP8, stream);
+  if (st & MOE_FFN_STAGE_COMBINE)
+    return launch_combine(p, L, dense ? MOE_DTYPE_BF16 : MOE_DTYPE_FP8, stream);
   return hipSuccess;
 }
 

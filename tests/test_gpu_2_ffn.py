@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import oracle
-from synth import make_inputs
+from synth import config_inputs, make_inputs
 from tests.gpu_util import (TOL, bench_block_m, cfg_inputs, check_align, check_finite,
                             check_routing, gpu_forward, moe, oracle_forward, oracle_full, out_f64,
                             say)
@@ -66,11 +66,56 @@ def test_prefill_workload_block_sizes(block_m, tiles):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("block_m", [128, 256])
+def test_prefill_workload_fp8(block_m):
+    # the prefill workload's shapes with e4m3 weights (per-row scales) and
+    # per-token / per-slot activation scales: the grouped-GEMM tiles on the
+    # fp8 MFMA, every output row against the oracle
+    inp = config_inputs(5, device="cuda", dtype="fp8")
+    say(f"ffn config 5 shapes fp8 block_m={block_m}")
+    ids, w, al, out = gpu_forward(inp, block_m)
+    check_finite(out)
+    ids_o, w_o, ref = _oracle_prefill_fp8()
+    check_routing(ids, w, ids_o, w_o)
+    check_align(al, ids_o, inp.E, block_m, inp.S)
+    err = oracle.normwise_rel_err(out_f64(out), ref)
+    say(f"  normwise rel err {err:.3e} (tol {TOL['fp8']})")
+    assert err <= TOL["fp8"]
+
+
+_PREFILL_FP8 = []
+
+
+def _oracle_prefill_fp8():
+    if not _PREFILL_FP8:  # computed once per process (seconds of fp64 work)
+        _PREFILL_FP8.append(oracle_forward(config_inputs(5, device="cuda", dtype="fp8")))
+    return _PREFILL_FP8[0]
+
+
 PREFILL_CASES = [  # T, E, H, I, k, routing: several row tiles, ragged blocks,
     (700, 8, 1024, 384, 2, "normal"),    # FC1 2I = 768: three 256-row tiles, ragged blocks
     (333, 4, 640, 512, 3, "zipf"),       # FC2 H = 640: two full and one half 256-row tile
     (129, 1, 256, 128, 1, "normal"),     # one expert: a full block and a 1-token block
 ]
+
+
+@pytest.mark.parametrize("block_m", [128, 256])
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: "T{}_E{}_H{}_I{}_k{}_{}".format(*c))
+def test_prefill_tiles_ragged_fp8(case, block_m):
+    # fp8 through the grouped-GEMM tiles (H, I >= 256) or, for the one-expert
+    # case with I = 128, the streaming kernels
+    T, E, H, I, k, routing = case
+    say(f"ffn prefill tiles fp8 T={T} E={E} H={H} I={I} k={k} {routing} block_m={block_m}")
+    inp = make_inputs(T, E, H, I, k, dtype="fp8", routing=routing, seed=T + block_m + 1,
+                      device="cuda")
+    ids, w, al, out = gpu_forward(inp, block_m)
+    check_finite(out)
+    ids_o, w_o, ref = oracle_forward(inp)
+    check_routing(ids, w, ids_o, w_o)
+    check_align(al, ids_o, E, block_m, inp.S)
+    err = oracle.normwise_rel_err(out_f64(out), ref)
+    say(f"  normwise rel err {err:.3e}")
+    assert err <= TOL["fp8"]
 
 
 @pytest.mark.parametrize("tiles", list(TILES))
