@@ -12,6 +12,12 @@ top-8, balanced routing (every expert gets 2 slots), seed 0.
 Prints one JSON line: tokens/s of the whole step, the HBM roofline of the
 dominant kernel (FC1, timed live with HIP events on the same stream), and the
 CPU oracle timed on a bounded sample of the same workload.
+
+Warm-up: the --warmup steps, then more untimed steps until at least
+MIN_WARMUP_S of warm-up have run. MI355X needs that long under load to reach
+its steady clocks: 20 timed decode steps after 5 warm-up steps (2 ms) measured
+0.400 ms per step and FC1 at 0.258 ms, after 100 (38 ms) 0.375 and 0.239 ms,
+the rate of long runs. The line reports both counts.
 """
 import argparse
 import hashlib
@@ -24,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE FC1+FC2 layer tokens/s; expert-weight HBM GB/s (% of peak) at decode"
+MIN_WARMUP_S = 0.05
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2516.6
 MFMA_FP8_PEAK_TFLOPS = 5033.2  # dense (no 2:1 sparsity)
@@ -60,8 +67,9 @@ def parse():
                     help="T <= 64: the whole layer through one moe_forward_small call "
                          "(separate launches; no alignment step up to 16 tokens)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--event-stride", type=int, default=10,
-                    help="bracket FC1 with timing events on every N-th timed step")
+    ap.add_argument("--event-stride", type=int, default=0,
+                    help="bracket FC1 with timing events on every N-th timed step "
+                         "(0: max(1, steps // 10), so every run has ten samples or more)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -227,24 +235,38 @@ def main():
     out = torch.empty((T, H), dtype=torch.float32 if inp.dtype == "f32" else torch.bfloat16,
                       device=dev)
 
-    def ffn(flags):
+    stream = torch.cuda.current_stream()
+
+    # the library calls of a step, checked and marshalled once (moe's prepare=True):
+    # each launch in the timed loop is then one C call, so the host stays ahead of
+    # the GPU even in short runs and no launch gap lands between an event and its
+    # kernel
+    def prepared_ffn(flags):
         f = flags | args.flags
         if blk:
-            moe.ffn_fp8_block(inp.x, w1, s1, w2, s2, ids, wts, sid, be, npad, M, f, ws, out)
-        elif wo:
-            moe.ffn_w8a16(inp.x, w1, s1, w2, s2, ids, wts, sid, be, npad, M, f, ws, out)
-        elif inp.dtype == "fp8":
-            moe.ffn_fp8(inp.x, w1, s1, w2, s2, ids, wts, sid, be, npad, M, f, ws, out)
-        elif inp.dtype == "bf16":
-            moe.ffn_bf16(inp.x, w1, w2, ids, wts, sid, be, npad, M, f, ws, out)
-        else:
-            moe.ffn_f32(inp.x, w1, w2, ids, wts, sid, be, npad, M, f, ws, out)
+            return moe.ffn_fp8_block(inp.x, w1, s1, w2, s2, ids, wts, sid, be, npad, M, f, ws,
+                                     out, stream, prepare=True)
+        if wo:
+            return moe.ffn_w8a16(inp.x, w1, s1, w2, s2, ids, wts, sid, be, npad, M, f, ws, out,
+                                 stream, prepare=True)
+        if inp.dtype == "fp8":
+            return moe.ffn_fp8(inp.x, w1, s1, w2, s2, ids, wts, sid, be, npad, M, f, ws, out,
+                               stream, prepare=True)
+        if inp.dtype == "bf16":
+            return moe.ffn_bf16(inp.x, w1, w2, ids, wts, sid, be, npad, M, f, ws, out, stream,
+                                prepare=True)
+        return moe.ffn_f32(inp.x, w1, w2, ids, wts, sid, be, npad, M, f, ws, out, stream,
+                           prepare=True)
 
-    stream = torch.cuda.current_stream()
+    ffn_calls = {f: prepared_ffn(f) for f in
+                 (moe.STAGE_FC1, moe.STAGE_FC2 | moe.STAGE_COMBINE, 0)}
+
+    def ffn(flags):
+        ffn_calls[flags]()
     # FC1 is bracketed by events on every EVENT_STRIDE-th timed step: a pair of
     # event records costs ~6 us of stream time on MI355X, which on every step
     # would slow the timed steps themselves by ~3 % at decode
-    stride = max(1, args.event_stride)
+    stride = args.event_stride if args.event_stride > 0 else max(1, args.steps // 10)
     n_ev = (args.steps + stride - 1) // stride
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
@@ -259,20 +281,24 @@ def main():
             sys.exit("bench.py: --single-launch takes at most 16 tokens and 256 slots")
         ws_small = torch.empty(moe.forward_small_workspace_bytes(T, E, H, I, k, dt_code),
                                dtype=torch.uint8, device=dev)
+        small_call = moe.forward_small(inp.logits, inp.x, w1, w2, k, False, s1, s2, small_flags,
+                                       out, ids, wts, ws_small, stream, prepare=True)
 
     def step_small(i=None):
         if i is not None:
             ev_a[i].record(stream)
-        moe.forward_small(inp.logits, inp.x, w1, w2, k, False, s1, s2, small_flags, out, ids,
-                          wts, ws_small, stream)
+        small_call()
         if i is not None:
             ev_b[i].record(stream)
+
+    route_call = moe.route_align(inp.logits, k, M, out=(ids, wts, sid, be, npad), stream=stream,
+                                 prepare=True) if E == Eg else None
 
     def step(i=None):
         if small:
             return step_small(i)
         if E == Eg:
-            moe.route_align(inp.logits, k, M, out=(ids, wts, sid, be, npad), stream=stream)
+            route_call()
         else:  # the rank routes over all experts and aligns its local ones
             moe.route_topk(inp.logits, k, out=(ids, wts), stream=stream)
             moe.align_block(ids, E, M, out=(sid, be, npad), stream=stream)
@@ -283,9 +309,17 @@ def main():
             ev_b[i].record(stream)
         ffn(moe.STAGE_FC2 | moe.STAGE_COMBINE)
 
+    tw = time.perf_counter()
+    warm = 0
     for _ in range(args.warmup):
         step()
+        warm += 1
     torch.cuda.synchronize()
+    while time.perf_counter() - tw < MIN_WARMUP_S and warm < 5000:
+        for _ in range(8):
+            step()
+        warm += 8
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i // stride if i % stride == 0 else None)
@@ -370,9 +404,30 @@ def main():
                     "unit": "GB/s", "frac": round(fc1_gbs / HBM_PEAK_GBS, 4),
                     "traffic": measured_traffic("fc1", wl), "kernel": "fc1 (FC1 gate|up + SiLU*up)",
                     "kernel_ms": round(fc1_ms, 4), "alg_bytes_per_launch": fc1_bytes}
+    # the FFN launches alone (FC1 + FC2 + combine, p50 of their own events after the
+    # timed region): at decode the layer's algorithmic bytes (weights, x, output,
+    # routing results; no intermediates) against HBM, at prefill its FLOPs
+    # against the matrix cores
+    ffn_roofline = None
+    if ffn_ev is not None:
+        ffn_ms = float(np.percentile(ffn_ev, 50))
+        if M >= 128:
+            peak = MFMA_FP8_PEAK_TFLOPS if inp.dtype == "fp8" else MFMA_BF16_PEAK_TFLOPS
+            tfs = flops / (ffn_ms * 1e-3) / 1e12
+            ffn_roofline = {"bound": "mfma", "achieved": round(tfs, 1), "peak": peak,
+                            "unit": "TFLOP/s", "frac": round(tfs / peak, 4),
+                            "ffn_ms": round(ffn_ms, 4), "alg_flops": flops}
+        else:
+            ffn_bytes = w_bytes + T * H * bx + T * H * 2 + S * 8
+            gbs = ffn_bytes / (ffn_ms * 1e-3) / 1e9
+            ffn_roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                            "ffn_ms": round(ffn_ms, 4), "alg_bytes": ffn_bytes}
+    roofline["samples"] = n_ev
     rec = {
         "metric": METRIC, "value": round(T / step_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": warm,
+        "ms_per_step": round(ms_per_step, 4),
         "step_ms_p10_p50_p90": [round(float(np.percentile(step_ev, q)), 4) for q in (10, 50, 90)],
         "ffn_only_ms_p10_p50_p90": None if ffn_ev is None else
         [round(float(np.percentile(ffn_ev, q)), 4) for q in (10, 50, 90)],
@@ -387,6 +442,9 @@ def main():
         "tflops": round(flops / step_s / 1e12, 2),
         "mfma_bf16_frac": round(flops / step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": roofline,
+        "ffn_roofline": ffn_roofline,
+        "samples": {"step_intervals": int(len(step_ev)), "fc1_events": n_ev,
+                    "ffn_only": 0 if ffn_ev is None else int(len(ffn_ev))},
         "source_digest": source_digest(),
     }
     if not args.no_cpu_baseline and args.ep == 1 and args.tp == 1:

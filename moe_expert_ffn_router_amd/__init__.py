@@ -218,7 +218,7 @@ align = align_block  # the alignment step under its short name
 
 
 def route_align(logits: torch.Tensor, k: int, block_m: int, renormalize: bool = False,
-                out=None, stream=None):
+                out=None, stream=None, prepare: bool = False):
     """Routing and alignment in one call (moe_route_align). logits [T, E] float32.
     Returns (topk_ids, topk_weights, sorted_ids, block_expert, num_padded), or
     fills `out`, a tuple of those five tensors."""
@@ -231,10 +231,35 @@ def route_align(logits: torch.Tensor, k: int, block_m: int, renormalize: bool = 
     else:
         ids, wts = _routing_outputs(out[:2], T, k, dev)
         sorted_ids, block_expert, num_padded = _align_outputs(out[2:], T, k, E, block_m, dev)
-    _check(lib.moe_route_align(_ptr(logits), T, E, k, int(bool(renormalize)), block_m, _ptr(ids),
-                               _ptr(wts), _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded),
-                               _stream(stream)))
-    return ids, wts, sorted_ids, block_expert, num_padded
+    keep = (logits, ids, wts, sorted_ids, block_expert, num_padded)
+    args = (_ptr(logits), T, E, k, int(bool(renormalize)), block_m, _ptr(ids), _ptr(wts),
+            _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded), _stream(stream))
+    return _run(lib.moe_route_align, args, keep, prepare,
+                (ids, wts, sorted_ids, block_expert, num_padded))
+
+
+# ------------------------------------------------------- prepared calls ---
+
+class Prepared:
+    """A library call whose arguments were checked and marshalled once (pass
+    ``prepare=True`` to route_align, the ffn_* calls or forward_small): calling
+    it makes only the C call, which validates its arguments again on the host,
+    and checks the status. For loops that launch the same call many times; it
+    keeps its tensors alive, and they must not be resized or reallocated."""
+    __slots__ = ("_fn", "_args", "_keep")
+
+    def __init__(self, fn, args, keep):
+        self._fn, self._args, self._keep = fn, args, keep
+
+    def __call__(self):
+        _check(self._fn(*self._args))
+
+
+def _run(fn, args, keep, prepare, result):
+    if prepare:
+        return Prepared(fn, args, keep)
+    _check(fn(*args))
+    return result
 
 
 # ----------------------------------------------------------------- FFN ---
@@ -287,17 +312,19 @@ def _ffn_buffers(x, T, E, H, I, k, block_m, dtype, out_dtype, workspace, out):
 
 
 def ffn_bf16(x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert, num_padded,
-             block_m: int, flags: int = 0, workspace=None, out=None, stream=None):
+             block_m: int, flags: int = 0, workspace=None, out=None, stream=None,
+             prepare: bool = False):
     """moe_ffn_bf16: x [T,H], w1 [E,2I,H], w2 [E,H,I] bfloat16 -> out [T,H] bfloat16."""
     T, E, H, I, k = _ffn_args(x, w1, w2, (torch.bfloat16,), (torch.bfloat16,), topk_ids,
                               topk_weights, sorted_ids, block_expert, num_padded, block_m)
     workspace, out = _ffn_buffers(x, T, E, H, I, k, block_m, MOE_DTYPE_BF16, torch.bfloat16,
                                   workspace, out)
-    _check(lib.moe_ffn_bf16(_ptr(x), _ptr(w1), _ptr(w2), _ptr(topk_ids), _ptr(topk_weights),
-                            _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded), T, E, H,
-                            I, k, block_m, flags, _ptr(workspace), workspace.numel(),
-                            _ptr(out), _stream(stream)))
-    return out
+    keep = (x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert, num_padded, workspace,
+            out)
+    args = (_ptr(x), _ptr(w1), _ptr(w2), _ptr(topk_ids), _ptr(topk_weights), _ptr(sorted_ids),
+            _ptr(block_expert), _ptr(num_padded), T, E, H, I, k, block_m, flags,
+            _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream))
+    return _run(lib.moe_ffn_bf16, args, keep, prepare, out)
 
 
 def _scale_shapes(dtype, E, H, I):
@@ -307,7 +334,8 @@ def _scale_shapes(dtype, E, H, I):
 
 
 def _ffn_scaled(fn, dtype, x, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids,
-                block_m, flags, workspace, out, stream, block_expert, num_padded):
+                block_m, flags, workspace, out, stream, block_expert, num_padded,
+                prepare=False):
     T, E, H, I, k = _ffn_args(x, w1, w2, _FP8, (torch.bfloat16,), topk_ids, topk_weights,
                               sorted_ids, block_expert, num_padded, block_m)
     s1, s2 = _scale_shapes(dtype, E, H, I)
@@ -315,54 +343,60 @@ def _ffn_scaled(fn, dtype, x, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights
     _need(w2_scale, "w2_scale", (torch.float32,), x.device, s2)
     workspace, out = _ffn_buffers(x, T, E, H, I, k, block_m, dtype, torch.bfloat16,
                                   workspace, out)
-    _check(fn(_ptr(x), _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale), _ptr(topk_ids),
-              _ptr(topk_weights), _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded), T, E,
-              H, I, k, block_m, flags, _ptr(workspace), workspace.numel(), _ptr(out),
-              _stream(stream)))
-    return out
+    keep = (x, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids, block_expert,
+            num_padded, workspace, out)
+    args = (_ptr(x), _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale), _ptr(topk_ids),
+            _ptr(topk_weights), _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded), T, E,
+            H, I, k, block_m, flags, _ptr(workspace), workspace.numel(), _ptr(out),
+            _stream(stream))
+    return _run(fn, args, keep, prepare, out)
 
 
 def ffn_fp8(x, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids, block_expert,
-            num_padded, block_m: int, flags: int = 0, workspace=None, out=None, stream=None):
+            num_padded, block_m: int, flags: int = 0, workspace=None, out=None, stream=None,
+            prepare: bool = False):
     """moe_ffn_fp8: x [T,H] bfloat16; w1 [E,2I,H], w2 [E,H,I] e4m3fn codes (uint8 or
     float8_e4m3fn) with float32 per-output-row scales -> out [T,H] bfloat16."""
     return _ffn_scaled(lib.moe_ffn_fp8, MOE_DTYPE_FP8, x, w1, w1_scale, w2, w2_scale, topk_ids,
                        topk_weights, sorted_ids, block_m, flags, workspace, out, stream,
-                       block_expert, num_padded)
+                       block_expert, num_padded, prepare)
 
 
 def ffn_w8a16(x, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids, block_expert,
-              num_padded, block_m: int, flags: int = 0, workspace=None, out=None, stream=None):
+              num_padded, block_m: int, flags: int = 0, workspace=None, out=None, stream=None,
+              prepare: bool = False):
     """moe_ffn_w8a16: weight-only fp8. Arguments as ffn_fp8; activations stay
     bfloat16 -> out [T,H] bfloat16."""
     return _ffn_scaled(lib.moe_ffn_w8a16, MOE_DTYPE_W8A16, x, w1, w1_scale, w2, w2_scale,
                        topk_ids, topk_weights, sorted_ids, block_m, flags, workspace, out,
-                       stream, block_expert, num_padded)
+                       stream, block_expert, num_padded, prepare)
 
 
 def ffn_fp8_block(x, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids,
                   block_expert, num_padded, block_m: int, flags: int = 0, workspace=None,
-                  out=None, stream=None):
+                  out=None, stream=None, prepare: bool = False):
     """moe_ffn_fp8_block: x [T,H] bfloat16; w1 [E,2I,H], w2 [E,H,I] e4m3fn codes with
     float32 scales per 128x128 block (w1_scale [E,2I/128,H/128], w2_scale [E,H/128,I/128])
     -> out [T,H] bfloat16."""
     return _ffn_scaled(lib.moe_ffn_fp8_block, MOE_DTYPE_FP8_BLOCK, x, w1, w1_scale, w2,
                        w2_scale, topk_ids, topk_weights, sorted_ids, block_m, flags, workspace,
-                       out, stream, block_expert, num_padded)
+                       out, stream, block_expert, num_padded, prepare)
 
 
 def ffn_f32(x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert, num_padded,
-            block_m: int, flags: int = 0, workspace=None, out=None, stream=None):
+            block_m: int, flags: int = 0, workspace=None, out=None, stream=None,
+            prepare: bool = False):
     """moe_ffn_f32: float32 throughout."""
     T, E, H, I, k = _ffn_args(x, w1, w2, (torch.float32,), (torch.float32,), topk_ids,
                               topk_weights, sorted_ids, block_expert, num_padded, block_m)
     workspace, out = _ffn_buffers(x, T, E, H, I, k, block_m, MOE_DTYPE_F32, torch.float32,
                                   workspace, out)
-    _check(lib.moe_ffn_f32(_ptr(x), _ptr(w1), _ptr(w2), _ptr(topk_ids), _ptr(topk_weights),
-                           _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded), T, E, H,
-                           I, k, block_m, flags, _ptr(workspace), workspace.numel(),
-                           _ptr(out), _stream(stream)))
-    return out
+    keep = (x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert, num_padded, workspace,
+            out)
+    args = (_ptr(x), _ptr(w1), _ptr(w2), _ptr(topk_ids), _ptr(topk_weights), _ptr(sorted_ids),
+            _ptr(block_expert), _ptr(num_padded), T, E, H, I, k, block_m, flags,
+            _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream))
+    return _run(lib.moe_ffn_f32, args, keep, prepare, out)
 
 
 def forward(x, logits, w1, w2, k: int, block_m: Optional[int] = None, renormalize: bool = False,
@@ -440,7 +474,7 @@ def _small_outputs(x, T, H, k, out, topk_ids, topk_weights):
 
 def forward_small(logits, x, w1, w2, k: int, renormalize: bool = False, w1_scale=None,
                   w2_scale=None, flags: int = 0, out=None, topk_ids=None, topk_weights=None,
-                  workspace=None, stream=None):
+                  workspace=None, stream=None, prepare: bool = False):
     """moe_forward_small: the whole layer in one call for T <= small_max_tokens():
     up to 16 tokens (and 256 slots) without an alignment step (separate
     launches; one cooperative launch with flags | FORWARD_ONE_KERNEL), beyond
@@ -455,12 +489,12 @@ def forward_small(logits, x, w1, w2, k: int, renormalize: bool = False, w1_scale
         workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=x.device)
     else:
         _need(workspace, "workspace", (torch.uint8,), x.device, min_numel=n)
-    _check(lib.moe_forward_small(_ptr(logits), _ptr(x), _ptr(w1), _ptr(w1_scale) if fp8 else None,
-                                 _ptr(w2), _ptr(w2_scale) if fp8 else None, T, E, H, I, k,
-                                 1 if renormalize else 0, dtype, flags, _ptr(topk_ids),
-                                 _ptr(topk_weights), _ptr(workspace), workspace.numel(),
-                                 _ptr(out), _stream(stream)))
-    return out, topk_ids, topk_weights
+    keep = (logits, x, w1, w2, w1_scale, w2_scale, topk_ids, topk_weights, workspace, out)
+    args = (_ptr(logits), _ptr(x), _ptr(w1), _ptr(w1_scale) if fp8 else None, _ptr(w2),
+            _ptr(w2_scale) if fp8 else None, T, E, H, I, k, 1 if renormalize else 0, dtype,
+            flags, _ptr(topk_ids), _ptr(topk_weights), _ptr(workspace), workspace.numel(),
+            _ptr(out), _stream(stream))
+    return _run(lib.moe_forward_small, args, keep, prepare, (out, topk_ids, topk_weights))
 
 
 def forward_small_static(logits, x, w1, w2, k: int, renormalize: bool = False, w1_scale=None,

@@ -42,6 +42,12 @@ def test_bench_json_line():
     for key in ("value", "unit", "cores", "kind", "sample"):
         assert key in cb, key
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
+    # the FFN launches alone, and how many samples each figure rests on (a short
+    # run still brackets FC1 on every step)
+    ffn = d["ffn_roofline"]
+    assert ffn["bound"] == "hbm" and 0 < ffn["frac"] < 1 and ffn["ffn_ms"] > 0
+    assert d["samples"]["fc1_events"] == 5 and d["samples"]["step_intervals"] == 4
+    assert d["samples"]["ffn_only"] == 5 and roof["samples"] == 5
 
 
 @pytest.mark.gpu
@@ -50,6 +56,7 @@ def test_bench_json_line():
     (["--config", "3", "--block-fp8"], "_block128"),
     (["--config", "2", "--small-path"], "_small_path"),
     (["--config", "3", "--single-launch"], "_single_launch"),
+    (["--config", "5", "--fp8"], "prefill_fp8_"),
 ])
 def test_bench_modes(args, suffix):
     """Every measurement mode of the benchmark prints one line naming its workload."""
@@ -60,5 +67,6 @@ def test_bench_modes(args, suffix):
     lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
     assert len(lines) == 1
     d = json.loads(lines[0])
-    assert d["config"]["workload"].endswith(suffix)
+    wl = d["config"]["workload"]
+    assert wl.endswith(suffix) or wl.startswith(suffix), wl
     assert d["value"] > 0 and d["roofline"]["achieved"] > 0 and d["cpu_baseline"] is None

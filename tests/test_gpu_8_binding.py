@@ -87,3 +87,37 @@ def test_scaled_and_small_argument_checks(setup):
     _expect(ValueError, lambda: m.align_block(ids, inp.E, 16, out=(sid[:8], be, npad)))
     call()
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_prepared_calls_match_direct_calls(setup, dtype):
+    # prepare=True checks and marshals once; the prepared calls, run several
+    # times, give the bits of the direct calls
+    m, _, _ = setup
+    say(f"binding: prepared calls {dtype}")
+    inp = make_inputs(24, 16, 256, 256, 4, dtype=dtype, routing="zipf", seed=8, device="cuda")
+    bm = 64
+    ref = m.forward(inp.x, inp.logits, inp.w1, inp.w2, inp.k, bm, w1_scale=inp.w1_scale,
+                    w2_scale=inp.w2_scale)
+    ids, w, sid, be, npad = m.route_align(inp.logits, inp.k, bm)
+    route = m.route_align(inp.logits, inp.k, bm, out=(ids, w, sid, be, npad), prepare=True)
+    code = m.MOE_DTYPE_FP8 if dtype == "fp8" else m.MOE_DTYPE_BF16
+    ws = m.alloc_workspace(inp.T, inp.E, inp.H, inp.I, inp.k, bm, code, "cuda")
+    out = torch.empty_like(ref)
+    if dtype == "fp8":
+        ffn = m.ffn_fp8(inp.x, inp.w1, inp.w1_scale, inp.w2, inp.w2_scale, ids, w, sid, be,
+                        npad, bm, 0, ws, out, prepare=True)
+    else:
+        ffn = m.ffn_bf16(inp.x, inp.w1, inp.w2, ids, w, sid, be, npad, bm, 0, ws, out,
+                         prepare=True)
+    small = m.forward_small(inp.logits, inp.x, inp.w1, inp.w2, inp.k, False, inp.w1_scale,
+                            inp.w2_scale, prepare=True)
+    assert isinstance(route, m.Prepared) and isinstance(ffn, m.Prepared)
+    for _ in range(3):
+        out.zero_()
+        route()
+        ffn()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    small()
+    torch.cuda.synchronize()
