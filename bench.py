@@ -389,40 +389,58 @@ def main():
                     "traffic": None,
                     "kernel": "moe_forward_small (whole layer: route, FC1, FC2, combine)",
                     "kernel_ms": round(fc1_ms, 4), "alg_bytes_per_launch": layer_bytes}
-    elif M >= 128:  # grouped-GEMM tiles (prefill-sized blocks): FC1 is bound by MFMA
+    elif M >= 128:  # grouped-GEMM tiles (prefill-sized blocks)
+        # the roofline bound is whichever of the two times is longer: the FLOPs at the
+        # matrix-core peak or the algorithmic bytes at the HBM peak (at ~256 tokens per
+        # expert the weights make it the bytes: 256 FLOP per weight byte in bf16
+        # against the chip's 2516.6 TFLOP/s / 8 TB/s = 315); both fractions are given
         fc1_flops = S_loc * 2 * I * H * 2
         fc1_tfs = fc1_flops / (fc1_ms * 1e-3) / 1e12
         peak = MFMA_FP8_PEAK_TFLOPS if inp.dtype == "fp8" else MFMA_BF16_PEAK_TFLOPS
-        roofline = {"bound": "mfma", "achieved": round(fc1_tfs, 1), "peak": peak,
-                    "unit": "TFLOP/s", "frac": round(fc1_tfs / peak, 4),
-                    "traffic": measured_traffic("fc1", wl), "kernel": "fc1 (FC1 gate|up + SiLU*up)",
-                    "kernel_ms": round(fc1_ms, 4), "alg_flops_per_launch": fc1_flops,
-                    "alg_bytes_per_launch": fc1_bytes,
-                    "hbm_gbs": round(fc1_gbs, 1)}
+        mfma = {"achieved": round(fc1_tfs, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(fc1_tfs / peak, 4)}
+        hbm = {"achieved": round(fc1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+               "frac": round(fc1_gbs / HBM_PEAK_GBS, 4)}
+        t_mfma_ms = fc1_flops / (peak * 1e12) * 1e3
+        t_hbm_ms = fc1_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
+        if t_hbm_ms >= t_mfma_ms:
+            roofline = {"bound": "hbm", **hbm, "mfma": mfma}
+        else:
+            roofline = {"bound": "mfma", **mfma, "hbm": hbm}
+        roofline.update({"traffic": measured_traffic("fc1", wl),
+                         "kernel": "fc1 (FC1 gate|up + SiLU*up)", "kernel_ms": round(fc1_ms, 4),
+                         "alg_flops_per_launch": fc1_flops, "alg_bytes_per_launch": fc1_bytes,
+                         "bound_ms": {"mfma": round(t_mfma_ms, 4), "hbm": round(t_hbm_ms, 4)}})
     else:
         roofline = {"bound": "hbm", "achieved": round(fc1_gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(fc1_gbs / HBM_PEAK_GBS, 4),
                     "traffic": measured_traffic("fc1", wl), "kernel": "fc1 (FC1 gate|up + SiLU*up)",
                     "kernel_ms": round(fc1_ms, 4), "alg_bytes_per_launch": fc1_bytes}
     # the FFN launches alone (FC1 + FC2 + combine, p50 of their own events after the
-    # timed region): at decode the layer's algorithmic bytes (weights, x, output,
-    # routing results; no intermediates) against HBM, at prefill its FLOPs
-    # against the matrix cores
+    # timed region): the layer's algorithmic bytes (weights, x, output, routing
+    # results; no intermediates) against HBM; at prefill also its FLOPs against the
+    # matrix cores, the longer of the two times naming the bound
     ffn_roofline = None
     if ffn_ev is not None:
         ffn_ms = float(np.percentile(ffn_ev, 50))
-        if M >= 128:
+        ffn_bytes = w_bytes + T * H * bx + T * H * 2 + S * 8
+        gbs = ffn_bytes / (ffn_ms * 1e-3) / 1e9
+        hbm = {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+               "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        if M >= 128:  # as for FC1: the longer of the MFMA and the HBM time bounds it
             peak = MFMA_FP8_PEAK_TFLOPS if inp.dtype == "fp8" else MFMA_BF16_PEAK_TFLOPS
             tfs = flops / (ffn_ms * 1e-3) / 1e12
-            ffn_roofline = {"bound": "mfma", "achieved": round(tfs, 1), "peak": peak,
-                            "unit": "TFLOP/s", "frac": round(tfs / peak, 4),
-                            "ffn_ms": round(ffn_ms, 4), "alg_flops": flops}
+            mfma = {"achieved": round(tfs, 1), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(tfs / peak, 4)}
+            if ffn_bytes / (HBM_PEAK_GBS * 1e9) >= flops / (peak * 1e12):
+                ffn_roofline = {"bound": "hbm", **hbm, "mfma": mfma}
+            else:
+                ffn_roofline = {"bound": "mfma", **mfma, "hbm": hbm}
+            ffn_roofline.update({"ffn_ms": round(ffn_ms, 4), "alg_flops": flops,
+                                 "alg_bytes": ffn_bytes})
         else:
-            ffn_bytes = w_bytes + T * H * bx + T * H * 2 + S * 8
-            gbs = ffn_bytes / (ffn_ms * 1e-3) / 1e9
-            ffn_roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                            "ffn_ms": round(ffn_ms, 4), "alg_bytes": ffn_bytes}
+            ffn_roofline = {"bound": "hbm", **hbm, "ffn_ms": round(ffn_ms, 4),
+                            "alg_bytes": ffn_bytes}
     roofline["samples"] = n_ev
     rec = {
         "metric": METRIC, "value": round(T / step_s, 1), "unit": "tokens/s", "n_gpus": 1,

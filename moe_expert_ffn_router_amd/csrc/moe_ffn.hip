@@ -53,9 +53,9 @@ constexpr int kHotChunk = 256;  // bytes of K per staged chunk (both dtypes)
 // r0..r0+15 at one column) hit distinct banks.
 constexpr int kLdsRow = kHotChunk;
 // LDS of a hot launch: two staging buffers, the queue's two pick words, then
-// the hot-first block order (hot_first_order: kOrdMax + 8 ints)
+// the hot-first block order (hot_first_order: kOrdMax + kOrdCnt ints)
 constexpr int kHotLds = 2 * kHotTok * kLdsRow + 16;
-constexpr int kHotLdsTotal = kHotLds + 4 * (2048 + 8);
+constexpr int kHotLdsTotal = kHotLds + 4 * (2048 + 12);
 __device__ __forceinline__ int hswz(int row, int col16) { return row * kLdsRow + ((col16 ^ (row & 7)) << 4); }
 
 // ------------------------------------------------- work partitioning ---
@@ -80,84 +80,105 @@ __device__ __forceinline__ Share wg_share(long total, int remap) {
 // quads differ in cost, so equal static shares would leave workgroups idle
 // while others still hold slow quads). Workgroup g starts with unit v(g), its
 // XCD-remapped index; every later unit comes from one global counter (zero at
-// launch). The next pick is requested as soon as a unit starts, so the
-// atomic's latency hides under the unit's streaming; it is published to the
-// workgroup through one of two LDS words, alternating, with one barrier.
+// launch), published to the workgroup through one of two LDS words,
+// alternating, with one barrier. A short unit requests its successor as it
+// starts, so the atomic's latency hides under its streaming; a long one
+// (early()) requests it only when it ends: taken at its start, the successor
+// would be tied to this workgroup for the whole long unit while others run
+// dry (kernel timestamps at 64 tokens, top-8 of 128 experts: every
+// workgroup holding a hot unit of ~170 us had taken a second unit at time
+// zero, and the last workgroups ended 100 us after the first).
 // Which workgroup computes a unit never changes the result.
 struct QuadQueue {
   int* cnt;
-  int total, nxt = 0, par = 0;
+  int total, nxt = -1, par = 0;  // nxt: thread 0's requested unit, -1 none yet
   __device__ QuadQueue(int* c, int n, int remap) : cnt(c), total(n) {}
   __device__ __forceinline__ int first(int remap) {
     int wg = blockIdx.x;
     const int G = gridDim.x;
     if (remap && (G & 7) == 0) wg = (wg & 7) * (G >> 3) + (wg >> 3);
-    prefetch(wg);
     return wg < total ? wg : -1;
   }
-  __device__ __forceinline__ void prefetch(int cur) {
-    if (threadIdx.x == 0 && cur < total) nxt = (int)gridDim.x + atomicAdd(cnt, 1);
+  // Request the successor of a unit now (all threads call it; thread 0 acts).
+  __device__ __forceinline__ void early() {
+    if (threadIdx.x == 0) nxt = (int)gridDim.x + atomicAdd(cnt, 1);
   }
   // All threads call it after finishing a unit.
   __device__ __forceinline__ int next(volatile __attribute__((address_space(3))) int* slots) {
-    if (threadIdx.x == 0) slots[par] = nxt;
+    if (threadIdx.x == 0) {
+      slots[par] = nxt >= 0 ? nxt : (int)gridDim.x + atomicAdd(cnt, 1);
+      nxt = -1;
+    }
     __syncthreads();
     const int u = slots[par];
     par ^= 1;
-    prefetch(u);
     return u < total ? u : -1;
   }
 };
 
 // Hot-first block order of the dynamic queue. ord[0, nb) receives the blocks
-// holding more than kColdMax tokens first (list order), then the others
-// (reverse list order): hot quads cost more than cold ones (they stage the
-// block's token rows as well), so handing them out first lets the cold quads
-// fill the tail, like a longest-first schedule. A block is hot iff its entry
-// kColdMax is a real slot (real entries form a prefix): one load per block.
-// All threads of the workgroup call it; returns the number of hot blocks, or
-// -1 (ord untouched) when nb exceeds kOrdMax. `wcnt` is 8 ints of LDS.
+// holding more than M/2 tokens ("very hot") first, then the other blocks of
+// more than kColdMax tokens, both in list order, then the rest (reverse list
+// order): hot units cost more than cold ones (they stage the block's token
+// rows as well) and more so the more tokens the block holds, so handing them
+// out heaviest first lets the cheaper units fill the tail, like a
+// longest-first schedule. Real entries of a block form a prefix, so a block
+// holds more than n tokens iff its entry n is a real slot: a load or two per
+// block. All threads of the workgroup call it; returns the number of hot
+// blocks (very hot included), or -1 (ord untouched) when nb exceeds kOrdMax.
+// `wcnt` is 12 ints of LDS, `tmp` kOrdMax ints of LDS (scratch). Every
+// workgroup computes the same order (it only depends on the block lists).
 constexpr int kOrdMax = 2048;
-static_assert(kHotLdsTotal == kHotLds + 4 * (kOrdMax + 8), "hot LDS layout");
+constexpr int kOrdCnt = 12;
+static_assert(kHotLdsTotal == kHotLds + 4 * (kOrdMax + kOrdCnt), "hot LDS layout");
 __device__ int hot_first_order(const int32_t* __restrict__ sorted_ids,
                                const int32_t* __restrict__ block_expert, int nb, int M, int S,
-                               int E, int* ord, int* wcnt) {
+                               int E, int* ord, int* wcnt, int* tmp) {
   if (nb > kOrdMax) return -1;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const uint64_t below = (1ull << lane) - 1;
-  int hot_base = 0, cold_base = 0;
+  const int kv = M / 2;  // more tokens than this: very hot
+  int v_base = 0, h_base = 0, c_base = 0;
   for (int b0 = 0; b0 < nb; b0 += 256) {
     const int b = b0 + t;
-    bool hot = false;
+    bool hot = false, vhot = false;
     if (b < nb && M > kColdMax) {
       const int e = block_expert[b];
-      hot = (unsigned)e < (unsigned)E &&
-            (unsigned)sorted_ids[(size_t)b * M + kColdMax] < (unsigned)S;
+      const int32_t* ids = sorted_ids + (size_t)b * M;
+      hot = (unsigned)e < (unsigned)E && (unsigned)ids[kColdMax] < (unsigned)S;
+      vhot = hot && kv > kColdMax && (unsigned)ids[kv] < (unsigned)S;
     }
-    const uint64_t hb = __ballot(hot), cb = __ballot(b < nb && !hot);
+    const uint64_t vb = __ballot(vhot), hb = __ballot(hot && !vhot), cb = __ballot(b < nb && !hot);
     if (lane == 0) {
-      wcnt[w] = __popcll(hb);
-      wcnt[4 + w] = __popcll(cb);
+      wcnt[w] = __popcll(vb);
+      wcnt[4 + w] = __popcll(hb);
+      wcnt[8 + w] = __popcll(cb);
     }
     __syncthreads();
-    int hp = hot_base, cp = cold_base, ht = 0, ct = 0;
+    int vp = v_base, hp = h_base, cp = c_base, vt = 0, ht = 0, ct = 0;
     for (int i = 0; i < 4; ++i) {
       if (i < w) {
-        hp += wcnt[i];
-        cp += wcnt[4 + i];
+        vp += wcnt[i];
+        hp += wcnt[4 + i];
+        cp += wcnt[8 + i];
       }
-      ht += wcnt[i];
-      ct += wcnt[4 + i];
+      vt += wcnt[i];
+      ht += wcnt[4 + i];
+      ct += wcnt[8 + i];
     }
     if (b < nb) {
-      if (hot) ord[hp + __popcll(hb & below)] = b;
+      if (vhot) ord[vp + __popcll(vb & below)] = b;
+      else if (hot) tmp[hp + __popcll(hb & below)] = b;
       else ord[nb - 1 - (cp + __popcll(cb & below))] = b;
     }
-    hot_base += ht;
-    cold_base += ct;
+    v_base += vt;
+    h_base += ht;
+    c_base += ct;
     __syncthreads();
   }
-  return hot_base;
+  for (int i = t; i < h_base; i += 256) ord[v_base + i] = tmp[i];
+  __syncthreads();
+  return v_base + h_base;
 }
 
 // Number of real (non-sentinel) entries of block b; they form a prefix.
@@ -1037,12 +1058,16 @@ struct BlkGroup {
   u32x4 p[U], q[U], b[U];  // 16 codes of tiles P, Q and of the token per line
   float sa[U];             // activation group scale of this lane's token per line
   float sp[U], sq[U];      // weight block scales of tiles P and Q per line
+  // Every lane loads its token's codes and scales, also a lane without a
+  // token: its callers point it at row 0, which exists, and its products stay
+  // in its own output column, which is never stored (a load under a condition
+  // costs register copies that wait for the load).
   __device__ __forceinline__ void issue(const uint8_t* __restrict__ ap,
                                         const uint8_t* __restrict__ aq,
                                         const uint8_t* __restrict__ bp,
                                         const float* __restrict__ as,
                                         const float* __restrict__ wsp,
-                                        const float* __restrict__ wsq, bool ok, int c) {
+                                        const float* __restrict__ wsq, int c) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       p[u] = __builtin_nontemporal_load((const u32x4*)(ap + (size_t)(c + u) * 128));
@@ -1050,12 +1075,8 @@ struct BlkGroup {
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      b[u] = u32x4{0, 0, 0, 0};
-      sa[u] = 0.f;
-      if (ok) {
-        b[u] = *(const u32x4*)(bp + (size_t)(c + u) * 128);
-        sa[u] = as[c + u];
-      }
+      b[u] = *(const u32x4*)(bp + (size_t)(c + u) * 128);
+      sa[u] = as[c + u];
       sp[u] = wsp[c + u];
       sq[u] = wsq[c + u];
     }
@@ -1087,23 +1108,37 @@ __device__ __forceinline__ void blk_kloop(const uint8_t* __restrict__ ap,
                                           const uint8_t* __restrict__ bp,
                                           const float* __restrict__ as,
                                           const float* __restrict__ wsp,
-                                          const float* __restrict__ wsq, bool ok, int kbytes,
+                                          const float* __restrict__ wsq, int kbytes,
                                           f32x4& accp, f32x4& accq) {
   const int nch = kbytes / 128;
   const int ngrp = nch / U;
   BlkGroup<U> g0, g1;
-  if (ngrp > 0) g0.issue(ap, aq, bp, as, wsp, wsq, ok, 0);
+  if (ngrp > 0) g0.issue(ap, aq, bp, as, wsp, wsq, 0);
   int g = 0;
-  for (; g + 1 < ngrp; g += 2) {
-    g1.issue(ap, aq, bp, as, wsp, wsq, ok, (g + 1) * U);
+  // no condition in the steady-state loop and each set refilled in place
+  // after its MFMAs (the barriers keep the refill behind them), so one group
+  // stays in flight while the other is consumed. Measured on the 16-token
+  // decode shapes: FC1 137.4 -> 132.2 us; the same form in cold_kloop and
+  // w8_kloop measured 2-5 % slower than their looser schedule and is not used
+  // there.
+  for (; g + 2 < ngrp; g += 2) {
+    g1.issue(ap, aq, bp, as, wsp, wsq, (g + 1) * U);
     g0.compute(accp, accq);
-    if (g + 2 < ngrp) g0.issue(ap, aq, bp, as, wsp, wsq, ok, (g + 2) * U);
+    __builtin_amdgcn_sched_barrier(0);
+    g0.issue(ap, aq, bp, as, wsp, wsq, (g + 2) * U);
     g1.compute(accp, accq);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  if (g < ngrp) g0.compute(accp, accq);
+  if (g + 1 < ngrp) {
+    g1.issue(ap, aq, bp, as, wsp, wsq, (g + 1) * U);
+    g0.compute(accp, accq);
+    g1.compute(accp, accq);
+  } else if (g < ngrp) {
+    g0.compute(accp, accq);
+  }
   for (int c = ngrp * U; c < nch; ++c) {
     BlkGroup<1> one;
-    one.issue(ap, aq, bp, as, wsp, wsq, ok, c);
+    one.issue(ap, aq, bp, as, wsp, wsq, c);
     one.compute(accp, accq);
   }
 }
@@ -1127,7 +1162,7 @@ __device__ __forceinline__ void fc1_cold_blk(const Fc1Args& p, int e, int r, int
   const float* wsp = p.w1s + ((size_t)e * nb + (r * 8) / kBlk) * kb;
   const float* wsq = p.w1s + ((size_t)e * nb + (p.I + r * 8) / kBlk) * kb;
   f32x4 accp = {}, accq = {};
-  blk_kloop<kBlkU>(ap, aq, bp, as, wsp, wsq, ok, p.H, accp, accq);
+  blk_kloop<kBlkU>(ap, aq, bp, as, wsp, wsq, p.H, accp, accq);
   const f32x4 g = diag_sum(accp), u = diag_sum(accq);
   if ((lane & 8) == 0 && lane < 32 && ok) store_h<true>(p, slot, r * 8 + 4 * (lane >> 4), g, u);
 }
@@ -1150,7 +1185,7 @@ __device__ __forceinline__ void fc1_cold_blk_sliced(const Fc1Args& p, int e, int
   const float* wsp = p.w1s + ((size_t)e * nb + (r * 8) / kBlk) * kb + c0;
   const float* wsq = p.w1s + ((size_t)e * nb + (p.I + r * 8) / kBlk) * kb + c0;
   f32x4 accp = {}, accq = {};
-  blk_kloop<kBlkU>(ap, aq, bp, as, wsp, wsq, ok, (c1 - c0) * 128, accp, accq);
+  blk_kloop<kBlkU>(ap, aq, bp, as, wsp, wsq, (c1 - c0) * 128, accp, accq);
   if (!sliced_reduce(red, j, accp, accq)) return;
   const f32x4 g = diag_sum(accp), u = diag_sum(accq);
   if ((lane & 8) == 0 && lane < 32 && ok) store_h<true>(p, slot, r * 8 + 4 * (lane >> 4), g, u);
@@ -1172,7 +1207,7 @@ __device__ __forceinline__ void fc2_cold_blk(const Fc2Args& p, int e, int r, int
   const float* as = p.hs + (size_t)s * kb;
   const float* ws = p.w2s + ((size_t)e * nb + (r * 16) / kBlk) * kb;
   f32x4 accp = {}, accq = {};
-  blk_kloop<1>(ap, aq, bp, as, ws, ws, ok, p.I, accp, accq);  // short rows: occupancy over depth
+  blk_kloop<1>(ap, aq, bp, as, ws, ws, p.I, accp, accq);  // short rows: occupancy over depth
   const f32x4 vp = diag_sum(accp), vq = diag_sum(accq);
   if ((lane & 8) == 0 && lane < 32 && ok) {
     const int row = r * 16 + 4 * (lane >> 4);
@@ -1203,15 +1238,26 @@ struct QuadRunner {
   // NT = 1: quad q of block b, wave w taking tile 4q + w; NT = 2: oct q,
   // wave w taking tiles 8q + 2w and 8q + 2w + 1 (a hot block's token rows are
   // then staged once for twice the weight rows)
-  template <int NT>
-  __device__ __forceinline__ void run(int b, int q) {
-    const int r = NT == 1 ? q * 4 + w : q * 8 + 2 * w;
+  __device__ __forceinline__ void enter(int b) {
     if (b != cur_b) {
       cur_b = b;
       e = p.block_expert[b];
       m = (unsigned)e < (unsigned)p.E ? block_valid(p.sorted_ids, b, M, p.S) : 0;
       cslot = ti < m ? p.sorted_ids[(size_t)b * M + ti] : p.S;
     }
+  }
+  // Tile r of a cold block (at most kColdMax tokens) as one unit of the whole
+  // workgroup, K-sliced over its 4 waves by Sliced_; j counts the
+  // workgroup's sliced tiles.
+  template <void (*Sliced_)(const Args&, int, int, int, f32x4*, int)>
+  __device__ __forceinline__ void run_sliced(int b, int r, f32x4* __restrict__ red, int& j) {
+    enter(b);
+    if (m > 0) Sliced_(p, e, r, cslot, red, j++);
+  }
+  template <int NT>
+  __device__ __forceinline__ void run(int b, int q) {
+    const int r = NT == 1 ? q * 4 + w : q * 8 + 2 * w;
+    enter(b);
     if (HOT && m > kColdMax) {
       for (int t0 = 0; t0 < m; t0 += kHotTok) {
         const int mt = min(4, (m - t0 + 15) >> 4);
@@ -1240,10 +1286,13 @@ struct QuadRunner {
 // so more waves stream weights at once; it stays correct for any block,
 // reading the weights once per 8 tokens. With DYN, units are handed out by a
 // QuadQueue over the hot-first block order (hot_first_order): the octs of the
-// hot blocks, then the quads of the others; else each workgroup takes one
-// contiguous equal share of the quad list.
+// hot blocks, then the quads of the others (or, given Sliced_, their single
+// tiles, each K-sliced over the workgroup's 4 waves: a quarter of a quad's
+// cost, so the units that fill the tail behind the long hot ones are fine
+// grained); else each workgroup takes one contiguous equal share of the quad
+// list.
 template <bool FP8, bool HOT, bool DYN, typename Args, void (*Cold_)(const Args&, int, int, int),
-          typename HotOps>
+          typename HotOps, void (*Sliced_)(const Args&, int, int, int, f32x4*, int) = nullptr>
 __device__ __forceinline__ void run_quads(const Args& p, int n_rt, uint8_t* lds) {
   const int M = 1 << p.log2m;
   const int nb = num_blocks(p.num_padded, p.S, p.E, p.log2m);
@@ -1255,20 +1304,36 @@ __device__ __forceinline__ void run_quads(const Args& p, int n_rt, uint8_t* lds)
   } else {
     auto* slots = (volatile __attribute__((address_space(3))) int*)(lds + 2 * kHotTok * kLdsRow);
     int* ord = (int*)(lds + kHotLds);
+    // (the staging buffers, not in use yet, serve as its scratch)
     const int nh = hot_first_order(p.sorted_ids, p.block_expert, nb, M, p.S, p.E, ord,
-                                   ord + kOrdMax);
+                                   ord + kOrdMax, (int*)lds);
     // hot blocks as octs (two tiles per wave) where the policy takes them
     constexpr int kHotNT = HotOps::kOcts ? 2 : 1;
     const bool order = nh >= 0 && (n_rt & (4 * kHotNT - 1)) == 0;
     const int hpb = n_rt / (4 * kHotNT);        // units per hot block
     const int hot_units = order ? nh * hpb : 0;  // they come first
-    QuadQueue qq(p.queue, hot_units + (nb - (order ? nh : 0)) * qpb, p.remap);
+    // cold units per block: single sliced tiles where the order proves the
+    // blocks cold, else quads (run<1> then also serves hot blocks)
+    const bool sliced = Sliced_ != nullptr && order;
+    const int cpb = sliced ? n_rt : qpb;
+    // the staging buffers of the hot passes double as the sliced tiles'
+    // partial sums: units are separated by the barrier in next()
+    f32x4* red = (f32x4*)lds;
+    static_assert(2 * kRedF4 * 16 <= 2 * kHotTok * kLdsRow, "sliced partials fit the staging");
+    int j = 0;
+    QuadQueue qq(p.queue, hot_units + (nb - (order ? nh : 0)) * cpb, p.remap);
     for (int u = qq.first(p.remap); u >= 0; u = qq.next(slots)) {
       const bool hot = u < hot_units;
-      const int v = hot ? u : u - hot_units, per = hot ? hpb : qpb;
+      const int v = hot ? u : u - hot_units, per = hot ? hpb : cpb;
       const int b = order ? ord[(hot ? 0 : nh) + v / per] : v / per;
+      if (order && !hot) qq.early();  // a cold unit: short
       if (kHotNT == 2 && hot) qr.template run<kHotNT>(b, v % per);
-      else qr.template run<1>(b, v % per);
+      else if constexpr (Sliced_ != nullptr) {
+        if (sliced && !hot) qr.template run_sliced<Sliced_>(b, v % per, red, j);
+        else qr.template run<1>(b, v % per);
+      } else {
+        qr.template run<1>(b, v % per);
+      }
     }
   }
 }
@@ -1276,8 +1341,8 @@ __device__ __forceinline__ void run_quads(const Args& p, int n_rt, uint8_t* lds)
 template <bool FP8, bool HOT>
 __global__ __launch_bounds__(256) void fc1_kernel(Fc1Args p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[HOT ? kHotLdsTotal : 16];
-  run_quads<FP8, HOT, HOT, Fc1Args, fc1_cold<FP8, cold_u<FP8, HOT>()>, Fc1Hot<FP8>>(p, p.I >> 3,
-                                                                                   lds);
+  run_quads<FP8, HOT, HOT, Fc1Args, fc1_cold<FP8, cold_u<FP8, HOT>()>, Fc1Hot<FP8>,
+            fc1_cold_sliced<FP8, cold_u<FP8, false>()>>(p, p.I >> 3, lds);
 }
 
 // Whether an FC1 launch of T tokens (at most 16: the cold-only launches) runs

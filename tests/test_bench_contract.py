@@ -70,3 +70,11 @@ def test_bench_modes(args, suffix):
     wl = d["config"]["workload"]
     assert wl.endswith(suffix) or wl.startswith(suffix), wl
     assert d["value"] > 0 and d["roofline"]["achieved"] > 0 and d["cpu_baseline"] is None
+    if wl.startswith("prefill"):
+        # the bound named is the longer of the MFMA and the HBM time, the other
+        # fraction rides along
+        roof = d["roofline"]
+        bms = roof["bound_ms"]
+        assert roof["bound"] == max(bms, key=bms.get)
+        other = "mfma" if roof["bound"] == "hbm" else "hbm"
+        assert 0 < roof[other]["frac"] < 1 and 0 < roof["frac"] < 1
