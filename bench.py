@@ -374,7 +374,9 @@ def main():
         + ("_w8a16" if wo else "") + ("_block128" if blk else "") \
         + ("_single_launch" if args.single_launch else "") \
         + ("_small_path" if args.small_path else "") + (f"_ep{args.ep}_rank0" if args.ep > 1 else "") \
-        + (f"_tp{args.tp}_rank0" if args.tp > 1 else "")
+        + (f"_tp{args.tp}_rank0" if args.tp > 1 else "") \
+        + ("_range_gemm" if args.flags & moe.RANGE_GEMM else "") \
+        + ("_no_xcd_remap" if args.flags & moe.NO_XCD_REMAP else "")
     if args.single_launch:  # one kernel for the whole layer: its bytes over its duration
         gbs = layer_bytes / (fc1_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,

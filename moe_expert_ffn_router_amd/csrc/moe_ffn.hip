@@ -706,10 +706,17 @@ __device__ __forceinline__ void fc1_hot_pass(const Fc1Args& p, int e, int r0, in
 }
 
 // Hot-pass policies of run_quads. kOcts: hot blocks run as octs (two tiles per
-// wave); bf16 only, the fp8 passes would drop to one wave per SIMD.
+// wave); bf16 only, the fp8 passes would drop to one wave per SIMD. kOctsIfFull:
+// only when the octs fill at least half of the grid; with fewer, an oct is
+// long against the launch's whole work and the last ones set its time, so
+// quads (more, shorter units) finish sooner. FC1 kernel traces at 64 tokens,
+// top-8 of 128 experts: whole layer (384 octs, 512 workgroups) octs 214 against
+// quads 238 us; its EP2 share 167.5 against 135.0 us, its TP2 share (192 octs)
+// 167.0 against 127.7 us. FC2's units are shorter: octs won in all three.
 template <bool FP8>
 struct Fc1Hot {
   static constexpr bool kOcts = !FP8;
+  static constexpr bool kOctsIfFull = true;
   template <int MT, int NT>
   static __device__ __forceinline__ void pass(const Fc1Args& p, int e, int r0, int b, int M,
                                               int m, int t0, uint8_t* lds) {
@@ -840,6 +847,7 @@ __device__ __forceinline__ void fc2_hot_pass(const Fc2Args& p, int e, int r0, in
 template <bool FP8>
 struct Fc2Hot {
   static constexpr bool kOcts = !FP8;
+  static constexpr bool kOctsIfFull = false;
   template <int MT, int NT>
   static __device__ __forceinline__ void pass(const Fc2Args& p, int e, int r0, int b, int M,
                                               int m, int t0, uint8_t* lds) {
@@ -1309,9 +1317,11 @@ __device__ __forceinline__ void run_quads(const Args& p, int n_rt, uint8_t* lds)
     const int nh = hot_first_order(p.sorted_ids, p.block_expert, nb, M, p.S, p.E, ord,
                                    ord + kOrdMax, (int*)lds);
     // hot blocks as octs (two tiles per wave) where the policy takes them
-    constexpr int kHotNT = HotOps::kOcts ? 2 : 1;
-    const bool order = nh >= 0 && (n_rt & (4 * kHotNT - 1)) == 0;
-    const int hpb = n_rt / (4 * kHotNT);        // units per hot block
+    bool octs = HotOps::kOcts && nh >= 0 && (n_rt & 7) == 0;
+    if (HotOps::kOctsIfFull && octs) octs = 2L * nh * (n_rt >> 3) >= (long)gridDim.x;
+    const int hnt = octs ? 2 : 1;
+    const bool order = nh >= 0 && (n_rt & (4 * hnt - 1)) == 0;
+    const int hpb = n_rt / (4 * hnt);           // units per hot block
     const int hot_units = order ? nh * hpb : 0;  // they come first
     // cold units per block: single sliced tiles where the order proves the
     // blocks cold, else quads (run<1> then also serves hot blocks)
@@ -1328,8 +1338,13 @@ __device__ __forceinline__ void run_quads(const Args& p, int n_rt, uint8_t* lds)
       const int v = hot ? u : u - hot_units, per = hot ? hpb : cpb;
       const int b = order ? ord[(hot ? 0 : nh) + v / per] : v / per;
       if (order && !hot) qq.early();  // a cold unit: short
-      if (kHotNT == 2 && hot) qr.template run<kHotNT>(b, v % per);
-      else if constexpr (Sliced_ != nullptr) {
+      if constexpr (HotOps::kOcts) {
+        if (octs && hot) {
+          qr.template run<2>(b, v % per);
+          continue;
+        }
+      }
+      if constexpr (Sliced_ != nullptr) {
         if (sliced && !hot) qr.template run_sliced<Sliced_>(b, v % per, red, j);
         else qr.template run<1>(b, v % per);
       } else {
