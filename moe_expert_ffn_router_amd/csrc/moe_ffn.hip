@@ -320,21 +320,50 @@ struct ColdGroup {
 // loaded only if ok) over kbytes bytes of every row. Two register groups
 // alternate: the next group's loads are issued before the current group's
 // MFMAs, so with in-order load counters they stay in flight meanwhile.
+//
+// The groups are walked in rotated order, starting at group rot mod ngrp and
+// wrapping around (the chunks past the last whole group, and an fp8 trailing
+// half chunk, still come last). Callers rotate by cold_rot(tile index): the
+// waves that start together then read their rows at different offsets instead
+// of all starting at a row's first line and advancing in step (5 is odd, so
+// with a power-of-two group count consecutive tiles start on distinct groups).
+// Measured at 16 tokens, fp8 FC1 kernel traces of one box: 127.2 -> 123.4 us,
+// and with the XCD placement off 143.0 -> 123.5 us: the unrotated stream's
+// rate depended on placement (fp8 FC1 had also ranged over 126-149 us from
+// box to box), the rotated one did not. The bf16 tiles (rows twice as long,
+// four chunks per group) measured 0.5-1.5 % slower rotated, so only fp8
+// rotates.
+__host__ __device__ constexpr int cold_rot(int r) { return r * 5; }
+
+// First chunk (of U) of the gi-th group walked when ngrp groups start at
+// group s0 (< ngrp) and wrap around.
+template <int U>
+__device__ __forceinline__ int rot_chunk(int gi, int s0, int ngrp) {
+  const int x = gi + s0;
+  return (x >= ngrp ? x - ngrp : x) * U;
+}
+
 template <bool FP8, int U>
 __device__ __forceinline__ void cold_kloop(const uint8_t* __restrict__ ap,
                                            const uint8_t* __restrict__ aq,
                                            const uint8_t* __restrict__ bp, bool ok, int kbytes,
-                                           f32x4& accp, f32x4& accq) {
+                                           f32x4& accp, f32x4& accq, int rot) {
   constexpr int CH = Cold<FP8>::kChunk, ST = Cold<FP8>::kStep;
   const int nch = kbytes / CH;
   const int ngrp = nch / U;
+  const int s0 = FP8 && ngrp > 0 ? rot % ngrp : 0;
+  // first chunk of the gi-th group walked (bf16: in order, see above)
+  auto chunk = [&](int gi) {
+    if constexpr (!FP8) return gi * U;
+    return rot_chunk<U>(gi, s0, ngrp);
+  };
   ColdGroup<FP8, U> g0, g1;
-  if (ngrp > 0) g0.issue(ap, aq, bp, ok, 0);
+  if (ngrp > 0) g0.issue(ap, aq, bp, ok, chunk(0));
   int g = 0;
   for (; g + 1 < ngrp; g += 2) {
-    g1.issue(ap, aq, bp, ok, (g + 1) * U);
+    g1.issue(ap, aq, bp, ok, chunk(g + 1));
     g0.compute(accp, accq);
-    if (g + 2 < ngrp) g0.issue(ap, aq, bp, ok, (g + 2) * U);
+    if (g + 2 < ngrp) g0.issue(ap, aq, bp, ok, chunk(g + 2));
     g1.compute(accp, accq);
   }
   if (g < ngrp) g0.compute(accp, accq);
@@ -563,7 +592,7 @@ __device__ __forceinline__ void fc1_cold(const Fc1Args& p, int e, int r, int slo
     su = *(const f32x4*)(p.w1s + (size_t)e * 2 * p.I + p.I + col);
   }
   f32x4 accp = {}, accq = {};
-  cold_kloop<FP8, U>(ap, aq, bp, ok, (int)rowb, accp, accq);
+  cold_kloop<FP8, U>(ap, aq, bp, ok, (int)rowb, accp, accq, cold_rot(r));
   f32x4 g = diag_sum(accp), u = diag_sum(accq);
   if (holder && ok) {
     if (FP8) {
@@ -639,7 +668,7 @@ __device__ __forceinline__ void fc1_cold_sliced(const Fc1Args& p, int e, int r, 
     su = *(const f32x4*)(p.w1s + (size_t)e * 2 * p.I + p.I + col);
   }
   f32x4 accp = {}, accq = {};
-  cold_kloop<FP8, U>(ap, aq, bp, ok, kb, accp, accq);
+  cold_kloop<FP8, U>(ap, aq, bp, ok, kb, accp, accq, cold_rot(r));
   if (!sliced_reduce(red, j, accp, accq)) return;
   f32x4 g = diag_sum(accp), u = diag_sum(accq);
   if (holder && ok) {
@@ -787,7 +816,7 @@ __device__ __forceinline__ void fc2_cold(const Fc2Args& p, int e, int r, int slo
     sq = *(const f32x4*)(p.w2s + (size_t)e * p.H + row + 8);
   }
   f32x4 accp = {}, accq = {};
-  cold_kloop<FP8, U>(ap, aq, bp, ok, (int)rowb, accp, accq);
+  cold_kloop<FP8, U>(ap, aq, bp, ok, (int)rowb, accp, accq, cold_rot(r));
   f32x4 vp = diag_sum(accp), vq = diag_sum(accq);
   if (holder && ok) {
     if (FP8) {
@@ -917,21 +946,24 @@ struct W8Group {
 
 // accp/accq += codes of tiles P/Q (ap, aq: this lane's 16-byte piece of each
 // 128-byte line) . bf16 token tile (bp: the matching 32 bytes of each
-// 256-byte activation chunk) over kbytes = K bytes of codes per row.
+// 256-byte activation chunk) over kbytes = K bytes of codes per row, the groups
+// in the rotated order of cold_kloop (16-token decode: FC1 135.5 -> 134.1 us,
+// FC2 72.3 -> 70.6 us).
 template <int U>
 __device__ __forceinline__ void w8_kloop(const uint8_t* __restrict__ ap,
                                          const uint8_t* __restrict__ aq,
                                          const uint8_t* __restrict__ bp, bool ok, int kbytes,
-                                         f32x4& accp, f32x4& accq) {
+                                         f32x4& accp, f32x4& accq, int rot) {
   const int nch = kbytes / 128;
   const int ngrp = nch / U;
+  const int s0 = ngrp > 0 ? rot % ngrp : 0;  // rotated group order, as cold_kloop
   W8Group<U> g0, g1;
-  if (ngrp > 0) g0.issue(ap, aq, bp, ok, 0);
+  if (ngrp > 0) g0.issue(ap, aq, bp, ok, rot_chunk<U>(0, s0, ngrp));
   int g = 0;
   for (; g + 1 < ngrp; g += 2) {
-    g1.issue(ap, aq, bp, ok, (g + 1) * U);
+    g1.issue(ap, aq, bp, ok, rot_chunk<U>(g + 1, s0, ngrp));
     g0.compute(accp, accq);
-    if (g + 2 < ngrp) g0.issue(ap, aq, bp, ok, (g + 2) * U);
+    if (g + 2 < ngrp) g0.issue(ap, aq, bp, ok, rot_chunk<U>(g + 2, s0, ngrp));
     g1.compute(accp, accq);
   }
   if (g < ngrp) g0.compute(accp, accq);
@@ -967,7 +999,7 @@ __device__ __forceinline__ void fc1_cold_w8(const Fc1Args& p, int e, int r, int 
     su = *(const f32x4*)(p.w1s + (size_t)e * 2 * p.I + p.I + col);
   }
   f32x4 accp = {}, accq = {};
-  w8_kloop<kW8U>(ap, aq, bp, ok, (int)rowq, accp, accq);
+  w8_kloop<kW8U>(ap, aq, bp, ok, (int)rowq, accp, accq, cold_rot(r));
   f32x4 g = diag_sum(accp), u = diag_sum(accq);
   if (holder && ok) {
 #pragma unroll
@@ -1004,7 +1036,7 @@ __device__ __forceinline__ void fc1_cold_w8_sliced(const Fc1Args& p, int e, int 
     su = *(const f32x4*)(p.w1s + (size_t)e * 2 * p.I + p.I + col);
   }
   f32x4 accp = {}, accq = {};
-  w8_kloop<kW8U>(ap, aq, bp, ok, (c1 - c0) * 128, accp, accq);
+  w8_kloop<kW8U>(ap, aq, bp, ok, (c1 - c0) * 128, accp, accq, cold_rot(r));
   if (!sliced_reduce(red, j, accp, accq)) return;
   f32x4 g = diag_sum(accp), u = diag_sum(accq);
   if (holder && ok) {
@@ -1035,7 +1067,7 @@ __device__ __forceinline__ void fc2_cold_w8(const Fc2Args& p, int e, int r, int 
     sq = *(const f32x4*)(p.w2s + (size_t)e * p.H + row + 8);
   }
   f32x4 accp = {}, accq = {};
-  w8_kloop<1>(ap, aq, bp, ok, (int)rowq, accp, accq);  // short rows: occupancy over depth
+  w8_kloop<1>(ap, aq, bp, ok, (int)rowq, accp, accq, cold_rot(r));  // short rows: occupancy over depth
   f32x4 vp = diag_sum(accp), vq = diag_sum(accq);
   if (holder && ok) {
 #pragma unroll
@@ -1110,7 +1142,9 @@ struct BlkGroup {
 
 // accp/accq = sum over the kbytes/128 lines of a row of the scaled line
 // partials of tiles P and Q. as: the lane's token's group scales; wsp/wsq:
-// the block-scale rows of P's and Q's row block.
+// the block-scale rows of P's and Q's row block. rot: group order as in
+// cold_kloop; FC2 rotates (16-token decode: 70.8 -> 69.0 us), FC1 does not
+// (133.5 -> 139.5 us rotated, in this loop's in-place form).
 template <int U>
 __device__ __forceinline__ void blk_kloop(const uint8_t* __restrict__ ap,
                                           const uint8_t* __restrict__ aq,
@@ -1118,11 +1152,12 @@ __device__ __forceinline__ void blk_kloop(const uint8_t* __restrict__ ap,
                                           const float* __restrict__ as,
                                           const float* __restrict__ wsp,
                                           const float* __restrict__ wsq, int kbytes,
-                                          f32x4& accp, f32x4& accq) {
+                                          f32x4& accp, f32x4& accq, int rot) {
   const int nch = kbytes / 128;
   const int ngrp = nch / U;
+  const int s0 = ngrp > 0 ? rot % ngrp : 0;  // rotated group order, as cold_kloop
   BlkGroup<U> g0, g1;
-  if (ngrp > 0) g0.issue(ap, aq, bp, as, wsp, wsq, 0);
+  if (ngrp > 0) g0.issue(ap, aq, bp, as, wsp, wsq, rot_chunk<U>(0, s0, ngrp));
   int g = 0;
   // no condition in the steady-state loop and each set refilled in place
   // after its MFMAs (the barriers keep the refill behind them), so one group
@@ -1131,15 +1166,15 @@ __device__ __forceinline__ void blk_kloop(const uint8_t* __restrict__ ap,
   // w8_kloop measured 2-5 % slower than their looser schedule and is not used
   // there.
   for (; g + 2 < ngrp; g += 2) {
-    g1.issue(ap, aq, bp, as, wsp, wsq, (g + 1) * U);
+    g1.issue(ap, aq, bp, as, wsp, wsq, rot_chunk<U>(g + 1, s0, ngrp));
     g0.compute(accp, accq);
     __builtin_amdgcn_sched_barrier(0);
-    g0.issue(ap, aq, bp, as, wsp, wsq, (g + 2) * U);
+    g0.issue(ap, aq, bp, as, wsp, wsq, rot_chunk<U>(g + 2, s0, ngrp));
     g1.compute(accp, accq);
     __builtin_amdgcn_sched_barrier(0);
   }
   if (g + 1 < ngrp) {
-    g1.issue(ap, aq, bp, as, wsp, wsq, (g + 1) * U);
+    g1.issue(ap, aq, bp, as, wsp, wsq, rot_chunk<U>(g + 1, s0, ngrp));
     g0.compute(accp, accq);
     g1.compute(accp, accq);
   } else if (g < ngrp) {
@@ -1171,7 +1206,7 @@ __device__ __forceinline__ void fc1_cold_blk(const Fc1Args& p, int e, int r, int
   const float* wsp = p.w1s + ((size_t)e * nb + (r * 8) / kBlk) * kb;
   const float* wsq = p.w1s + ((size_t)e * nb + (p.I + r * 8) / kBlk) * kb;
   f32x4 accp = {}, accq = {};
-  blk_kloop<kBlkU>(ap, aq, bp, as, wsp, wsq, p.H, accp, accq);
+  blk_kloop<kBlkU>(ap, aq, bp, as, wsp, wsq, p.H, accp, accq, 0);  // unrotated: see blk_kloop
   const f32x4 g = diag_sum(accp), u = diag_sum(accq);
   if ((lane & 8) == 0 && lane < 32 && ok) store_h<true>(p, slot, r * 8 + 4 * (lane >> 4), g, u);
 }
@@ -1194,7 +1229,7 @@ __device__ __forceinline__ void fc1_cold_blk_sliced(const Fc1Args& p, int e, int
   const float* wsp = p.w1s + ((size_t)e * nb + (r * 8) / kBlk) * kb + c0;
   const float* wsq = p.w1s + ((size_t)e * nb + (p.I + r * 8) / kBlk) * kb + c0;
   f32x4 accp = {}, accq = {};
-  blk_kloop<kBlkU>(ap, aq, bp, as, wsp, wsq, (c1 - c0) * 128, accp, accq);
+  blk_kloop<kBlkU>(ap, aq, bp, as, wsp, wsq, (c1 - c0) * 128, accp, accq, 0);
   if (!sliced_reduce(red, j, accp, accq)) return;
   const f32x4 g = diag_sum(accp), u = diag_sum(accq);
   if ((lane & 8) == 0 && lane < 32 && ok) store_h<true>(p, slot, r * 8 + 4 * (lane >> 4), g, u);
@@ -1216,7 +1251,7 @@ __device__ __forceinline__ void fc2_cold_blk(const Fc2Args& p, int e, int r, int
   const float* as = p.hs + (size_t)s * kb;
   const float* ws = p.w2s + ((size_t)e * nb + (r * 16) / kBlk) * kb;
   f32x4 accp = {}, accq = {};
-  blk_kloop<1>(ap, aq, bp, as, ws, ws, p.I, accp, accq);  // short rows: occupancy over depth
+  blk_kloop<1>(ap, aq, bp, as, ws, ws, p.I, accp, accq, cold_rot(r));  // short rows: occupancy over depth
   const f32x4 vp = diag_sum(accp), vq = diag_sum(accq);
   if ((lane & 8) == 0 && lane < 32 && ok) {
     const int row = r * 16 + 4 * (lane >> 4);
