@@ -66,6 +66,26 @@ def test_prefill_workload_block_sizes(block_m, tiles):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("block_m", [16, 64])
+def test_prefill_workload_decode_kernels(block_m):
+    # the 4096-token workload at decode block sizes, so the streaming kernels
+    # with LDS-staged hot blocks run it: at 64 nearly every block is hot and
+    # the hot-first queue orders ~640 blocks; at 16 there are more blocks
+    # (> 2048) than the queue orders, so units go out in list order as quads;
+    # every output row against the oracle
+    inp = cfg_inputs(5)
+    say(f"ffn config 5 block_m={block_m} (decode kernels)")
+    ids, w, al, out = gpu_forward(inp, block_m)
+    check_finite(out)
+    ids_o, w_o, ref = oracle_full(5)
+    check_routing(ids, w, ids_o, w_o)
+    check_align(al, ids_o, inp.E, block_m, inp.S)
+    assert int(al[2][0]) // block_m > (2048 if block_m == 16 else 0)
+    err = oracle.normwise_rel_err(out_f64(out), ref)
+    say(f"  normwise rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("block_m", [128, 256])
 def test_prefill_workload_fp8(block_m):
     # the prefill workload's shapes with e4m3 weights (per-row scales) and
