@@ -1635,15 +1635,18 @@ __device__ __forceinline__ void ring_barrier() {
 // and c+2 are in flight. Loads retire in issue order, so waiting for all but
 // the newest weight tile's loads leaves chunk c+1 complete. nj = 16-token
 // groups of this wave holding tokens (0 = idle wave, which only stages).
-// The chunks are walked from chunk rot mod nch on, wrapping around; callers
-// pass cold_rot(row tile), so the blocks sharing a weight tile stay in step
-// (it is read once from HBM and served to the partner from L2) while the
-// units of other row tiles start elsewhere in K. Measured on the prefill
-// workload (kernel traces, one box each): e4m3 FC1 732 -> 624 us and FC2 387
-// -> 376 us against the loop before; against the same loop with rot = 0, FC1
-// 784 -> 627 us, bf16 FC2 587 -> 579 us, bf16 FC1 unchanged (1104 us). It
-// also left bf16 FC1 without the 36 bytes of scratch per lane it had
-// spilled (the compiler places the per-unit values differently).
+// The chunks are walked from chunk rot mod nch on, wrapping around. FC2
+// passes cold_rot(row tile): the blocks sharing a weight tile stay in step (it
+// is read once from HBM and served to the partner from L2) while the units of
+// other row tiles start elsewhere in K. FC1 passes cold_rot(block): the row
+// tiles sharing a block's 2 MB token tile stay in step instead, which measured
+// better there. Prefill workload, kernel traces (one box each): against the
+// same loop with rot = 0, e4m3 FC1 784 -> 627 us, bf16 FC2 587 -> 579 us, bf16
+// FC1 unchanged (1104 us); FC1 keyed by block instead of row tile, bf16
+// 1086 -> 1065 us, e4m3 623 -> 619 us (FC2 keyed by block: 571 -> 580 us, so
+// FC2 keeps the row tile). The change also left bf16 FC1 without the 36 bytes
+// of scratch per lane it had spilled (the compiler places the per-unit values
+// differently).
 template <bool FP8>
 __device__ __forceinline__ void dense_kloop(const DenseStage& st, int kbytes, int nj, int wr,
                                             int wc, uint8_t* __restrict__ lds, f32x4 (&acc)[4][8],
@@ -1828,7 +1831,7 @@ __global__ __launch_bounds__(kDThreads) void dense_fc1_kernel(Fc1Args p) {
       }
       f32x4 acc[4][8] = {};
       const int nj = min(8, max(0, (m - 128 * wc + 15) >> 4));
-      dense_kloop<FP8>(st, (int)rowb, nj, wr, wc, lds, acc, cold_rot(r));
+      dense_kloop<FP8>(st, (int)rowb, nj, wr, wc, lds, acc, cold_rot(b));
       if (nj == 0) continue;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
