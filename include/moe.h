@@ -71,7 +71,11 @@ enum {
 /* `flags` bits of the moe_ffn_* calls.
  * Stage bits select which stages run; 0 (no stage bit) runs the whole FFN.
  * Running the stages in separate calls with the same workspace gives the same
- * result as one call (the workspace carries the intermediates).
+ * result as one call (the workspace carries the intermediates). A call that
+ * runs FC2 without FC1 continues from the last call on that workspace that
+ * ran FC1 (with the same problem and buffers): it reads that call's h, and the
+ * work counters that call cleared (each FC2 launch leaves them cleared again,
+ * so FC2 may be run more than once).
  *   FC1      : [fp8: per-token activation quantisation +] FC1 gate|up + SiLU*up
  *   FC2      : [fp8: per-slot quantisation of h +] FC2
  *   COMBINE  : top-k weighted combine into `out`

@@ -46,6 +46,11 @@
 namespace moe {
 
 constexpr int kColdMax = 8;     // a block with at most this many tokens is cold
+// Work counters of a launch's dynamic schedule: FC1 uses queue[0, kQueues),
+// FC2 queue[kQueues, 2 kQueues); queue[2 kQueues] counts FC2's finished
+// workgroups (finish_queue).
+constexpr int kQueues = 8;
+constexpr int kQueueInts = 2 * kQueues + 1;
 constexpr int kHotTok = 64;     // tokens per pass of a hot quad (4 MFMA column tiles)
 constexpr int kHotChunk = 256;  // bytes of K per staged chunk (both dtypes)
 // LDS rows are 256 bytes, unpadded: 16-byte column c of row r sits at column
@@ -115,6 +120,23 @@ struct QuadQueue {
     return u < total ? u : -1;
   }
 };
+
+// End of an FC2 launch's dynamic schedule (all threads call it once, after
+// their last pick): the last workgroup to get here sets the launch's n
+// counters and the finish counter q[kQueues] back to zero, so a later call
+// that runs FC2 alone finds them as the FC1 call's zeroing left them. Every
+// workgroup arrives only after its last atomic on the counters has
+// returned, so nothing touches them after the reset; the stores reach the
+// next kernel at the launch boundary.
+__device__ __forceinline__ void finish_queue(int* __restrict__ q, int n) {
+  if (threadIdx.x == 0) {
+    int* done = q + kQueues;
+    if (atomicAdd(done, 1) == (int)gridDim.x - 1) {
+      for (int i = 0; i < n; ++i) q[i] = 0;
+      *done = 0;
+    }
+  }
+}
 
 // Hot-first block order of the dynamic queue. ord[0, nb) receives the blocks
 // holding more than M/2 tokens ("very hot") first, then the other blocks of
@@ -746,6 +768,7 @@ template <bool FP8>
 struct Fc1Hot {
   static constexpr bool kOcts = !FP8;
   static constexpr bool kOctsIfFull = true;
+  static constexpr bool kResetQueue = false;  // FC1 calls zero the counters first
   template <int MT, int NT>
   static __device__ __forceinline__ void pass(const Fc1Args& p, int e, int r0, int b, int M,
                                               int m, int t0, uint8_t* lds) {
@@ -877,6 +900,7 @@ template <bool FP8>
 struct Fc2Hot {
   static constexpr bool kOcts = !FP8;
   static constexpr bool kOctsIfFull = false;
+  static constexpr bool kResetQueue = true;  // see finish_queue
   template <int MT, int NT>
   static __device__ __forceinline__ void pass(const Fc2Args& p, int e, int r0, int b, int M,
                                               int m, int t0, uint8_t* lds) {
@@ -1386,6 +1410,7 @@ __device__ __forceinline__ void run_quads(const Args& p, int n_rt, uint8_t* lds)
         qr.template run<1>(b, v % per);
       }
     }
+    if constexpr (HotOps::kResetQueue) finish_queue(p.queue, 1);
   }
 }
 
@@ -1696,7 +1721,6 @@ __device__ __forceinline__ void dense_kloop(const DenseStage& st, int kbytes, in
 // tile running side by side on one XCD, so the tile is fetched from HBM once
 // and served to the partner from L2. Which workgroup computes a unit never
 // changes the result. With remap off, units are dealt round-robin instead.
-constexpr int kQueues = 8;
 
 __device__ __forceinline__ int hw_xcc_id() {
   int v;
@@ -1935,6 +1959,7 @@ __global__ __launch_bounds__(kDThreads) void dense_fc2_kernel(Fc2Args p) {
       }
     }
   }
+  finish_queue(p.queue, kQueues);
 }
 
 // ----------------------------------------------- per-row FP8 quantiser ---
@@ -2556,7 +2581,7 @@ FfnWorkspace ffn_workspace_layout(int T, int E, int H, int I, int k, int dtype) 
     put(L.xs_off, L.xs_bytes, (size_t)T * xg * 4);
   }
   put(L.y_off, L.y_bytes, S * H * (dtype == MOE_DTYPE_BF16 ? 2 : 4));
-  put(L.q_off, L.q_bytes, S ? 2 * kQueues * sizeof(int) : 0);
+  put(L.q_off, L.q_bytes, S ? kQueueInts * sizeof(int) : 0);
   put(L.plan_off, L.plan_bytes, S && E > 0 ? gemm_plan_ints((int)S, E) * sizeof(int) : 0);
   L.total = o;
   return L;
@@ -2652,8 +2677,8 @@ hipError_t launch_ffn_bf16(const FfnProblem& p, hipStream_t stream) {
   }
   const bool dense = p.block_m >= 128;  // prefill-sized blocks: grouped GEMM tiles
   const bool hot = p.T > 2 * kColdMax;  // see run_quads
-  if ((dense || hot) && (st & (MOE_FFN_STAGE_FC1 | MOE_FFN_STAGE_FC2))) {
-    zero_counters_kernel<<<1, 64, 0, stream>>>(queue, 2 * kQueues);
+  if ((dense || hot) && (st & MOE_FFN_STAGE_FC1)) {  // FC2 alone: see finish_queue
+    zero_counters_kernel<<<1, 64, 0, stream>>>(queue, kQueueInts);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_FC1) {
@@ -2702,8 +2727,8 @@ hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
   // chunks of K at least)
   const bool dense = p.block_m >= 128 && p.H >= 256 && p.I >= 256;
   hipError_t err;
-  if ((dense || hot) && (st & (MOE_FFN_STAGE_FC1 | MOE_FFN_STAGE_FC2))) {
-    zero_counters_kernel<<<1, 64, 0, stream>>>(queue, 2 * kQueues);
+  if ((dense || hot) && (st & MOE_FFN_STAGE_FC1)) {  // FC2 alone: see finish_queue
+    zero_counters_kernel<<<1, 64, 0, stream>>>(queue, kQueueInts);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (st & MOE_FFN_STAGE_FC1) {

@@ -210,11 +210,14 @@ def test_all_tokens_to_one_expert_many_groups():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-def test_determinism_stages_remap_and_guards(dtype):
+@pytest.mark.parametrize("M", [16, 128])
+def test_determinism_stages_remap_and_guards(dtype, M):
+    # M = 16: the streaming kernels with LDS-staged hot blocks (40 tokens, zipf
+    # routing); M = 128: the grouped-GEMM tiles; both schedule units from work
+    # counters in the workspace
     m = moe()
     inp = make_inputs(40, 16, 512, 256, 4, dtype=dtype, routing="zipf", seed=4, device="cuda")
-    say(f"ffn determinism/stages/remap/guards {dtype}")
-    M = 16
+    say(f"ffn determinism/stages/remap/guards {dtype} block_m={M}")
     ids, w = m.route_topk(inp.logits, inp.k)
     sid, be, npad = m.align_block(ids, inp.E, M)
     call = (lambda **kw: m.ffn_fp8(inp.x, inp.w1, inp.w1_scale, inp.w2, inp.w2_scale, ids, w,
@@ -230,10 +233,16 @@ def test_determinism_stages_remap_and_guards(dtype):
     call(flags=m.STAGE_FC1, workspace=ws, out=d)
     call(flags=m.STAGE_FC2, workspace=ws, out=d)
     call(flags=m.STAGE_COMBINE, workspace=ws, out=d)
+    # FC2 alone again, twice: each call continues from the FC1 call's h and
+    # work counters (an FC2 launch leaves its counters cleared)
+    e = torch.empty_like(d)
+    call(flags=m.STAGE_FC2, workspace=ws, out=e)
+    call(flags=m.STAGE_FC2 | m.STAGE_COMBINE, workspace=ws, out=e)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
     assert torch.equal(a.view(torch.int16), d.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), e.view(torch.int16))
     g = guard.cpu().numpy()
     assert np.all(g[:64] == 0x7F7F) and np.all(g[64 + inp.T * inp.H:] == 0x7F7F)
 
