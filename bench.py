@@ -258,8 +258,12 @@ def main():
         return moe.ffn_f32(inp.x, w1, w2, ids, wts, sid, be, npad, M, f, ws, out, stream,
                            prepare=True)
 
+    # a step runs the FFN as three calls: PREP (the counter clearing and x
+    # quantisers FC1 needs first), FC1 alone between events, then FC2 and the
+    # combine; the FFN-only loop runs it as one call
     ffn_calls = {f: prepared_ffn(f) for f in
-                 (moe.STAGE_FC1, moe.STAGE_FC2 | moe.STAGE_COMBINE, 0)}
+                 (moe.STAGE_PREP, moe.STAGE_FC1 | moe.PREPARED,
+                  moe.STAGE_FC2 | moe.STAGE_COMBINE, 0)}
 
     def ffn(flags):
         ffn_calls[flags]()
@@ -302,9 +306,10 @@ def main():
         else:  # the rank routes over all experts and aligns its local ones
             moe.route_topk(inp.logits, k, out=(ids, wts), stream=stream)
             moe.align_block(ids, E, M, out=(sid, be, npad), stream=stream)
+        ffn(moe.STAGE_PREP)
         if i is not None:
             ev_a[i].record(stream)
-        ffn(moe.STAGE_FC1)
+        ffn(moe.STAGE_FC1 | moe.PREPARED)
         if i is not None:
             ev_b[i].record(stream)
         ffn(moe.STAGE_FC2 | moe.STAGE_COMBINE)

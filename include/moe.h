@@ -70,13 +70,19 @@ enum {
 
 /* `flags` bits of the moe_ffn_* calls.
  * Stage bits select which stages run; 0 (no stage bit) runs the whole FFN.
+ *   PREP     : what FC1's kernel needs first: clearing the work counters of
+ *              the dynamically scheduled launches [fp8: + per-token
+ *              quantisation of x; block FP8: + x group quantisation]. A call
+ *              that runs FC1 runs PREP too, unless it passes MOE_FFN_PREPARED:
+ *              then an earlier call on the same workspace ran PREP for these
+ *              inputs, and no FC1 ran since.
  * Running the stages in separate calls with the same workspace gives the same
  * result as one call (the workspace carries the intermediates). A call that
  * runs FC2 without FC1 continues from the last call on that workspace that
  * ran FC1 (with the same problem and buffers): it reads that call's h, and the
- * work counters that call cleared (each FC2 launch leaves them cleared again,
+ * work counters its PREP cleared (each FC2 launch leaves them cleared again,
  * so FC2 may be run more than once).
- *   FC1      : [fp8: per-token activation quantisation +] FC1 gate|up + SiLU*up
+ *   FC1      : FC1 gate|up + SiLU*up (with PREP unless MOE_FFN_PREPARED)
  *   FC2      : [fp8: per-slot quantisation of h +] FC2
  *   COMBINE  : top-k weighted combine into `out`
  * MOE_FFN_NO_XCD_REMAP turns off the placement of contiguous weight ranges
@@ -89,6 +95,8 @@ enum {
 #define MOE_FFN_STAGE_FC1 (1u << 0)
 #define MOE_FFN_STAGE_FC2 (1u << 1)
 #define MOE_FFN_STAGE_COMBINE (1u << 2)
+#define MOE_FFN_STAGE_PREP (1u << 3)
+#define MOE_FFN_PREPARED (1u << 11)
 #define MOE_FFN_NO_XCD_REMAP (1u << 8)
 #define MOE_FFN_RANGE_GEMM (1u << 10)
 /* moe_forward_small only: run the whole layer as one cooperative kernel */

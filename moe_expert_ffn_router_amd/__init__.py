@@ -31,7 +31,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK = 0
 MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_FP8, MOE_DTYPE_W8A16, MOE_DTYPE_FP8_BLOCK = 0, 1, 2, 3, 4
-STAGE_FC1, STAGE_FC2, STAGE_COMBINE = 1 << 0, 1 << 1, 1 << 2
+STAGE_FC1, STAGE_FC2, STAGE_COMBINE, STAGE_PREP = 1 << 0, 1 << 1, 1 << 2, 1 << 3
+PREPARED = 1 << 11  # with STAGE_FC1: an earlier call ran STAGE_PREP (see include/moe.h)
 NO_XCD_REMAP = 1 << 8
 FORWARD_ONE_KERNEL = 1 << 9  # forward_small: the whole layer as one cooperative launch
 RANGE_GEMM = 1 << 10  # bf16 prefill blocks: 256 x 256 tiles over per-expert token ranges

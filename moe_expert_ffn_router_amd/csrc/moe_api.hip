@@ -38,8 +38,9 @@ moe_status check_ffn(const void* x, const void* w1, const void* w2, const int32_
   const int mult = dtype == MOE_DTYPE_F32 ? 4 : 128;
   if (H < mult || I < mult || H % mult != 0 || I % mult != 0) return MOE_ERR_SHAPE;
   if (!is_pow2_le256(block_m)) return MOE_ERR_SHAPE;
-  const unsigned known = MOE_FFN_STAGE_FC1 | MOE_FFN_STAGE_FC2 | MOE_FFN_STAGE_COMBINE |
-                         MOE_FFN_NO_XCD_REMAP | MOE_FFN_RANGE_GEMM;
+  const unsigned known = MOE_FFN_STAGE_PREP | MOE_FFN_STAGE_FC1 | MOE_FFN_STAGE_FC2 |
+                         MOE_FFN_STAGE_COMBINE | MOE_FFN_PREPARED | MOE_FFN_NO_XCD_REMAP |
+                         MOE_FFN_RANGE_GEMM;
   if (flags & ~known) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !w1 || !w2 || !topk_ids || !topk_weights || !sorted_ids || !block_expert ||

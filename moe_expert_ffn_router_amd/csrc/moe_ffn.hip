@@ -2617,9 +2617,15 @@ static int ilog2(int v) {
   return l;
 }
 
+// The stages a call runs: those named (all when none is), PREP with FC1
+// unless the caller has run it already (MOE_FFN_PREPARED).
 static unsigned stages(unsigned flags) {
-  const unsigned s = flags & (MOE_FFN_STAGE_FC1 | MOE_FFN_STAGE_FC2 | MOE_FFN_STAGE_COMBINE);
-  return s ? s : (MOE_FFN_STAGE_FC1 | MOE_FFN_STAGE_FC2 | MOE_FFN_STAGE_COMBINE);
+  constexpr unsigned kAll =
+      MOE_FFN_STAGE_PREP | MOE_FFN_STAGE_FC1 | MOE_FFN_STAGE_FC2 | MOE_FFN_STAGE_COMBINE;
+  unsigned s = flags & kAll;
+  if (!s) s = kAll;
+  if ((s & MOE_FFN_STAGE_FC1) && !(flags & MOE_FFN_PREPARED)) s |= MOE_FFN_STAGE_PREP;
+  return s;
 }
 
 static hipError_t launch_combine(const FfnProblem& p, const FfnWorkspace& L, int dtype,
@@ -2677,7 +2683,7 @@ hipError_t launch_ffn_bf16(const FfnProblem& p, hipStream_t stream) {
   }
   const bool dense = p.block_m >= 128;  // prefill-sized blocks: grouped GEMM tiles
   const bool hot = p.T > 2 * kColdMax;  // see run_quads
-  if ((dense || hot) && (st & MOE_FFN_STAGE_FC1)) {  // FC2 alone: see finish_queue
+  if ((dense || hot) && (st & MOE_FFN_STAGE_PREP)) {  // (FC2 without PREP: finish_queue)
     zero_counters_kernel<<<1, 64, 0, stream>>>(queue, kQueueInts);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
@@ -2727,13 +2733,15 @@ hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
   // chunks of K at least)
   const bool dense = p.block_m >= 128 && p.H >= 256 && p.I >= 256;
   hipError_t err;
-  if ((dense || hot) && (st & MOE_FFN_STAGE_FC1)) {  // FC2 alone: see finish_queue
+  if ((dense || hot) && (st & MOE_FFN_STAGE_PREP)) {  // (FC2 without PREP: finish_queue)
     zero_counters_kernel<<<1, 64, 0, stream>>>(queue, kQueueInts);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  if (st & MOE_FFN_STAGE_FC1) {
+  if (st & MOE_FFN_STAGE_PREP) {
     launch_quant_rows<uint16_t>((const uint16_t*)p.x, p.T, p.H, xq, xs, stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (st & MOE_FFN_STAGE_FC1) {
     Fc1Args a{xq, xs, p.w1, p.w1_scale, p.sorted_ids, p.block_expert, p.num_padded,
               p.H, p.I, p.k, S, log2m, remap, h, queue, p.E};
     if (dense)
@@ -2811,11 +2819,13 @@ hipError_t launch_ffn_fp8_block(const FfnProblem& p, hipStream_t stream) {
   float* xs = (float*)(ws + L.xs_off);
   float* y = (float*)(ws + L.y_off);
   hipError_t err;
-  if (st & MOE_FFN_STAGE_FC1) {
+  if (st & MOE_FFN_STAGE_PREP) {
     const long ng = (long)p.T * (p.H / kBlk);
     quant_groups_kernel<uint16_t><<<(unsigned)((ng + 15) / 16), 256, 0, stream>>>(
         (const uint16_t*)p.x, p.T, p.H, xq, xs);
     if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (st & MOE_FFN_STAGE_FC1) {
     Fc1Args a{xq, xs, p.w1, p.w1_scale, p.sorted_ids, p.block_expert, p.num_padded,
               p.H, p.I, p.k, S, log2m, remap, h, nullptr, p.E};
     if (sliced_fc1(false, p.T))

@@ -145,6 +145,10 @@ def test_ffn_validation(call):
     assert call(ws=P + 128) == ALIGN
     assert call(wsb=16) == WORKSPACE
     assert call(flags=1 << 20) == UNSUP
+    # every documented flag is accepted (the workspace check comes after the flag check)
+    for f in (1, 2, 4, 8, 1 | (1 << 11), 1 << 8, 1 << 10):
+        assert call(flags=f, wsb=16) == WORKSPACE, f
+    assert call(flags=1 << 9, wsb=16) == UNSUP              # moe_forward_small's flag
     assert call(T=0, x=None, out=None, ws=None) == OK       # empty batch: nothing launched
 
 

@@ -238,11 +238,17 @@ def test_determinism_stages_remap_and_guards(dtype, M):
     e = torch.empty_like(d)
     call(flags=m.STAGE_FC2, workspace=ws, out=e)
     call(flags=m.STAGE_FC2 | m.STAGE_COMBINE, workspace=ws, out=e)
+    # PREP in a call of its own, FC1 after it without (MOE_FFN_PREPARED)
+    f = torch.empty_like(d)
+    call(flags=m.STAGE_PREP, workspace=ws, out=f)
+    call(flags=m.STAGE_FC1 | m.PREPARED, workspace=ws, out=f)
+    call(flags=m.STAGE_FC2 | m.STAGE_COMBINE, workspace=ws, out=f)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
     assert torch.equal(a.view(torch.int16), d.view(torch.int16))
     assert torch.equal(a.view(torch.int16), e.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), f.view(torch.int16))
     g = guard.cpu().numpy()
     assert np.all(g[:64] == 0x7F7F) and np.all(g[64 + inp.T * inp.H:] == 0x7F7F)
 
