@@ -103,9 +103,13 @@ def test_determinism_and_stages():
     d = torch.empty_like(a)
     for st in (m.STAGE_FC1, m.STAGE_FC2, m.STAGE_COMBINE):
         call(flags=st, workspace=ws, out=d)
+    f = torch.empty_like(a)  # PREP in a call of its own
+    for st in (m.STAGE_PREP, m.STAGE_FC1 | m.PREPARED, m.STAGE_FC2 | m.STAGE_COMBINE):
+        call(flags=st, workspace=ws, out=f)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert torch.equal(a.view(torch.int16), d.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), f.view(torch.int16))
 
 
 def test_empty_batch_and_bad_scales():
