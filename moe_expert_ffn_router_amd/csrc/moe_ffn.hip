@@ -1536,6 +1536,20 @@ constexpr int kDAStages = 3;              // weight-tile ring
 constexpr int kDBStages = 2;              // token-tile ring
 constexpr int kDLds = (kDAStages + kDBStages) * kDTile;
 constexpr int kDALoads = 4;  // direct-to-LDS loads per wave for one weight tile
+// A block whose expert's tokens spill a little past one block (a "tail" of
+// at most kDTail tokens in the expert's next and last block) takes those
+// tokens into its own unit, so the weight tile streams once for both: the
+// tail rows sit past the 256 token rows of the token stage, in two more
+// 16-token groups. To fit, the merging ring keeps two weight stages instead
+// of three (two 32 KB weight stages and two 36 KB token stages, 136 KB).
+constexpr int kDTail = 32;
+template <bool MG>
+struct DRing {
+  static constexpr int kAStages = MG ? 2 : kDAStages;
+  static constexpr int kBTile = (kDTok + (MG ? kDTail : 0)) * kDChunk;
+  static constexpr int kLds = kAStages * kDTile + kDBStages * kBTile;
+};
+static_assert(DRing<false>::kLds == kDLds && DRing<true>::kLds <= 160 * 1024, "LDS ring");
 // LDS rows are 128 bytes (8 columns of 16 bytes) with no padding; column c of
 // row r sits at column c ^ (r & 7), conflict-free for the MFMA fragment
 // reads (16 consecutive rows, one column) on gfx950.
@@ -1553,6 +1567,9 @@ struct DenseStage {
   const uint8_t* arow[4];  // this lane's source weight rows (+ logical column)
   const uint8_t* brow[4];  // this lane's source token rows (+ logical column)
   int bgroups;             // this wave's token groups holding real tokens (0..4)
+  // merged tail (waves 0..3 stage its 8-row groups, to token rows 256 + 8 w)
+  const uint8_t* trow;
+  bool tload;              // this wave's tail group holds tokens
   __device__ __forceinline__ void issue_a(uint8_t* __restrict__ tile, int c) const {
     const int w = threadIdx.x >> 6;
 #pragma unroll
@@ -1560,6 +1577,7 @@ struct DenseStage {
       __builtin_amdgcn_global_load_lds((const void*)(arow[i] + (size_t)c * kDChunk),
                                        (lds_ptr_t)(tile + (32 * w + 8 * i) * kDChunk), 16, 0, 0);
   }
+  template <bool MG = false>
   __device__ __forceinline__ void issue_b(uint8_t* __restrict__ tile, int c) const {
     const int w = threadIdx.x >> 6;
 #pragma unroll
@@ -1567,6 +1585,9 @@ struct DenseStage {
       if (i < bgroups)
         __builtin_amdgcn_global_load_lds((const void*)(brow[i] + (size_t)c * kDChunk),
                                          (lds_ptr_t)(tile + (32 * w + 8 * i) * kDChunk), 16, 0, 0);
+    if (MG && tload)
+      __builtin_amdgcn_global_load_lds((const void*)(trow + (size_t)c * kDChunk),
+                                       (lds_ptr_t)(tile + (kDTok + 8 * w) * kDChunk), 16, 0, 0);
   }
 };
 
@@ -1591,10 +1612,12 @@ __device__ __forceinline__ int dstage_bgroups(int m) {
 // (lane >> 4) and 4 + (lane >> 4) of its row (the two the bf16 path reads for
 // its two k-steps), the same in A and B, so every product pairs equal k.
 // Waves whose tokens end early use NJ < 8.
-template <int NJ, bool FP8>
+// TAIL (bf16): the wave also multiplies its 16-token group of a merged tail
+// (token rows 256 + 16 wc ..) into acct.
+template <int NJ, bool FP8, bool TAIL = false>
 __device__ __forceinline__ void dense_compute(const uint8_t* __restrict__ ta,
                                               const uint8_t* __restrict__ tb, int wr, int wc,
-                                              f32x4 (&acc)[4][8]) {
+                                              f32x4 (&acc)[4][8], f32x4 (&acct)[4]) {
   const int lane = threadIdx.x & 63;
   // fragment rows are 16-aligned bases + (lane & 15), so row & 7 == lane & 7
   const uint8_t* pa = ta + (64 * wr + (lane & 15)) * kDChunk;
@@ -1616,14 +1639,16 @@ __device__ __forceinline__ void dense_compute(const uint8_t* __restrict__ ta,
     }
     return;
   }
+  const uint8_t* pt = tb + (kDTok + 16 * wc + (lane & 15)) * kDChunk;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int cs = (((s << 2) + (lane >> 4)) ^ (lane & 7)) << 4;
-    bf16x8 fa[4], fb[NJ];
+    bf16x8 fa[4], fb[NJ > 0 ? NJ : 1], ft;
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8*)(pa + i * 16 * kDChunk + cs);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) fb[j] = *(const bf16x8*)(pb + j * 16 * kDChunk + cs);
+    if constexpr (TAIL) ft = *(const bf16x8*)(pt + cs);
     // all reads of the k-step are issued before its first MFMA, so their
     // latencies overlap instead of one read per 4 MFMAs
     __builtin_amdgcn_sched_barrier(0);
@@ -1631,6 +1656,10 @@ __device__ __forceinline__ void dense_compute(const uint8_t* __restrict__ ta,
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i][j] = mfma_bf16(fa[i], fb[j], acc[i][j]);
+    if constexpr (TAIL) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acct[i] = mfma_bf16(fa[i], ft, acct[i]);
+    }
   }
 }
 
@@ -1672,10 +1701,11 @@ __device__ __forceinline__ void ring_barrier() {
 // FC2 keeps the row tile). The change also left bf16 FC1 without the 36 bytes
 // of scratch per lane it had spilled (the compiler places the per-unit values
 // differently).
-template <bool FP8>
-__device__ __forceinline__ void dense_kloop(const DenseStage& st, int kbytes, int nj, int wr,
-                                            int wc, uint8_t* __restrict__ lds, f32x4 (&acc)[4][8],
-                                            int rot) {
+template <bool FP8, bool MG = false>
+__device__ __forceinline__ void dense_kloop(const DenseStage& st, int kbytes, int nj, bool tj,
+                                            int wr, int wc, uint8_t* __restrict__ lds,
+                                            f32x4 (&acc)[4][8], f32x4 (&acct)[4], int rot) {
+  using R = DRing<MG>;
   const int nch = kbytes / kDChunk;  // at least 2 (K >= 128)
   // chunks in rotated order (as the cold tiles): the c-th chunk walked
   const int s0 = rot % nch;
@@ -1686,7 +1716,37 @@ __device__ __forceinline__ void dense_kloop(const DenseStage& st, int kbytes, in
   // tile addresses are computed from the LDS base so they stay in the LDS
   // address space
   uint8_t* const ra = lds;
-  uint8_t* const rb = lds + kDAStages * kDTile;
+  uint8_t* const rb = lds + R::kAStages * kDTile;
+  auto compute = [&](const uint8_t* ta, const uint8_t* tb) {
+    if (MG && tj) {  // a merged tail rides on a full block: nj is 8, or 0 past a 128-block
+      if (nj > 0)
+        dense_compute<8, FP8, MG>(ta, tb, wr, wc, acc, acct);
+      else
+        dense_compute<0, FP8, MG>(ta, tb, wr, wc, acc, acct);
+    } else if (nj > 4)
+      dense_compute<8, FP8>(ta, tb, wr, wc, acc, acct);
+    else if (nj > 2)
+      dense_compute<4, FP8>(ta, tb, wr, wc, acc, acct);
+    else if (nj > 0)
+      dense_compute<2, FP8>(ta, tb, wr, wc, acc, acct);
+  };
+  if constexpr (MG) {
+    // two stages of each operand: chunk c+1 is in flight while c is multiplied
+    st.issue_a(ra, kc(0));
+    st.issue_b<MG>(rb, kc(0));
+    wait_vm<0>();
+    ring_barrier();
+    for (int c = 0; c < nch; ++c) {
+      if (c + 1 < nch) {
+        st.issue_b<MG>(rb + ((c + 1) & 1) * R::kBTile, kc(c + 1));
+        st.issue_a(ra + ((c + 1) & 1) * kDTile, kc(c + 1));
+      }
+      compute(ra + (c & 1) * kDTile, rb + (c & 1) * R::kBTile);
+      wait_vm<0>();
+      ring_barrier();
+    }
+    return;
+  }
   st.issue_a(ra, kc(0));
   st.issue_b(rb, kc(0));
   st.issue_a(ra + kDTile, kc(1));
@@ -1697,14 +1757,7 @@ __device__ __forceinline__ void dense_kloop(const DenseStage& st, int kbytes, in
     const int ia2 = ia == 0 ? 2 : ia - 1;  // weight stage of chunk c+2
     if (c + 1 < nch) st.issue_b(rb + ((c + 1) & 1) * kDTile, kc(c + 1));
     if (c + 2 < nch) st.issue_a(ra + ia2 * kDTile, kc(c + 2));
-    const uint8_t* ta = ra + ia * kDTile;
-    const uint8_t* tb = rb + (c & 1) * kDTile;
-    if (nj > 4)
-      dense_compute<8, FP8>(ta, tb, wr, wc, acc);
-    else if (nj > 2)
-      dense_compute<4, FP8>(ta, tb, wr, wc, acc);
-    else if (nj > 0)
-      dense_compute<2, FP8>(ta, tb, wr, wc, acc);
+    compute(ra + ia * kDTile, rb + (c & 1) * kDTile);
     if (c + 2 < nch)
       wait_vm<kDALoads>();
     else
@@ -1800,18 +1853,29 @@ __device__ __forceinline__ void find_run(const int32_t* __restrict__ block_exper
 }
 
 // Map unit u of the (expert, row tile, block) order to (row tile r, block b).
+// With MG, a run (the blocks of one expert) of two or more blocks whose last
+// block holds at most kDTail tokens has that block merged into the one
+// before it: merge is set, and tail_m is the last block's token count.
 struct UnitMap {
   int nb, n_rt;
   int run_b0 = 0, run_q = 0, e = 0;
   long run_u0 = 0, run_u1 = 0;
+  int tail_m = 0;
+  bool merge = false;
+  template <bool MG = false>
   __device__ __forceinline__ void locate(const int32_t* __restrict__ block_expert, int u, int& r,
-                                         int& b) {
+                                         int& b, const int32_t* __restrict__ sorted_ids = nullptr,
+                                         int M = 0, int S = 0) {
     if (u >= run_u1 || u < run_u0) {
       const int bn = (int)(u / n_rt);
       e = block_expert[bn];
       find_run(block_expert, nb, bn, e, run_b0, run_q);
       run_u0 = (long)run_b0 * n_rt;
       run_u1 = run_u0 + (long)run_q * n_rt;
+      if (MG) {
+        tail_m = run_q >= 2 ? block_valid(sorted_ids, run_b0 + run_q - 1, M, S) : kDTail + 1;
+        merge = tail_m <= kDTail;
+      }
     }
     const long loc = u - run_u0;
     r = (int)(loc / run_q);
@@ -1821,9 +1885,11 @@ struct UnitMap {
 
 // FC1 of prefill-sized blocks; FP8: e4m3 x codes and weights, scaled per
 // weight row and per token in the epilogue; h is written in bf16 either way.
+// bf16 merges tails (UnitMap); the fp8 tiles keep three weight stages.
 template <bool FP8>
 __global__ __launch_bounds__(kDThreads) void dense_fc1_kernel(Fc1Args p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kDLds];
+  constexpr bool MG = !FP8;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[DRing<MG>::kLds];
   const int M = 1 << p.log2m;
   const int nb = num_blocks(p.num_padded, p.S, p.E, p.log2m);
   const int n_rt = (2 * p.I) / kDRows;  // 128 gate + 128 up rows per unit
@@ -1835,10 +1901,18 @@ __global__ __launch_bounds__(kDThreads) void dense_fc1_kernel(Fc1Args p) {
   DenseSched sched(p.queue, units, p.remap);
   for (int u; (u = sched.next(lds)) >= 0;) {
     int r, b;
-    um.locate(p.block_expert, u, r, b);
+    um.locate<MG>(p.block_expert, u, r, b, p.sorted_ids, M, p.S);
     const int e = um.e;
-    const int mb = (unsigned)e < (unsigned)p.E ? block_valid(p.sorted_ids, b, M, p.S) : 0;
-    for (int t0 = 0; t0 < mb; t0 += kDTok) {
+    int mb = (unsigned)e < (unsigned)p.E ? block_valid(p.sorted_ids, b, M, p.S) : 0;
+    int tm = 0;  // tokens of a tail merged into this unit (block b + 1)
+    if (MG && um.merge) {
+      const int last = um.run_b0 + um.run_q - 1;
+      if (b == last)
+        mb = 0;  // computed with block b - 1
+      else if (b == last - 1)
+        tm = um.tail_m;
+    }
+    for (int t0 = 0; t0 < mb; t0 += kDTok) {  // one pass: M <= kDTok
       const int m = mb - t0;
       DenseStage st;
       const int col = dstage_col();
@@ -1853,9 +1927,30 @@ __global__ __launch_bounds__(kDThreads) void dense_fc1_kernel(Fc1Args p) {
         const int slot = rho < m ? p.sorted_ids[(size_t)b * M + t0 + rho] : slot0;
         st.brow[i] = (const uint8_t*)p.x + (size_t)(slot / p.k) * rowb + col;
       }
-      f32x4 acc[4][8] = {};
+      if constexpr (MG) {
+        const int tr = 8 * w + (lane >> 3);  // waves 0..3: tail rows 8 w ..
+        st.tload = w < 4 && 8 * w < tm;
+        const int ts = w < 4 && tr < tm ? p.sorted_ids[(size_t)(b + 1) * M + tr] : slot0;
+        st.trow = (const uint8_t*)p.x + (size_t)(ts / p.k) * rowb + col;
+      }
+      f32x4 acc[4][8] = {}, acct[4] = {};
       const int nj = min(8, max(0, (m - 128 * wc + 15) >> 4));
-      dense_kloop<FP8>(st, (int)rowb, nj, wr, wc, lds, acc, cold_rot(b));
+      const bool tj = tm > 16 * wc;
+      dense_kloop<FP8, MG>(st, (int)rowb, nj, tj, wr, wc, lds, acc, acct, cold_rot(b));
+      if constexpr (MG) {
+        if (tj) {
+          const int ti = 16 * wc + (lane & 15);
+          const int slot = ti < tm ? p.sorted_ids[(size_t)(b + 1) * M + ti] : p.S;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            f32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = __shfl_xor(acct[i][q], 32);
+            if (lane < 32 && slot < p.S)
+              store_h<false>(p, slot, r * 128 + (4 * wr + i) * 8 + 4 * g, acct[i], o);
+          }
+        }
+      }
       if (nj == 0) continue;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -1900,7 +1995,9 @@ __global__ __launch_bounds__(kDThreads) void dense_fc1_kernel(Fc1Args p) {
 }
 
 // FC2 of prefill-sized blocks; FP8: e4m3 h codes and weights, scaled per
-// weight row and per slot in the epilogue, y written as f32.
+// weight row and per slot in the epilogue. Tails are not merged here: on the
+// prefill workload FC2 ran 567 us unmerged on three weight stages, 589 us on
+// two, 571 us merged on two (one box, kernel traces), so FC2 keeps three.
 template <bool FP8>
 __global__ __launch_bounds__(kDThreads) void dense_fc2_kernel(Fc2Args p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kDLds];
@@ -1932,9 +2029,9 @@ __global__ __launch_bounds__(kDThreads) void dense_fc2_kernel(Fc2Args p) {
         const int slot = rho < m ? p.sorted_ids[(size_t)b * M + t0 + rho] : slot0;
         st.brow[i] = (const uint8_t*)p.h + (size_t)slot * rowb + col;
       }
-      f32x4 acc[4][8] = {};
+      f32x4 acc[4][8] = {}, acct[4];
       const int nj = min(8, max(0, (m - 128 * wc + 15) >> 4));
-      dense_kloop<FP8>(st, (int)rowb, nj, wr, wc, lds, acc, cold_rot(r));
+      dense_kloop<FP8>(st, (int)rowb, nj, false, wr, wc, lds, acc, acct, cold_rot(r));
       if (nj == 0) continue;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {

@@ -157,6 +157,49 @@ def test_prefill_tiles_ragged(case, block_m, tiles):
     assert err <= TOL["bf16"]
 
 
+# Per-expert token counts at each block size that leave an expert's last
+# block with 1, 16, 17, 32 and 33 tokens, give one expert three blocks (a
+# 5-token last block), one expert no token and one a single partial block.
+# The bf16 grouped-GEMM FC1 computes a last block of at most 32 tokens
+# together with the block before it (one pass over the weights).
+TAIL_COUNTS = {256: [257, 272, 273, 288, 289, 517, 0, 100],
+               128: [129, 144, 145, 160, 161, 261, 0, 50]}
+
+
+def _counted_logits(counts, seed):
+    """Router logits of a top-2 routing in which expert e gets counts[e]
+    slots: the slots sorted by expert are split in halves, token t takes
+    entries t and t + T (distinct, since no count exceeds T), tokens shuffled."""
+    lst = np.repeat(np.arange(len(counts)), counts)
+    T = len(lst) // 2
+    assert 2 * T == len(lst) and max(counts) <= T
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(T)
+    logits = np.zeros((T, len(counts)), np.float32)
+    logits[perm, lst[:T]] = 4.0
+    logits[perm, lst[T:]] = 3.5
+    return logits
+
+
+@pytest.mark.parametrize("block_m", [128, 256])
+def test_prefill_merged_tails(block_m):
+    counts = TAIL_COUNTS[block_m]
+    logits = _counted_logits(counts, block_m)
+    T, E = logits.shape
+    say(f"ffn merged tails T={T} E={E} k=2 block_m={block_m} counts={counts}")
+    inp = make_inputs(T, E, 384, 256, 2, dtype="bf16", seed=block_m + 7, device="cuda",
+                      logits=logits)
+    ids, w, al, out = gpu_forward(inp, block_m)
+    check_finite(out)
+    ids_o, w_o, ref = oracle_forward(inp)
+    assert np.array_equal(np.bincount(ids_o.ravel(), minlength=E), counts)
+    check_routing(ids, w, ids_o, w_o)
+    check_align(al, ids_o, E, block_m, inp.S)
+    err = oracle.normwise_rel_err(out_f64(out), ref)
+    say(f"  normwise rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 CASES = [  # T, E, H, I, k, routing
     (37, 16, 256, 384, 3, "normal"),
     (5, 4, 128, 128, 4, "normal"),
