@@ -213,8 +213,11 @@ size_t moe_ffn_workspace_bytes(int T, int E, int H, int I, int k, int block_m, i
  *                nothing, so out is this shard's partial sum.
  *  Intermediate h is rounded to bf16 before FC2.
  *  Limits: 0 <= T, 1 <= E <= 1024, 1 <= k <= E, T * k < 2^24, H and I
- *  multiples of 128, block_m a power of two in [1, 256]; x, w1, w2, out and
- *  workspace 16-byte aligned (workspace 256-byte aligned).
+ *  multiples of 8, block_m a power of two in [1, 256]; x, w1, w2, out and
+ *  workspace 16-byte aligned (workspace 256-byte aligned). H and I multiples
+ *  of 128 run the tiled kernels (weight streaming, grouped-GEMM tiles); other
+ *  multiples of 8 a plain path of one wave per output element, which reads
+ *  the weights once per slot (correct for any such shape, not a fast path).
  */
 moe_status moe_ffn_bf16(const uint16_t* x, const uint16_t* w1, const uint16_t* w2,
                         const int32_t* topk_ids, const float* topk_weights,
@@ -261,7 +264,7 @@ moe_status moe_ffn_fp8(const uint16_t* x, const uint8_t* w1, const float* w1_sca
  *  is multiplied by w_scale[e, n/128, c] * a[row, c] and added in fp32:
  *  g, u -> h = SiLU(g) * u in fp32, quantised per (slot, group of 128) the
  *  same way, -> y; combine as moe_ffn_fp8. Other arguments and limits as
- *  moe_ffn_bf16 (H and I multiples of 128); scale pointers non-null and
+ *  moe_ffn_bf16, but H and I multiples of 128; scale pointers non-null and
  *  4-byte aligned when T > 0. Workspace: moe_ffn_workspace_bytes(...,
  *  MOE_DTYPE_FP8_BLOCK). Every block runs the decode-regime streaming
  *  kernels (weights re-read once per 8 tokens of a block): meant for small T.
@@ -288,8 +291,9 @@ moe_status moe_ffn_fp8_block(const uint16_t* x, const uint8_t* w1, const float* 
  *  w2            [E, H, I] e4m3fn codes, w2_scale [E, H] fp32 per output row.
  *  g = w1_scale[e, n] * sum_c dec(w1[e, n, c]) * x[t, c] (likewise u);
  *  h = SiLU(g) * u rounded to bf16; y = w2_scale[e, n] * (dec(w2[e, n]) . h)
- *  rounded to bf16; combine and everything else as moe_ffn_bf16 (same limits,
- *  scale pointers non-null and 16-byte aligned when T > 0). Workspace:
+ *  rounded to bf16; combine and everything else as moe_ffn_bf16 (same limits
+ *  but H and I multiples of 128, scale pointers non-null and 16-byte aligned
+ *  when T > 0). Workspace:
  *  moe_ffn_workspace_bytes(..., MOE_DTYPE_W8A16). Every block runs the
  *  decode-regime streaming kernels (weights are re-read once per 8 tokens of a
  *  block), so the path is meant for small T.

@@ -27,15 +27,15 @@ moe_status check_common(int T, int E, int k) {
 
 size_t capacity(long S, int E, int block_m) { return moe::align_capacity(S, E, block_m); }
 
-// Validation shared by the three FFN entry points.
+// Validation shared by the FFN entry points; H and I must be multiples of
+// mult (f32: 4; bf16 and fp8: 8; weight-only and block-scaled fp8: 128).
 moe_status check_ffn(const void* x, const void* w1, const void* w2, const int32_t* topk_ids,
                      const float* topk_weights, const int32_t* sorted_ids,
                      const int32_t* block_expert, const int32_t* num_padded, int T, int E, int H,
                      int I, int k, int block_m, unsigned flags, const void* workspace,
-                     size_t workspace_bytes, const void* out, int dtype) {
+                     size_t workspace_bytes, const void* out, int dtype, int mult) {
   moe_status s = check_common(T, E, k);
   if (s != MOE_OK) return s;
-  const int mult = dtype == MOE_DTYPE_F32 ? 4 : 128;
   if (H < mult || I < mult || H % mult != 0 || I % mult != 0) return MOE_ERR_SHAPE;
   if (!is_pow2_le256(block_m)) return MOE_ERR_SHAPE;
   const unsigned known = MOE_FFN_STAGE_PREP | MOE_FFN_STAGE_FC1 | MOE_FFN_STAGE_FC2 |
@@ -244,7 +244,7 @@ MOE_EXPORT moe_status moe_ffn_bf16(const uint16_t* x, const uint16_t* w1, const 
                                    size_t workspace_bytes, uint16_t* out, moe_stream_t stream) {
   moe_status s = check_ffn(x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert,
                            num_padded, T, E, H, I, k, block_m, flags, workspace, workspace_bytes,
-                           out, MOE_DTYPE_BF16);
+                           out, MOE_DTYPE_BF16, 8);
   if (s != MOE_OK || T == 0) return s;
   return hip_status(moe::launch_ffn_bf16(
       problem(x, w1, nullptr, w2, nullptr, topk_ids, topk_weights, sorted_ids, block_expert,
@@ -261,7 +261,7 @@ MOE_EXPORT moe_status moe_ffn_fp8(const uint16_t* x, const uint8_t* w1, const fl
                                   size_t workspace_bytes, uint16_t* out, moe_stream_t stream) {
   moe_status s = check_ffn(x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert,
                            num_padded, T, E, H, I, k, block_m, flags, workspace, workspace_bytes,
-                           out, MOE_DTYPE_FP8);
+                           out, MOE_DTYPE_FP8, 8);
   if (s != MOE_OK || T == 0) return s;
   if (!w1_scale || !w2_scale) return MOE_ERR_NULL;
   if (!aligned(w1_scale, 16) || !aligned(w2_scale, 16)) return MOE_ERR_ALIGN;
@@ -281,7 +281,7 @@ MOE_EXPORT moe_status moe_ffn_w8a16(const uint16_t* x, const uint8_t* w1, const 
   // the bf16 path's shape rules (H, I multiples of 128: whole 128-byte lines of codes) and
   // its workspace
   moe_status s = check_ffn(x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert, num_padded, T, E,
-                H, I, k, block_m, flags, workspace, workspace_bytes, out, MOE_DTYPE_BF16);
+                H, I, k, block_m, flags, workspace, workspace_bytes, out, MOE_DTYPE_BF16, 128);
   if (s != MOE_OK || T == 0) return s;
   if (!w1_scale || !w2_scale) return MOE_ERR_NULL;
   if (!aligned(w1_scale, 16) || !aligned(w2_scale, 16)) return MOE_ERR_ALIGN;
@@ -301,7 +301,7 @@ MOE_EXPORT moe_status moe_ffn_fp8_block(const uint16_t* x, const uint8_t* w1,
                                         uint16_t* out, moe_stream_t stream) {
   moe_status s = check_ffn(x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert,
                            num_padded, T, E, H, I, k, block_m, flags, workspace, workspace_bytes,
-                           out, MOE_DTYPE_FP8_BLOCK);
+                           out, MOE_DTYPE_FP8_BLOCK, 128);
   if (s != MOE_OK || T == 0) return s;
   if (!w1_scale || !w2_scale) return MOE_ERR_NULL;
   if (!aligned(w1_scale, 4) || !aligned(w2_scale, 4)) return MOE_ERR_ALIGN;
@@ -319,7 +319,7 @@ MOE_EXPORT moe_status moe_ffn_f32(const float* x, const float* w1, const float* 
                                   size_t workspace_bytes, float* out, moe_stream_t stream) {
   moe_status s = check_ffn(x, w1, w2, topk_ids, topk_weights, sorted_ids, block_expert,
                            num_padded, T, E, H, I, k, block_m, flags, workspace, workspace_bytes,
-                           out, MOE_DTYPE_F32);
+                           out, MOE_DTYPE_F32, 4);
   if (s != MOE_OK || T == 0) return s;
   return hip_status(moe::launch_ffn_f32(
       problem(x, w1, nullptr, w2, nullptr, topk_ids, topk_weights, sorted_ids, block_expert,

@@ -40,6 +40,7 @@
 
 #include <map>
 #include <mutex>
+#include <type_traits>
 
 #include "../../include/moe.h"
 
@@ -2421,6 +2422,106 @@ __global__ __launch_bounds__(256) void fc2_f32_kernel(const float* __restrict__ 
   }
 }
 
+// ------------------------------------ bf16 / fp8, any multiple of 8 ---
+// Shapes whose H or I is not a multiple of 128 (every kernel above stages
+// whole 128-byte lines of a row): one wave per (aligned position, output
+// column), lanes split K in vectors of 8 elements, as the fp32 path. The
+// weights are read once per slot instead of once per block: a fallback for
+// such shapes, not a performance path. FP8: e4m3 codes decoded exactly to
+// fp32 (v_cvt_pk_f32_fp8), the per-row weight scale and the per-token /
+// per-slot activation scale applied to the fp32 sum.
+
+__device__ __forceinline__ void load8e(const uint16_t* p, float (&v)[8]) { load8(p, v); }
+__device__ __forceinline__ void load8e(const uint8_t* p, float (&v)[8]) {
+  const u32x2 q = *(const u32x2*)p;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[i], false);  // codes 4i, 4i+1
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[i], true);   // codes 4i+2, 4i+3
+    v[4 * i] = lo[0];
+    v[4 * i + 1] = lo[1];
+    v[4 * i + 2] = hi[0];
+    v[4 * i + 3] = hi[1];
+  }
+}
+
+// FC1: h[s, n] = SiLU(g) * u; bf16 h in bf16, FP8 h in fp32 (quantised next).
+template <bool FP8>
+__global__ __launch_bounds__(256) void gen_fc1_kernel(Fc1Args p) {
+  using ET = typename std::conditional<FP8, uint8_t, uint16_t>::type;
+  const int lane = threadIdx.x & 63;
+  const long W = (long)gridDim.x * 4;
+  const long total = ((long)num_blocks(p.num_padded, p.S, p.E, p.log2m) << p.log2m) * p.I;
+  for (long u = (long)blockIdx.x * 4 + (threadIdx.x >> 6); u < total; u += W) {
+    const int pos = (int)(u / p.I), n = (int)(u % p.I);
+    const int slot = p.sorted_ids[pos];
+    if (slot >= p.S) continue;
+    const int e = p.block_expert[pos >> p.log2m];
+    if ((unsigned)e >= (unsigned)p.E) continue;
+    const int t = slot / p.k;
+    const ET* xr = (const ET*)p.x + (size_t)t * p.H;
+    const ET* gr = (const ET*)p.w1 + ((size_t)e * 2 * p.I + n) * p.H;
+    const ET* ur = gr + (size_t)p.I * p.H;
+    float gs = 0.f, us = 0.f;
+    for (int c = lane * 8; c < p.H; c += kWave * 8) {
+      float xv[8], gv[8], uv[8];
+      load8e(xr + c, xv);
+      load8e(gr + c, gv);
+      load8e(ur + c, uv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        gs += gv[q] * xv[q];
+        us += uv[q] * xv[q];
+      }
+    }
+    gs = wave_sum(gs);
+    us = wave_sum(us);
+    if (lane == 0) {
+      if constexpr (FP8) {
+        const float xs = p.xs[t];
+        gs *= p.w1s[(size_t)e * 2 * p.I + n] * xs;
+        us *= p.w1s[(size_t)e * 2 * p.I + p.I + n] * xs;
+        ((float*)p.h)[(size_t)slot * p.I + n] = silu_mul(gs, us);
+      } else {
+        ((uint16_t*)p.h)[(size_t)slot * p.I + n] = (uint16_t)f32_to_bf16_rne(silu_mul(gs, us));
+      }
+    }
+  }
+}
+
+// FC2: y[s, n] = W2[e, n, :] . h[s, :]; bf16 y in bf16, FP8 y in fp32.
+template <bool FP8>
+__global__ __launch_bounds__(256) void gen_fc2_kernel(Fc2Args p) {
+  using ET = typename std::conditional<FP8, uint8_t, uint16_t>::type;
+  const int lane = threadIdx.x & 63;
+  const long W = (long)gridDim.x * 4;
+  const long total = ((long)num_blocks(p.num_padded, p.S, p.E, p.log2m) << p.log2m) * p.H;
+  for (long u = (long)blockIdx.x * 4 + (threadIdx.x >> 6); u < total; u += W) {
+    const int pos = (int)(u / p.H), n = (int)(u % p.H);
+    const int slot = p.sorted_ids[pos];
+    if (slot >= p.S) continue;
+    const int e = p.block_expert[pos >> p.log2m];
+    if ((unsigned)e >= (unsigned)p.E) continue;
+    const ET* hr = (const ET*)p.h + (size_t)slot * p.I;
+    const ET* wr = (const ET*)p.w2 + ((size_t)e * p.H + n) * p.I;
+    float s = 0.f;
+    for (int c = lane * 8; c < p.I; c += kWave * 8) {
+      float hv[8], wv[8];
+      load8e(hr + c, hv);
+      load8e(wr + c, wv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s += wv[q] * hv[q];
+    }
+    s = wave_sum(s);
+    if (lane == 0) {
+      if constexpr (FP8)
+        ((float*)p.y)[(size_t)slot * p.H + n] = s * (p.w2s[(size_t)e * p.H + n] * p.hs[slot]);
+      else
+        ((uint16_t*)p.y)[(size_t)slot * p.H + n] = (uint16_t)f32_to_bf16_rne(s);
+    }
+  }
+}
+
 // --------------------------------------------- single-launch small path ---
 // For batches of at most kSmallMaxT tokens the whole layer runs as one
 // cooperative persistent kernel ("vLLM SM architecture adaptation", section
@@ -2748,7 +2849,49 @@ static hipError_t launch_combine(const FfnProblem& p, const FfnWorkspace& L, int
   return hipGetLastError();
 }
 
+// bf16 / fp8 FFN for H or I not a multiple of 128 (gen_fc1_kernel,
+// gen_fc2_kernel), with the stages, workspace and combine of the paths below.
+template <bool FP8>
+static hipError_t launch_ffn_gen(const FfnProblem& p, hipStream_t stream) {
+  const int dtype = FP8 ? MOE_DTYPE_FP8 : MOE_DTYPE_BF16;
+  const FfnWorkspace L = ffn_workspace_layout(p.T, p.E, p.H, p.I, p.k, dtype);
+  const unsigned st = stages(p.flags);
+  const int S = p.T * p.k, log2m = ilog2(p.block_m);
+  char* ws = (char*)p.workspace;
+  void* h = ws + L.h_off;
+  void* y = ws + L.y_off;
+  uint8_t* hq = FP8 ? (uint8_t*)(ws + L.hq_off) : nullptr;
+  float* hs = FP8 ? (float*)(ws + L.hs_off) : nullptr;
+  uint8_t* xq = FP8 ? (uint8_t*)(ws + L.xq_off) : nullptr;
+  float* xs = FP8 ? (float*)(ws + L.xs_off) : nullptr;
+  constexpr int grid = 1024;
+  hipError_t err;
+  if (FP8 && (st & MOE_FFN_STAGE_PREP)) {
+    launch_quant_rows<uint16_t>((const uint16_t*)p.x, p.T, p.H, xq, xs, stream);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (st & MOE_FFN_STAGE_FC1) {
+    Fc1Args a{FP8 ? (const void*)xq : p.x, xs, p.w1, p.w1_scale, p.sorted_ids, p.block_expert,
+              p.num_padded, p.H, p.I, p.k, S, log2m, 0, h, nullptr, p.E};
+    gen_fc1_kernel<FP8><<<grid, 256, 0, stream>>>(a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (st & MOE_FFN_STAGE_FC2) {
+    if (FP8) {
+      launch_quant_rows<float>((const float*)h, S, p.I, hq, hs, stream);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    Fc2Args a{FP8 ? (const void*)hq : h, hs, p.w2, p.w2_scale, p.sorted_ids, p.block_expert,
+              p.num_padded, p.H, p.I, S, log2m, 0, y, FP8 ? 0 : 1, nullptr, p.E};
+    gen_fc2_kernel<FP8><<<grid, 256, 0, stream>>>(a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (st & MOE_FFN_STAGE_COMBINE) return launch_combine(p, L, dtype, stream);
+  return hipSuccess;
+}
+
 hipError_t launch_ffn_bf16(const FfnProblem& p, hipStream_t stream) {
+  if (p.H % 128 != 0 || p.I % 128 != 0) return launch_ffn_gen<false>(p, stream);
   const FfnWorkspace L = ffn_workspace_layout(p.T, p.E, p.H, p.I, p.k, MOE_DTYPE_BF16);
   const unsigned st = stages(p.flags);
   const int remap = (p.flags & MOE_FFN_NO_XCD_REMAP) ? 0 : 1;
@@ -2813,6 +2956,7 @@ hipError_t launch_ffn_bf16(const FfnProblem& p, hipStream_t stream) {
 }
 
 hipError_t launch_ffn_fp8(const FfnProblem& p, hipStream_t stream) {
+  if (p.H % 128 != 0 || p.I % 128 != 0) return launch_ffn_gen<true>(p, stream);
   const FfnWorkspace L = ffn_workspace_layout(p.T, p.E, p.H, p.I, p.k, MOE_DTYPE_FP8);
   const unsigned st = stages(p.flags);
   const int remap = (p.flags & MOE_FFN_NO_XCD_REMAP) ? 0 : 1;

@@ -131,9 +131,27 @@ def call_f32(**kw):
                            a["ws"], a["wsb"], a["out"], None)
 
 
+# the multiple of 8 H and I must be (bf16, fp8: any; weight-only and
+# block-scaled fp8: 128; f32: 4)
+MULT = {call_bf16: 8, call_fp8: 8, call_w8a16: 128, call_fp8_block: 128, call_f32: 4}
+
+
+@pytest.mark.parametrize("call", [call_bf16, call_fp8, call_w8a16, call_fp8_block, call_f32])
+def test_ffn_shape_multiples(call):
+    m = MULT[call]
+    assert call(H=m, I=m, wsb=16) == WORKSPACE               # the smallest allowed shape passes
+    assert call(H=200 if m < 128 else 256, I=m * 3, wsb=16) == WORKSPACE
+    for bad in (m // 2, m + m // 2, 202, 129):
+        if bad % m:
+            assert call(H=bad) == SHAPE, bad
+            assert call(I=bad) == SHAPE, bad
+    if m == 128:
+        assert call(H=200) == SHAPE and call(I=136) == SHAPE
+
+
 @pytest.mark.parametrize("call", [call_bf16, call_fp8, call_w8a16, call_fp8_block, call_f32])
 def test_ffn_validation(call):
-    assert call(H=200) == SHAPE if call is not call_f32 else call(H=202) == SHAPE
+    assert call(H=202) == SHAPE
     assert call(I=0) == SHAPE
     assert call(k=9) == SHAPE
     assert call(E=2000) == SHAPE

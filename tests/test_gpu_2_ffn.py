@@ -200,6 +200,47 @@ def test_prefill_merged_tails(block_m):
     assert err <= TOL["bf16"]
 
 
+ODD_CASES = [  # T, E, H, I, k, routing: H or I a multiple of 8 but not of 128
+    (37, 6, 200, 136, 2, "normal"),
+    (5, 3, 72, 40, 3, "normal"),
+    (64, 8, 256, 200, 2, "zipf"),
+    (300, 4, 136, 264, 2, "normal"),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("block_m", [16, 128])
+@pytest.mark.parametrize("case", ODD_CASES, ids=lambda c: "T{}_E{}_H{}_I{}_k{}_{}".format(*c))
+def test_odd_shapes_parity(case, block_m, dtype):
+    # shapes past the 128-byte-line kernels run the wave-per-output path;
+    # every row against the oracle, and the stages split over three calls on
+    # one workspace give the same bits as one call
+    T, E, H, I, k, routing = case
+    say(f"ffn odd shape {dtype} T={T} E={E} H={H} I={I} k={k} {routing} block_m={block_m}")
+    m = moe()
+    inp = make_inputs(T, E, H, I, k, dtype=dtype, routing=routing, seed=T + H + block_m,
+                      device="cuda")
+    ids, w, al, out = gpu_forward(inp, block_m)
+    check_finite(out)
+    ids_o, w_o, ref = oracle_forward(inp)
+    check_routing(ids, w, ids_o, w_o)
+    err = oracle.normwise_rel_err(out_f64(out), ref)
+    say(f"  normwise rel err {err:.3e}")
+    assert err <= TOL[dtype]
+    sid, be, npad = al
+    call = (lambda **kw: m.ffn_fp8(inp.x, inp.w1, inp.w1_scale, inp.w2, inp.w2_scale, ids, w,
+                                   sid, be, npad, block_m, **kw)) if dtype == "fp8" else \
+        (lambda **kw: m.ffn_bf16(inp.x, inp.w1, inp.w2, ids, w, sid, be, npad, block_m, **kw))
+    ws = m.alloc_workspace(T, E, H, I, k, block_m,
+                           m.MOE_DTYPE_FP8 if dtype == "fp8" else m.MOE_DTYPE_BF16, "cuda")
+    d = torch.empty_like(out)
+    call(flags=m.STAGE_PREP, workspace=ws, out=d)
+    call(flags=m.STAGE_FC1 | m.PREPARED, workspace=ws, out=d)
+    call(flags=m.STAGE_FC2 | m.STAGE_COMBINE, workspace=ws, out=d)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), d.view(torch.int16))
+
+
 CASES = [  # T, E, H, I, k, routing
     (37, 16, 256, 384, 3, "normal"),
     (5, 4, 128, 128, 4, "normal"),
