@@ -1687,8 +1687,10 @@ __device__ __forceinline__ void ring_barrier() {
 
 // The whole K loop of one unit; all 512 threads take part. While chunk c is
 // multiplied, the token tile of chunk c+1 and the weight tiles of chunks c+1
-// and c+2 are in flight. Loads retire in issue order, so waiting for all but
-// the newest weight tile's loads leaves chunk c+1 complete. nj = 16-token
+// and c+2 are in flight (MG, the merging ring: chunk c+1 of both). Loads
+// retire in issue order, so waiting for all but the newest weight tile's
+// loads leaves chunk c+1 complete. tj: this wave multiplies a merged tail's
+// token group as well (MG). nj = 16-token
 // groups of this wave holding tokens (0 = idle wave, which only stages).
 // The chunks are walked from chunk rot mod nch on, wrapping around. FC2
 // passes cold_rot(row tile): the blocks sharing a weight tile stay in step (it
