@@ -769,6 +769,7 @@ template <bool FP8>
 struct Fc1Hot {
   static constexpr bool kOcts = !FP8;
   static constexpr bool kOctsIfFull = true;
+  static constexpr bool kOctsOneRound = false;
   static constexpr bool kResetQueue = false;  // FC1 calls zero the counters first
   template <int MT, int NT>
   static __device__ __forceinline__ void pass(const Fc1Args& p, int e, int r0, int b, int M,
@@ -901,6 +902,7 @@ template <bool FP8>
 struct Fc2Hot {
   static constexpr bool kOcts = !FP8;
   static constexpr bool kOctsIfFull = false;
+  static constexpr bool kOctsOneRound = true;
   static constexpr bool kResetQueue = true;  // see finish_queue
   template <int MT, int NT>
   static __device__ __forceinline__ void pass(const Fc2Args& p, int e, int r0, int b, int M,
@@ -1383,6 +1385,17 @@ __device__ __forceinline__ void run_quads(const Args& p, int n_rt, uint8_t* lds)
     const bool order = nh >= 0 && (n_rt & (4 * hnt - 1)) == 0;
     const int hpb = n_rt / (4 * hnt);           // units per hot block
     const int hot_units = order ? nh * hpb : 0;  // they come first
+    // kOctsOneRound: hot octs beyond one per workgroup run as two quads each
+    // (the end of the hot list: the least hot blocks), so the hot work that
+    // starts in a second round is half as coarse
+    int oct_units = hot_units, hq_units = 0;
+    if constexpr (HotOps::kOctsOneRound) {
+      if (octs && order && hot_units > (int)gridDim.x) {
+        oct_units = gridDim.x;
+        hq_units = 2 * (hot_units - oct_units);
+      }
+    }
+    const int hot_all = oct_units + hq_units;
     // cold units per block: single sliced tiles where the order proves the
     // blocks cold, else quads (run<1> then also serves hot blocks)
     const bool sliced = Sliced_ != nullptr && order;
@@ -1392,10 +1405,15 @@ __device__ __forceinline__ void run_quads(const Args& p, int n_rt, uint8_t* lds)
     f32x4* red = (f32x4*)lds;
     static_assert(2 * kRedF4 * 16 <= 2 * kHotTok * kLdsRow, "sliced partials fit the staging");
     int j = 0;
-    QuadQueue qq(p.queue, hot_units + (nb - (order ? nh : 0)) * cpb, p.remap);
+    QuadQueue qq(p.queue, hot_all + (nb - (order ? nh : 0)) * cpb, p.remap);
     for (int u = qq.first(p.remap); u >= 0; u = qq.next(slots)) {
-      const bool hot = u < hot_units;
-      const int v = hot ? u : u - hot_units, per = hot ? hpb : cpb;
+      const bool hot = u < hot_all;
+      if (hot && u >= oct_units) {  // a hot quad: quad qi of the hot list
+        const int qi = 2 * oct_units + (u - oct_units);
+        qr.template run<1>(ord[qi / (2 * hpb)], qi % (2 * hpb));
+        continue;
+      }
+      const int v = hot ? u : u - hot_all, per = hot ? hpb : cpb;
       const int b = order ? ord[(hot ? 0 : nh) + v / per] : v / per;
       if (order && !hot) qq.early();  // a cold unit: short
       if constexpr (HotOps::kOcts) {
