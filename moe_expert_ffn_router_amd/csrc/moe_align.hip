@@ -186,9 +186,19 @@ __device__ __forceinline__ void align_small_body(const int32_t* ids, int S, int 
   const bool valid = (unsigned)e < (unsigned)E;  // else: remote slot or past S
   int rank = 0;
   if (valid) {
-    // ids before this slot, four per LDS read
+    // ids before this slot, four per LDS read; four reads per step, so that
+    // a slot near the end of a large batch has several in flight instead of
+    // waiting out one LDS round trip per four ids
     const int4* v4 = (const int4*)L.ids;
     int q = 0;
+    for (; q + 16 <= t; q += 16) {
+      const int4 v0 = v4[(q >> 2) + 0], v1 = v4[(q >> 2) + 1];
+      const int4 v2 = v4[(q >> 2) + 2], v3 = v4[(q >> 2) + 3];
+      rank += (v0.x == e) + (v0.y == e) + (v0.z == e) + (v0.w == e);
+      rank += (v1.x == e) + (v1.y == e) + (v1.z == e) + (v1.w == e);
+      rank += (v2.x == e) + (v2.y == e) + (v2.z == e) + (v2.w == e);
+      rank += (v3.x == e) + (v3.y == e) + (v3.z == e) + (v3.w == e);
+    }
     for (; q + 4 <= t; q += 4) {
       const int4 v = v4[q >> 2];
       rank += (v.x == e) + (v.y == e) + (v.z == e) + (v.w == e);
